@@ -184,12 +184,15 @@ class LRUCache:
     3. each hit gets stamp = clock;
     4. each miss, in ascending identity order, takes the lowest-index free
        slot, else the slot with the smallest (stamp, slot) among slots whose
-       stamp < clock (a slot touched in this call is never evicted); if there
-       is none the call fails with CapacityError (state is left as it was
-       when the failure was found); the evicted identity maps to -1 again; the
-       new slot gets stamp = clock and (identity, slot) is appended to the
-       miss list;
+       stamp < clock (a slot touched in this call is never evicted); the
+       evicted identity maps to -1 again; the new slot gets stamp = clock and
+       (identity, slot) is appended to the miss list;
     5. lookups += |U|, hits += |U| - misses.
+
+    Every miss finds a slot exactly when |U| <= S (each miss uses one slot not
+    touched in this call, and S - hits of them exist), so a call with
+    |U| > S fails with CapacityError before it changes anything, the clock
+    included.
 
     With n_slots == n_layers * n_experts the cache is the identity map
     (slot = id) and every lookup is a hit.
@@ -215,6 +218,8 @@ class LRUCache:
         idx = np.asarray(idx)
         ids = layer * self.E + idx.astype(np.int64)
         uniq = sorted(set(int(i) for i in ids.reshape(-1)))
+        if not self.identity and len(uniq) > self.S:
+            raise CapacityError("one call touches more identities than there are slots")
         self.clock += 1
         misses = []
         if self.identity:
@@ -240,8 +245,6 @@ class LRUCache:
                         key = (self.stamp[s], s)
                         if best is None or key < best:
                             best = key
-                if best is None:
-                    raise CapacityError("working set larger than the slot pool")
                 victim = best[1]
                 self.slot_of[self.id_of[victim]] = -1
             self.id_of[victim] = i

@@ -59,7 +59,9 @@ def test_hand_trace():
             if s >= 0:
                 assert c.slot_of[s] == i
         assert np.array_equal(slots, np.vectorize(lambda e: c.slot_of[e])(np.array(call["idx"])))
-    # the failing call left the state of call 4 (only the clock moved)
+    # the failing call changed nothing: state, clock and counts are call 4's
+    last = g["calls"][3]
+    assert c.stamp == last["stamp"] and c.id_of == last["id_of"] and c.clock == 4
     assert c.lookups == g["lookups_after_4"] and c.hits == g["hits_after_4"]
 
 
