@@ -1,0 +1,184 @@
+/*
+ * libmoe -- routed MoE layer with 3-bit block-quantised experts, for AMD
+ * Instinct MI355X (gfx950).  Plain C ABI: device or host pointers and sizes,
+ * no framework types.
+ *
+ * The layer is the one the Strata engine runs on the pages
+ * ("一张 RTX 4090 跑千亿模型，Strata 实测 155 tok/s", section 如何做到：三层存储):
+ * every token is routed to 10 of a layer's 512 experts plus one shared
+ * expert; the (layer, expert) identities -- 48 x 512 = 24,576 of them
+ * ("从一张到四张 RTX 4090 ...", section 先看结果: 48 layers) -- live in a
+ * pool of VRAM slots; a hit is computed straight from its slot, a miss is
+ * fetched from host RAM over PCIe first.  The pages name the IQ3 formats but
+ * print neither their layout, the router's scoring, the activation nor the
+ * eviction policy; the readings used here are spelled out per call below.
+ *
+ * Conventions for every call:
+ *  - returns MOE_OK or a negative moe_status; on a validation error nothing
+ *    is enqueued and no state changes; moe_last_error() gives detail;
+ *  - pointers are DEVICE pointers unless marked (host);
+ *  - `stream` is a hipStream_t (NULL = the null stream); work is enqueued
+ *    on it asynchronously unless the call says otherwise;
+ *  - tensors are row-major and contiguous; the caller owns every tensor it
+ *    passes; a context owns only its own slot table, workspace, pinned miss
+ *    list, side stream and events;
+ *  - one host thread uses a context at a time.
+ *
+ * Expert blob (one per identity, and one shared blob per layer), at
+ * moe_expert_bytes(d_model, d_ff) bytes apart: gate [d_ff][d_model], up
+ * [d_ff][d_model], down [d_model][d_ff]; each matrix is `codes`
+ * [rows][wpr] uint32 followed by `scales` [rows][cols/32] fp16, with
+ * wpr = ceil(cols/10) rounded up to a multiple of 4.  Weight (r, c) has code
+ * q = (codes[r][c/10] >> sh(c%10)) & 7 with sh(j) = 3j for j < 5 and
+ * 16 + 3(j-5) otherwise, and value (q - 4) * scales[r][c/32].  Unused code
+ * slots and pad words are zero.
+ */
+#ifndef LIBMOE_H
+#define LIBMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID = -1,  /* bad argument (null, out of range, wrong shape) */
+  MOE_ERR_ALIGN = -2,    /* pointer not aligned as the call requires */
+  MOE_ERR_CAPACITY = -3, /* a resolve touches more identities than the pool can pin */
+  MOE_ERR_HIP = -4,      /* a HIP runtime call failed; moe_last_error() has its text */
+  MOE_ERR_OOM = -5       /* the context could not allocate its own state */
+} moe_status;
+
+enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2 };
+
+typedef struct moe_ctx moe_ctx;
+
+typedef struct {
+  int32_t d_model;      /* multiple of 32, <= 8192 */
+  int32_t d_ff;         /* multiple of 32, <= 8192 */
+  int32_t n_experts;    /* routed experts per layer, 1..1024 */
+  int32_t top_k;        /* 1..min(n_experts, 32) */
+  int32_t n_layers;     /* >= 1 */
+  int32_t n_slots;      /* VRAM slots; == n_layers*n_experts means every identity is
+                           resident at slot = identity (no host store, no LRU) */
+  int32_t max_tokens;   /* largest T any call will pass; sizes the workspace */
+  const void *host_store; /* (host, pinned) [n_layers*n_experts][blob]; required when
+                             n_slots < n_layers*n_experts, else may be NULL */
+  void *slot_pool;        /* [n_slots][blob], 256-byte aligned */
+  const void *shared_pool;/* [n_layers][blob], 256-byte aligned */
+} moe_config;
+
+typedef struct {
+  int64_t lookups;      /* unique (layer, expert) identities asked for */
+  int64_t hits;         /* of those, already resident */
+  int64_t misses;       /* copied in from the host store */
+  uint64_t bytes_h2d;   /* bytes copied host -> device for misses */
+  int64_t resolve_calls;
+} moe_resolve_info;
+
+/* Bytes between consecutive blobs: the layout above rounded up to 256.
+ * 2,228,224 at (2048, 768); 51,200 at (256, 128); 0 for invalid dims. */
+size_t moe_expert_bytes(int32_t d_model, int32_t d_ff);
+
+/* Validates cfg and allocates the context's own state: slot table
+ * (slot_of[n_layers*n_experts], id_of[n_slots], stamp[n_slots]) in device
+ * memory, workspace sized by max_tokens, a pinned miss list, a side stream
+ * and events.  Does not touch slot_pool / shared_pool / host_store, which the
+ * caller fills.  The cache starts empty (every slot free, clock 0). */
+moe_status moe_create(const moe_config *cfg, moe_ctx **out);
+
+/* Synchronises the context's side stream and frees its own state. */
+moe_status moe_destroy(moe_ctx *ctx);
+
+/* Router of one layer (the pages: 10 of 512 experts per token).  Reading:
+ *   logits[t][e] = sum_c x[t][c] * w_router[e][c] + bias[e]    (fp32)
+ *   idx[t][0..k)  = the k experts with the largest logits, ordered by logit
+ *                   descending, ties to the lower expert index
+ *   w[t][j]       = exp(l_j - l_max) / sum_j' exp(l_j' - l_max), i.e. the
+ *                   softmax over all experts renormalised over the k chosen.
+ * x [T][d_model], w_router [n_experts][d_model], bias [n_experts] or NULL,
+ * logits [T][n_experts] or NULL (not returned), idx [T][top_k] int32,
+ * w [T][top_k].  1 <= T <= max_tokens.  Asynchronous. */
+moe_status moe_route(moe_ctx *ctx, int32_t layer, const float *x, int32_t T,
+                     const float *w_router, const float *bias, float *logits,
+                     int32_t *idx, float *w, void *stream);
+
+/* Maps the routed pairs of one layer to VRAM slots (the pages' hot cache:
+ * hits from VRAM, misses over PCIe from host RAM).  idx [T][top_k] as from
+ * moe_route; slot_of_pair [T][top_k] int32 out (may be NULL when every
+ * identity is resident, in which case nothing is enqueued for it).
+ * Resident mode (n_slots == n_layers*n_experts): slot = layer*E + expert,
+ * asynchronous.  Capped mode: LRU reading -- each call advances a clock; hits
+ * get stamp = clock; misses, in ascending identity order, take the lowest free
+ * slot, else the slot with the smallest (stamp, slot) among slots whose stamp
+ * is older than this call; the call synchronises on its resolve kernel,
+ * copies each missed blob host_store[id] -> slot_pool[slot] with
+ * hipMemcpyAsync on the side stream (after the work already on `stream`),
+ * and makes `stream` wait for those copies before returning.  If one call
+ * touches more identities than n_slots, it returns MOE_ERR_CAPACITY and the
+ * slot table is left as before the call.  info (host) may be NULL; it gets this
+ * call's counts. */
+moe_status moe_cache_resolve(moe_ctx *ctx, int32_t layer, const int32_t *idx, int32_t T,
+                             int32_t *slot_of_pair, moe_resolve_info *info, void *stream);
+
+/* Expert FFNs of one layer:  for every pair p = t*top_k + j,
+ *   y_pairs[p] = W_d (silu(W_g x_t) * (W_u x_t))  with the expert blob at
+ *                slot_pool[slot_of_pair[p]] (or the resident slot
+ *                layer*E + idx[p] when slot_of_pair is NULL),
+ *   y_shared[t] = the same with the layer's shared blob,
+ * silu(z) = z / (1 + exp(-z)).  x [T][d_model] fp32; y_pairs
+ * [T*top_k][d_model] fp32; y_shared [T][d_model] fp32.
+ * path: MOE_PATH_DECODE -- dequantised weights rounded once to fp16,
+ * activations kept at fp32 accuracy (split in two fp16 halves), fp32
+ * accumulation; MOE_PATH_PREFILL -- x, dequantised weights and h each rounded
+ * to fp16, fp32 accumulation, needs d_model and d_ff to be multiples of 64;
+ * MOE_PATH_AUTO -- decode for T <= 64, prefill above (decode when the
+ * dims rule prefill out).  Expert ids outside [0, n_experts) are ignored
+ * (their y_pairs rows are not written).  Uses the context's workspace: calls
+ * on one context must not overlap.  Asynchronous; deterministic (no
+ * floating-point atomics). */
+moe_status moe_expert_ffn(moe_ctx *ctx, int32_t layer, const float *x, int32_t T,
+                          const int32_t *idx, const int32_t *slot_of_pair,
+                          float *y_pairs, float *y_shared, int32_t path, void *stream);
+
+/* out[t] = sum_{j = 0..k-1, ascending} w[t][j] * y_pairs[t*k + j] + y_shared[t]
+ * (the shared expert is ungated and added last).  fp32 throughout. */
+moe_status moe_combine(moe_ctx *ctx, const float *y_pairs, const float *w,
+                       const float *y_shared, int32_t T, float *out, void *stream);
+
+/* --- observability and test support ------------------------------------- */
+
+/* Token -> expert bucketing as moe_expert_ffn does it internally:
+ * offsets [n_experts+1] int32 (exclusive scan of per-expert pair counts,
+ * offsets[E] = T*top_k) and perm [T*top_k] int32 (pair ids grouped by expert
+ * ascending, ascending pair id inside a group).  Asynchronous. */
+moe_status moe_bucket(moe_ctx *ctx, const int32_t *idx, int32_t T, int32_t *offsets,
+                      int32_t *perm, void *stream);
+
+/* Copies the slot table to host arrays (any may be NULL): slot_of
+ * [n_layers*n_experts], id_of [n_slots], stamp [n_slots].  Synchronises the
+ * device.  In resident mode the table is the identity and stamps are 0. */
+moe_status moe_cache_snapshot(moe_ctx *ctx, int32_t *slot_of, int32_t *id_of, uint32_t *stamp);
+
+/* Frees every slot, sets the clock and the cumulative counts to 0.
+ * Synchronises the device.  The recovery path after any error. */
+moe_status moe_cache_reset(moe_ctx *ctx);
+
+/* Cumulative counts since creation or the last reset (host out). */
+moe_status moe_get_stats(moe_ctx *ctx, moe_resolve_info *cumulative);
+
+/* Stacking helper for multi-layer runs (not part of the layer):
+ * x_next[t] = out[t] / sqrt(mean_c(out[t][c]^2) + 1e-6), fp32. */
+moe_status moe_rms_chain(moe_ctx *ctx, const float *out, int32_t T, float *x_next, void *stream);
+
+const char *moe_status_str(moe_status s);
+/* Detail of the last error on the calling thread ("" if none). */
+const char *moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LIBMOE_H */

@@ -1,0 +1,69 @@
+"""Device plumbing around libmoe: pools and buffers in torch memory, one context.
+
+torch provides the allocations (device memory, pinned host memory) and the
+stream; every step of the layer runs in libmoe's kernels through ``binding``.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import binding as B
+
+
+class MoeContext:
+    """Owns the slot pool, the shared pool, the optional pinned host store and a
+    libmoe context sized for ``max_tokens``."""
+
+    def __init__(self, d_model, d_ff, n_experts, top_k, n_layers, n_slots=None, max_tokens=16,
+                 device="cuda:0", host_store=None):
+        self.d_model, self.d_ff, self.E, self.k, self.L = d_model, d_ff, n_experts, top_k, n_layers
+        self.ids = n_layers * n_experts
+        self.n_slots = n_slots or self.ids
+        self.resident = self.n_slots == self.ids
+        self.max_tokens = max_tokens
+        self.device = torch.device(device)
+        self.stride = B.moe_expert_bytes(d_model, d_ff)
+        if self.stride == 0:
+            raise ValueError("invalid d_model / d_ff")
+        self.slot_pool = torch.empty((self.n_slots, self.stride), dtype=torch.uint8, device=self.device)
+        self.shared_pool = torch.empty((n_layers, self.stride), dtype=torch.uint8, device=self.device)
+        if not self.resident and host_store is None:
+            host_store = torch.empty((self.ids, self.stride), dtype=torch.uint8, pin_memory=True)
+        self.host_store = host_store
+        cfg = B.make_config(d_model, d_ff, n_experts, top_k, n_layers, self.n_slots, max_tokens,
+                            self.slot_pool, self.shared_pool, host_store)
+        self.ctx = B.moe_create(cfg)
+
+    def close(self):
+        if self.ctx:
+            B.moe_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def buffers(self, T):
+        d, k, dev = self.d_model, self.k, self.device
+        return dict(
+            logits=torch.empty((T, self.E), dtype=torch.float32, device=dev),
+            idx=torch.empty((T, k), dtype=torch.int32, device=dev),
+            w=torch.empty((T, k), dtype=torch.float32, device=dev),
+            slot=torch.empty((T, k), dtype=torch.int32, device=dev),
+            y_pairs=torch.empty((T * k, d), dtype=torch.float32, device=dev),
+            y_shared=torch.empty((T, d), dtype=torch.float32, device=dev),
+            out=torch.empty((T, d), dtype=torch.float32, device=dev),
+        )
+
+    def layer(self, layer, x, w_router, bias, buf, path=B.MOE_PATH_AUTO, stream=None, logits=True, info=False):
+        """route -> cache_resolve -> expert_ffn -> combine for one layer."""
+        T = x.shape[0]
+        B.moe_route(self.ctx, layer, x, T, w_router, bias, buf["logits"] if logits else None, buf["idx"], buf["w"],
+                    stream)
+        slot = buf["slot"] if (not self.resident or logits) else None
+        ri = B.moe_cache_resolve(self.ctx, layer, buf["idx"], T, slot, info, stream)
+        B.moe_expert_ffn(self.ctx, layer, x, T, buf["idx"], slot, buf["y_pairs"], buf["y_shared"], path, stream)
+        B.moe_combine(self.ctx, buf["y_pairs"], buf["w"], buf["y_shared"], T, buf["out"], stream)
+        return ri

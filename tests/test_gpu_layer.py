@@ -1,0 +1,120 @@
+"""GPU parity of the routed MoE layer against the CPU oracle, through the C ABI.
+
+Decode path: compared with the oracle in 'fp16_weights' mode (the path's
+operand rounding) tightly, and with the exact float64 definition at the stated
+bar.  Prefill path: compared with the 'fp16_operands' mode at the stated bar.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth
+import oracle
+from _gpu_helpers import TOL, check_bucket, check_routing, rel_err, say
+from quantized_expert_ffn_softmax_amd import binding as B
+
+pytestmark = pytest.mark.gpu
+
+TINY = dict(d_model=256, d_ff=128, n_experts=16, top_k=2)
+REAL = dict(d_model=2048, d_ff=768, n_experts=512, top_k=10)
+
+
+def _layer(seed=0, T=8, alpha=0.0, **shape):
+    from moe_synth.harness import SyntheticLayer
+    return SyntheticLayer(seed=seed, n_tokens=T, alpha=alpha, device="cuda:0", **shape)
+
+
+def _oracle(layer, gpu, precision):
+    return oracle.moe_layer(layer.x_np, layer.wr_np, layer.bias_np, layer.k, layer.blob_np, layer.shared_np,
+                            layer.d_model, layer.d_ff, precision=precision, idx=gpu["idx"], w=gpu["w"])
+
+
+def _check_layer(layer, path, tight_prec, tight_tol):
+    say(f"  layer T={layer.T} E={layer.E} k={layer.k} d={layer.d_model} f={layer.d_ff} path={path}")
+    gpu = layer.forward_gpu(path)
+    ties = check_routing(gpu, layer.x_np, layer.wr_np, layer.bias_np, layer.k)
+    ref = _oracle(layer, gpu, tight_prec)
+    e_pairs = rel_err(gpu["y_pairs"], ref["y_pairs"])
+    e_shared = rel_err(gpu["y_shared"], ref["y_shared"])
+    e_out = rel_err(gpu["out"], ref["out64"])
+    exact = _oracle(layer, gpu, "exact")
+    e_exact = rel_err(gpu["out"], exact["out64"])
+    say(f"    near-ties {ties}; vs {tight_prec}: pairs {e_pairs:.2e} shared {e_shared:.2e} out {e_out:.2e}; "
+        f"vs exact: out {e_exact:.2e}")
+    assert e_pairs <= tight_tol and e_shared <= tight_tol and e_out <= tight_tol
+    if path == B.MOE_PATH_DECODE:
+        assert e_exact <= TOL
+    # combine on the GPU's own expert outputs
+    comb = oracle.combine(gpu["y_pairs"].astype(np.float64), gpu["w"].astype(np.float64),
+                          gpu["y_shared"].astype(np.float64))
+    assert rel_err(gpu["out"], comb) <= 1e-6
+    return gpu
+
+
+@pytest.mark.parametrize("T", [1, 3, 8, 17, 40])
+def test_tiny_decode(T):
+    layer = _layer(T=T, **TINY)
+    _check_layer(layer, B.MOE_PATH_DECODE, "fp16_weights", 1e-4)
+    layer.close()
+
+
+@pytest.mark.parametrize("T", [1, 8, 65, 130])
+def test_tiny_prefill(T):
+    layer = _layer(T=T, **TINY)
+    _check_layer(layer, B.MOE_PATH_PREFILL, "fp16_operands", TOL)
+    layer.close()
+
+
+@pytest.mark.parametrize("k", [1, 16])
+def test_tiny_k_extremes(k):
+    shape = dict(TINY, top_k=k)
+    layer = _layer(T=8, **shape)
+    _check_layer(layer, B.MOE_PATH_DECODE, "fp16_weights", 1e-4)
+    _check_layer(layer, B.MOE_PATH_PREFILL, "fp16_operands", TOL)
+    layer.close()
+
+
+def test_real_layer_decode_T5():
+    layer = _layer(T=5, **REAL)
+    _check_layer(layer, B.MOE_PATH_DECODE, "fp16_weights", 1e-4)
+    layer.close()
+
+
+def test_real_layer_decode_T15_zipf():
+    layer = _layer(T=15, alpha=0.75, **REAL)
+    _check_layer(layer, B.MOE_PATH_DECODE, "fp16_weights", 1e-4)
+    layer.close()
+
+
+def test_real_layer_prefill_small():
+    layer = _layer(T=200, alpha=0.75, **REAL)
+    _check_layer(layer, B.MOE_PATH_PREFILL, "fp16_operands", TOL)
+    layer.close()
+
+
+def test_deterministic():
+    layer = _layer(T=15, alpha=0.75, **REAL)
+    for path in (B.MOE_PATH_DECODE, B.MOE_PATH_PREFILL):
+        a = layer.forward_gpu(path)
+        b = layer.forward_gpu(path)
+        for key in ("logits", "idx", "w", "y_pairs", "y_shared", "out"):
+            assert np.array_equal(a[key], b[key]), (path, key)
+    layer.close()
+
+
+def test_bucket_small_and_large():
+    for T in (8, 300, 2000):
+        layer = _layer(T=T, **REAL) if T <= 300 else None
+        ctx = layer.ctx if layer else None
+        if ctx is None:
+            from quantized_expert_ffn_softmax_amd.runtime import MoeContext
+            ctx = MoeContext(256, 128, 512, 10, 1, None, T)
+        rng = np.random.default_rng(T)
+        idx = np.stack([rng.choice(512, 10, replace=False) for _ in range(T)]).astype(np.int32)
+        idx_d = torch.from_numpy(idx).cuda()
+        off = torch.empty(513, dtype=torch.int32, device="cuda")
+        perm = torch.empty(T * 10, dtype=torch.int32, device="cuda")
+        B.moe_bucket(ctx.ctx, idx_d, T, off, perm)
+        torch.cuda.synchronize()
+        check_bucket(off.cpu().numpy(), perm.cpu().numpy(), idx, 512)
+        ctx.close()
