@@ -170,9 +170,11 @@ moe_status moe_cache_reset(moe_ctx *ctx);
 /* Cumulative counts since creation or the last reset (host out). */
 moe_status moe_get_stats(moe_ctx *ctx, moe_resolve_info *cumulative);
 
-/* Stacking helper for multi-layer runs (not part of the layer):
- * x_next[t] = out[t] / sqrt(mean_c(out[t][c]^2) + 1e-6), fp32. */
-moe_status moe_rms_chain(moe_ctx *ctx, const float *out, int32_t T, float *x_next, void *stream);
+/* Stacking helper for multi-layer runs (not part of the layer): each token's
+ * output centred over its d_model features and scaled to unit RMS,
+ * c = out[t] - mean_c(out[t][c]);  x_next[t] = c / sqrt(mean_c(c^2) + 1e-6),
+ * fp32.  out [T][d_model], x_next [T][d_model] (may not alias).  Asynchronous. */
+moe_status moe_chain_norm(moe_ctx *ctx, const float *out, int32_t T, float *x_next, void *stream);
 
 const char *moe_status_str(moe_status s);
 /* Detail of the last error on the calling thread ("" if none). */

@@ -362,12 +362,18 @@ def moe_layer(x, w_router, bias, k, blob_of_expert, shared_blob, d_model, d_ff,
                 out64=out)
 
 
-def rms_chain(out: np.ndarray) -> np.ndarray:
-    """Next layer's input in a stacked run: out[t] / sqrt(mean(out[t]^2) + 1e-6).
+def chain_norm(out: np.ndarray) -> np.ndarray:
+    """Next layer's input in a stacked run: each token's output centred over
+    its features, then scaled to unit RMS:  c = out[t] - mean(out[t]);
+    x_next[t] = c / sqrt(mean(c^2) + 1e-6).
 
     Not part of the pages' layer: it only keeps a 48-layer synthetic stack
-    bounded while keeping each layer's dependence on the previous one.
+    bounded while keeping each layer's dependence on the previous one.  The
+    centring matters: the stand-in weights have mean -0.5 * scale, so expert
+    outputs share a large common component; scaling alone would let it take
+    over within a few layers and route every token to the same experts.
     """
     o = np.asarray(out, dtype=np.float64)
-    r = np.sqrt(np.mean(o * o, axis=1, keepdims=True) + 1e-6)
-    return (o / r).astype(np.float32)
+    c = o - o.mean(axis=1, keepdims=True)
+    r = np.sqrt(np.mean(c * c, axis=1, keepdims=True) + 1e-6)
+    return (c / r).astype(np.float32)

@@ -74,7 +74,7 @@ _SIGS = {
     "moe_cache_snapshot": (_I, [_P, _P, _P, _P]),
     "moe_cache_reset": (_I, [_P]),
     "moe_get_stats": (_I, [_P, ctypes.POINTER(moe_resolve_info)]),
-    "moe_rms_chain": (_I, [_P, _P, _I, _P, _P]),
+    "moe_chain_norm": (_I, [_P, _P, _I, _P, _P]),
     "moe_status_str": (ctypes.c_char_p, [_I]),
     "moe_last_error": (ctypes.c_char_p, []),
 }
@@ -195,8 +195,8 @@ def moe_get_stats(ctx) -> dict:
     return ri.as_dict()
 
 
-def moe_rms_chain(ctx, out, T, x_next, stream=None):
-    _check(load().moe_rms_chain(ctx, _ptr(out), T, _ptr(x_next), _stream(stream)), "moe_rms_chain")
+def moe_chain_norm(ctx, out, T, x_next, stream=None):
+    _check(load().moe_chain_norm(ctx, _ptr(out), T, _ptr(x_next), _stream(stream)), "moe_chain_norm")
 
 
 def moe_status_str(s: int) -> str:

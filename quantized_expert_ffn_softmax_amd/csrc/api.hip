@@ -328,12 +328,12 @@ extern "C" moe_status moe_get_stats(moe_ctx *c, moe_resolve_info *cum) {
   return MOE_OK;
 }
 
-extern "C" moe_status moe_rms_chain(moe_ctx *c, const float *out, int32_t T, float *x_next, void *stream) {
-  MOE_CHECK(c, MOE_ERR_INVALID, "moe_rms_chain: null ctx");
-  MOE_CHECK(T >= 1 && T <= c->cfg.max_tokens, MOE_ERR_INVALID, "moe_rms_chain: T must be 1..max_tokens");
-  MOE_CHECK(out && x_next, MOE_ERR_INVALID, "moe_rms_chain: null pointer");
-  MOE_CHECK(aligned(out, 16) && aligned(x_next, 16), MOE_ERR_ALIGN, "moe_rms_chain: pointers must be 16-byte aligned");
-  hipError_t e = moe::launch_rms_chain(out, T, c->cfg.d_model, x_next, as_stream(stream));
-  if (e != hipSuccess) return moe_fail(MOE_ERR_HIP, std::string("moe_rms_chain: ") + hipGetErrorString(e));
+extern "C" moe_status moe_chain_norm(moe_ctx *c, const float *out, int32_t T, float *x_next, void *stream) {
+  MOE_CHECK(c, MOE_ERR_INVALID, "moe_chain_norm: null ctx");
+  MOE_CHECK(T >= 1 && T <= c->cfg.max_tokens, MOE_ERR_INVALID, "moe_chain_norm: T must be 1..max_tokens");
+  MOE_CHECK(out && x_next, MOE_ERR_INVALID, "moe_chain_norm: null pointer");
+  MOE_CHECK(aligned(out, 16) && aligned(x_next, 16), MOE_ERR_ALIGN, "moe_chain_norm: pointers must be 16-byte aligned");
+  hipError_t e = moe::launch_chain_norm(out, T, c->cfg.d_model, x_next, as_stream(stream));
+  if (e != hipSuccess) return moe_fail(MOE_ERR_HIP, std::string("moe_chain_norm: ") + hipGetErrorString(e));
   return MOE_OK;
 }

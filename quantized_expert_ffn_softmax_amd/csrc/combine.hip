@@ -1,5 +1,5 @@
 // Weighted combine of the k routed expert outputs plus the shared expert,
-// and the RMS helper that chains stacked layers.
+// and the normalisation helper that chains stacked layers.
 //
 // The shared expert is added ungated after the routed terms ("另加 1 个共享
 // 专家" -- one shared expert on top of the 10 routed ones: "一张 RTX 4090
@@ -33,21 +33,33 @@ __global__ void __launch_bounds__(256) combine_kernel(const float *__restrict__ 
   reinterpret_cast<float4 *>(out + (size_t)t * d)[c4] = acc;
 }
 
-// x_next[t] = out[t] / sqrt(mean(out[t]^2) + 1e-6); one workgroup per token.
-__global__ void __launch_bounds__(256) rms_chain_kernel(const float *__restrict__ out, int d,
-                                                        float *__restrict__ x_next) {
+// x_next[t] = c / sqrt(mean(c^2) + 1e-6) with c = out[t] - mean(out[t]); one
+// workgroup per token, two passes over the row (it stays in L2).
+__device__ inline float block_sum_256(float v, float *part) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const float tot = part[0] + part[1] + part[2] + part[3];
+  __syncthreads();
+  return tot;
+}
+
+__global__ void __launch_bounds__(256) chain_norm_kernel(const float *__restrict__ out, int d,
+                                                         float *__restrict__ x_next) {
   __shared__ float part[4];
   const int t = blockIdx.x;
   const float *row = out + (size_t)t * d;
+  float s = 0.f;
+  for (int c = threadIdx.x; c < d; c += blockDim.x) s += row[c];
+  const float mean = block_sum_256(s, part) / (float)d;
   float ss = 0.f;
-  for (int c = threadIdx.x; c < d; c += blockDim.x) ss = fmaf(row[c], row[c], ss);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  const float tot = part[0] + part[1] + part[2] + part[3];
-  const float inv = 1.0f / sqrtf(tot / (float)d + 1e-6f);
-  for (int c = threadIdx.x; c < d; c += blockDim.x) x_next[(size_t)t * d + c] = row[c] * inv;
+  for (int c = threadIdx.x; c < d; c += blockDim.x) {
+    const float v = row[c] - mean;
+    ss = fmaf(v, v, ss);
+  }
+  const float inv = 1.0f / sqrtf(block_sum_256(ss, part) / (float)d + 1e-6f);
+  for (int c = threadIdx.x; c < d; c += blockDim.x) x_next[(size_t)t * d + c] = (row[c] - mean) * inv;
 }
 
 }  // namespace
@@ -61,8 +73,8 @@ hipError_t launch_combine(const float *y_pairs, const float *w, const float *y_s
   return hipGetLastError();
 }
 
-hipError_t launch_rms_chain(const float *out, int T, int d, float *x_next, hipStream_t s) {
-  hipLaunchKernelGGL(rms_chain_kernel, dim3(T), dim3(256), 0, s, out, d, x_next);
+hipError_t launch_chain_norm(const float *out, int T, int d, float *x_next, hipStream_t s) {
+  hipLaunchKernelGGL(chain_norm_kernel, dim3(T), dim3(256), 0, s, out, d, x_next);
   return hipGetLastError();
 }
 

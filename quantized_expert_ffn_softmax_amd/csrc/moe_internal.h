@@ -145,5 +145,5 @@ hipError_t launch_ffn_prefill(const moe_ctx *c, int layer, const float *x, int T
                               const int32_t *slot_of_pair, float *y_pairs, float *y_shared, hipStream_t s);
 hipError_t launch_combine(const float *y_pairs, const float *w, const float *y_shared, int T, int k, int d,
                           float *out, hipStream_t s);
-hipError_t launch_rms_chain(const float *out, int T, int d, float *x_next, hipStream_t s);
+hipError_t launch_chain_norm(const float *out, int T, int d, float *x_next, hipStream_t s);
 }  // namespace moe

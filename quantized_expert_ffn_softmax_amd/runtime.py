@@ -15,7 +15,7 @@ class MoeContext:
     libmoe context sized for ``max_tokens``."""
 
     def __init__(self, d_model, d_ff, n_experts, top_k, n_layers, n_slots=None, max_tokens=16,
-                 device="cuda:0", host_store=None):
+                 device="cuda:0", host_store=None, slot_pool=None, shared_pool=None):
         self.d_model, self.d_ff, self.E, self.k, self.L = d_model, d_ff, n_experts, top_k, n_layers
         self.ids = n_layers * n_experts
         self.n_slots = n_slots or self.ids
@@ -25,8 +25,10 @@ class MoeContext:
         self.stride = B.moe_expert_bytes(d_model, d_ff)
         if self.stride == 0:
             raise ValueError("invalid d_model / d_ff")
-        self.slot_pool = torch.empty((self.n_slots, self.stride), dtype=torch.uint8, device=self.device)
-        self.shared_pool = torch.empty((n_layers, self.stride), dtype=torch.uint8, device=self.device)
+        self.slot_pool = slot_pool if slot_pool is not None else \
+            torch.empty((self.n_slots, self.stride), dtype=torch.uint8, device=self.device)
+        self.shared_pool = shared_pool if shared_pool is not None else \
+            torch.empty((n_layers, self.stride), dtype=torch.uint8, device=self.device)
         if not self.resident and host_store is None:
             host_store = torch.empty((self.ids, self.stride), dtype=torch.uint8, pin_memory=True)
         self.host_store = host_store

@@ -86,6 +86,6 @@ def test_null_context_calls(lib):
     assert lib.moe_destroy(None) == B.MOE_ERR_INVALID
     assert lib.moe_get_stats(None, None) == B.MOE_ERR_INVALID
     assert lib.moe_cache_reset(None) == B.MOE_ERR_INVALID
-    assert lib.moe_rms_chain(None, None, 1, None, None) == B.MOE_ERR_INVALID
+    assert lib.moe_chain_norm(None, None, 1, None, None) == B.MOE_ERR_INVALID
     with pytest.raises(B.MoeError):
         B.moe_destroy(None)

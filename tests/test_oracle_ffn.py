@@ -154,11 +154,15 @@ def test_teacher_forced_routing_reuses_given_idx():
     assert np.array_equal(free["out64"], forced["out64"])
 
 
-def test_rms_chain():
+def test_chain_norm():
     rng = np.random.default_rng(4)
-    o = rng.standard_normal((3, 64)) * 20
-    xn = oracle.rms_chain(o)
-    assert np.allclose(np.sqrt(np.mean(xn.astype(np.float64) ** 2, axis=1)), 1.0, rtol=1e-6)
+    o = rng.standard_normal((3, 64)) * 20 + 7.0
+    xn = oracle.chain_norm(o).astype(np.float64)
+    assert np.allclose(xn.mean(axis=1), 0.0, atol=1e-6)
+    assert np.allclose(np.sqrt(np.mean(xn ** 2, axis=1)), 1.0, rtol=1e-6)
+    # a constant row maps to zero; a shift of the row does not change the result
+    assert np.all(oracle.chain_norm(np.full((1, 8), 3.0)) == 0.0)
+    assert np.allclose(oracle.chain_norm(o + 5.0), xn, atol=1e-6)
 
 
 def test_page_constants():
