@@ -51,7 +51,7 @@ static void free_ctx(moe_ctx *c) {
   if (!c) return;
   void *dev[] = {c->slot_of, c->id_of, c->stamp, c->dstats, c->logits_ws, c->offsets_ws, c->perm_ws,
                  c->chunk_ws, c->work, c->n_work, c->xrec, c->hrec, c->x16, c->h16, c->tile_ws,
-                 c->slot_ws, c->dmiss};
+                 c->slot_ws, c->dmiss, c->route_part};
   for (void *p : dev)
     if (p) (void)hipFree(p);
   if (c->hmiss) (void)hipHostFree(c->hmiss);
@@ -120,6 +120,13 @@ extern "C" moe_status moe_create(const moe_config *cfg, moe_ctx **out) {
   c->max_tiles = (int)((hrows + 127) / 128 + k.n_experts + 2);
   TRY(dalloc(&c->tile_ws, (size_t)c->max_tiles * 4 + 4));
   TRY(dalloc(&c->slot_ws, c->max_pairs));
+  // decode-size router: about 256 workgroups in all, at least one 16-column
+  // chunk per wave (8 waves per workgroup)
+  c->route_ks = 256 / ((k.n_experts + 15) / 16);
+  if (c->route_ks < 1) c->route_ks = 1;
+  while (c->route_ks > 1 && k.d_model / 16 < c->route_ks * 8) c->route_ks /= 2;
+  TRY(dalloc(&c->route_part, (size_t)c->route_ks * 16 * k.n_experts));
+
   TRY(dalloc(&c->dmiss, 3 + 2 * (size_t)c->max_pairs + 2 * (size_t)k.n_experts));
   if (e == hipSuccess)
     e = hipHostMalloc((void **)&c->hmiss, (3 + 2 * (size_t)c->max_pairs + 2 * (size_t)k.n_experts) * sizeof(int32_t),

@@ -4,6 +4,7 @@
 // expert's tokens) that the FFN kernels walk.
 #include "device_util.h"
 #include "moe_internal.h"
+#include "record.h"
 
 namespace {
 
@@ -50,12 +51,20 @@ __device__ void build_work(const int *cnt_sh, const int *off_sh, int E, int T, i
 __global__ void __launch_bounds__(kBucketThreads) bucket_small(const int32_t *__restrict__ idx, int n, int E, int T,
                                                        int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
                                                        int build, int entry_m, moe::WorkEntry *work,
-                                                       int32_t *n_work) {
+                                                       int32_t *n_work, const float *__restrict__ x, int d, int nsb,
+                                                       uint16_t *__restrict__ xrec, int xrec_h) {
   __shared__ int ex[kSmallMax];
   __shared__ int cnt[1024];
   __shared__ int off[1025];
   __shared__ int sh[17];
   const int tid = threadIdx.x;
+  if (blockIdx.x > 0) {
+    // decode path: the other workgroups of this launch build the activation
+    // record of x (independent of the bucketing done by workgroup 0)
+    moe::build_xrec_range(x, T, d, nsb, xrec, xrec_h, (blockIdx.x - 1) * kBucketThreads + tid,
+                          (gridDim.x - 1) * kBucketThreads);
+    return;
+  }
   cnt[tid] = 0;
   __syncthreads();
   if (tid < n) {
@@ -144,11 +153,17 @@ __global__ void __launch_bounds__(kChunk) bucket_scatter(const int32_t *__restri
 namespace moe {
 
 hipError_t launch_bucket_ex(const moe_ctx *c, const int32_t *idx, int T, int32_t *offsets, int32_t *perm, bool build,
-                            int entry_m, hipStream_t s) {
+                            int entry_m, const float *x, uint16_t *xrec, int xrec_h, hipStream_t s) {
   const int E = c->cfg.n_experts, n = T * c->cfg.top_k;
   if (n <= kSmallMax) {
-    hipLaunchKernelGGL(bucket_small, dim3(1), dim3(kBucketThreads), 0, s, idx, n, E, T, offsets, perm, build ? 1 : 0,
-                       entry_m, c->work, c->n_work);
+    // with x: 1 + enough workgroups to build its record, ~8 values per thread
+    int blocks = 1;
+    if (x) {
+      const int vals = T * c->L.gate.nsb * moe::kSteps * 8;
+      blocks += (vals + 8 * kBucketThreads - 1) / (8 * kBucketThreads);
+    }
+    hipLaunchKernelGGL(bucket_small, dim3(blocks), dim3(kBucketThreads), 0, s, idx, n, E, T, offsets, perm,
+                       build ? 1 : 0, entry_m, c->work, c->n_work, x, c->cfg.d_model, c->L.gate.nsb, xrec, xrec_h);
     return hipGetLastError();
   }
   const int nch = (n + kChunk - 1) / kChunk;
@@ -161,7 +176,7 @@ hipError_t launch_bucket_ex(const moe_ctx *c, const int32_t *idx, int T, int32_t
 
 hipError_t launch_bucket(const moe_ctx *c, const int32_t *idx, int T, int32_t *offsets, int32_t *perm, bool build,
                          hipStream_t s) {
-  return launch_bucket_ex(c, idx, T, offsets, perm, build, 16, s);
+  return launch_bucket_ex(c, idx, T, offsets, perm, build, 16, nullptr, nullptr, 0, s);
 }
 
 }  // namespace moe

@@ -244,13 +244,13 @@ __global__ void __launch_bounds__(256) to_fp16_kernel(const float *__restrict__ 
 namespace moe {
 
 hipError_t launch_bucket_ex(const moe_ctx *c, const int32_t *idx, int T, int32_t *offsets, int32_t *perm, bool build,
-                            int entry_m, hipStream_t s);
+                            int entry_m, const float *x, uint16_t *xrec, int xrec_h, hipStream_t s);
 
 hipError_t launch_ffn_prefill(const moe_ctx *c, int layer, const float *x, int T, const int32_t *idx,
                               const int32_t *slot_of_pair, float *y_pairs, float *y_shared, hipStream_t s) {
   const moe_config &k = c->cfg;
   if (k.d_ff % kTN || k.d_model % kTN) return hipErrorInvalidValue;
-  hipError_t e = launch_bucket_ex(c, idx, T, c->offsets_ws, c->perm_ws, true, kTM, s);
+  hipError_t e = launch_bucket_ex(c, idx, T, c->offsets_ws, c->perm_ws, true, kTM, nullptr, nullptr, 0, s);
   if (e != hipSuccess) return e;
   const size_t nx = (size_t)T * k.d_model;
   hipLaunchKernelGGL(to_fp16_kernel, dim3((unsigned)((nx + 255) / 256)), dim3(256), 0, s, x, nx, (_Float16 *)c->x16);

@@ -106,6 +106,8 @@ struct moe_ctx {
   uint16_t *h16;         // prefill: [max_pairs + max_tokens][d_ff] fp16
   int32_t *tile_ws;      // prefill tile list
   int32_t *slot_ws;      // [max_pairs] slots when the caller passes none
+  float *route_part;     // [route_ks][16][n_experts] partial logits (decode-size router)
+  int32_t route_ks;      // column slices of the decode-size router
   int32_t max_pairs;
   int32_t max_work;
   int32_t n_chunks_max;

@@ -10,69 +10,6 @@ namespace {
 
 constexpr int kWave = 64;
 
-// --- logits, few tokens: each wave owns 4 expert rows and streams them once;
-// x is re-read from L2 per wave.  T <= 16.
-constexpr int kEpw = 4;        // experts per wave
-constexpr int kMaxTSmall = 16;
-
-__global__ void __launch_bounds__(256) router_logits_small(const float *__restrict__ x, int T, int d,
-                                                           const float *__restrict__ wr,
-                                                           const float *__restrict__ bias, int E,
-                                                           float *__restrict__ logits) {
-  const int lane = threadIdx.x & 63;
-  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-  const int e0 = wave * kEpw;
-  if (e0 >= E) return;
-  float acc[kEpw][kMaxTSmall];
-#pragma unroll
-  for (int a = 0; a < kEpw; ++a)
-#pragma unroll
-    for (int t = 0; t < kMaxTSmall; ++t) acc[a][t] = 0.f;
-  for (int c = lane * 4; c < d; c += kWave * 4) {
-    float4 wv[kEpw];
-#pragma unroll
-    for (int a = 0; a < kEpw; ++a) {
-      const int e = e0 + a < E ? e0 + a : E - 1;
-      wv[a] = *reinterpret_cast<const float4 *>(wr + (size_t)e * d + c);
-    }
-#pragma unroll
-    for (int t = 0; t < kMaxTSmall; ++t) {
-      if (t < T) {
-        const float4 xv = *reinterpret_cast<const float4 *>(x + (size_t)t * d + c);
-#pragma unroll
-        for (int a = 0; a < kEpw; ++a) {
-          acc[a][t] = fmaf(wv[a].x, xv.x, acc[a][t]);
-          acc[a][t] = fmaf(wv[a].y, xv.y, acc[a][t]);
-          acc[a][t] = fmaf(wv[a].z, xv.z, acc[a][t]);
-          acc[a][t] = fmaf(wv[a].w, xv.w, acc[a][t]);
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int a = 0; a < kEpw; ++a) {
-#pragma unroll
-    for (int t = 0; t < kMaxTSmall; ++t) {
-      float v = acc[a][t];
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-      acc[a][t] = v;
-    }
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int a = 0; a < kEpw; ++a) {
-      const int e = e0 + a;
-      if (e < E) {
-        const float b = bias ? bias[e] : 0.f;
-#pragma unroll
-        for (int t = 0; t < kMaxTSmall; ++t)
-          if (t < T) logits[(size_t)t * E + e] = acc[a][t] + b;
-      }
-    }
-  }
-}
-
 // --- logits, many tokens: LDS-tiled fp32 GEMM, 64x64 output tile, each thread 4x4.
 constexpr int kTm = 64, kTn = 64, kTk = 16;
 
@@ -128,12 +65,10 @@ __device__ inline bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
-__global__ void __launch_bounds__(256) router_topk(const float *__restrict__ logits, int T, int E, int k,
-                                                   int32_t *__restrict__ idx, float *__restrict__ w) {
+// top-k of one token's row by one wave
+__device__ void topk_row(const float *__restrict__ row, int E, int k, int32_t *__restrict__ idx_row,
+                         float *__restrict__ w_row) {
   const int lane = threadIdx.x & 63;
-  const int t = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-  if (t >= T) return;
-  const float *row = logits + (size_t)t * E;
   float v[kMaxPerLane];
   uint32_t taken = 0;
 #pragma unroll
@@ -169,9 +104,82 @@ __global__ void __launch_bounds__(256) router_topk(const float *__restrict__ log
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, kWave);
   if (lane < k) {
-    idx[(size_t)t * k + lane] = my_i;
-    w[(size_t)t * k + lane] = ex / sum;
+    idx_row[lane] = my_i;
+    w_row[lane] = ex / sum;
   }
+}
+
+__global__ void __launch_bounds__(256) router_topk(const float *__restrict__ logits, int T, int E, int k,
+                                                   int32_t *__restrict__ idx, float *__restrict__ w) {
+  const int t = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  if (t >= T) return;
+  topk_row(logits + (size_t)t * E, E, k, idx + (size_t)t * k, w + (size_t)t * k);
+}
+
+// --- decode-size batches (T <= 16): logits on fp32 MFMA.  Workgroup
+// (eg, ks) covers experts 16 eg .. 16 eg + 15 and the ks-th of KS slices of
+// the columns; each of its waves takes every kRouteWaves-th chunk of 16
+// columns of that slice.  v_mfma_f32_16x16x4_f32 with lane (m, g):
+// A = W[16 eg + m][col], B = x[token m][col], col = chunk + 4 g + i for the
+// i-th of the 4 MFMAs of a chunk; D: lane holds experts 4 g + i, token m.
+// Wave partials are added in wave order into part[ks][t][e]; a second,
+// single-workgroup kernel adds the KS slices in order, adds the bias and runs
+// the top-k (the kernel boundary is the cross-workgroup handoff: an in-kernel
+// one needs device-scope fences that write back and invalidate L2).
+typedef float f4v __attribute__((ext_vector_type(4)));
+constexpr int kRouteWaves = 8;
+
+__global__ void __launch_bounds__(64 * kRouteWaves) router_logits_mfma(const float *__restrict__ x, int T, int d,
+                                                                     const float *__restrict__ wr, int E, int KS,
+                                                                     float *__restrict__ part) {
+  __shared__ float red[kRouteWaves][64][4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m = lane & 15, g = lane >> 4;
+  const int eg = blockIdx.x / KS, ks = blockIdx.x % KS;
+  const int e = 16 * eg + m;
+  const int nchunk = d / 16;
+  const int c0 = (int)((long)nchunk * ks / KS), c1 = (int)((long)nchunk * (ks + 1) / KS);
+  f4v acc = {0.f, 0.f, 0.f, 0.f};
+  const float *wrow = wr + (size_t)(e < E ? e : 0) * d;
+  const float *xrow = x + (size_t)(m < T ? m : 0) * d;
+  for (int ch = c0 + wave; ch < c1; ch += kRouteWaves) {
+    const int col = ch * 16 + 4 * g;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+    if (e < E) a = *reinterpret_cast<const float4 *>(wrow + col);
+    if (m < T) b = *reinterpret_cast<const float4 *>(xrow + col);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) red[wave][lane][i] = acc[i];
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = red[0][lane][i];
+      for (int ww = 1; ww < kRouteWaves; ++ww) v += red[ww][lane][i];
+      const int ee = 16 * eg + 4 * g + i, t = m;
+      if (ee < E && t < T) part[((size_t)ks * T + t) * E + ee] = v;
+    }
+  }
+}
+
+// logits = sum of the KS slices (in order) + bias, then top-k, one wave per token
+__global__ void __launch_bounds__(1024) router_finish_small(const float *__restrict__ part, int T, int E, int KS,
+                                                            const float *__restrict__ bias, int k,
+                                                            float *__restrict__ logits, int32_t *__restrict__ idx,
+                                                            float *__restrict__ w) {
+  for (int i = threadIdx.x; i < T * E; i += blockDim.x) {
+    const int t = i / E, ee = i - t * E;
+    float v = part[(size_t)t * E + ee];
+    for (int q = 1; q < KS; ++q) v += part[((size_t)q * T + t) * E + ee];
+    logits[i] = v + (bias ? bias[ee] : 0.f);
+  }
+  __syncthreads();
+  const int wave = threadIdx.x >> 6;
+  for (int t = wave; t < T; t += 16) topk_row(logits + (size_t)t * E, E, k, idx + (size_t)t * k, w + (size_t)t * k);
 }
 
 }  // namespace
@@ -181,13 +189,16 @@ namespace moe {
 hipError_t launch_router(const moe_ctx *c, const float *x, int T, const float *wr, const float *bias, float *logits,
                          int32_t *idx, float *w, hipStream_t s) {
   const int E = c->cfg.n_experts, d = c->cfg.d_model, k = c->cfg.top_k;
-  if (T <= kMaxTSmall) {
-    const int waves = (E + kEpw - 1) / kEpw;
-    hipLaunchKernelGGL(router_logits_small, dim3((waves + 3) / 4), dim3(256), 0, s, x, T, d, wr, bias, E, logits);
-  } else {
-    hipLaunchKernelGGL(router_logits_gemm, dim3((E + kTn - 1) / kTn, (T + kTm - 1) / kTm), dim3(256), 0, s, x, T, d,
-                       wr, bias, E, logits);
+  if (T <= 16) {
+    const int KS = c->route_ks;
+    hipLaunchKernelGGL(router_logits_mfma, dim3(((E + 15) / 16) * KS), dim3(64 * kRouteWaves), 0, s, x, T, d, wr, E,
+                       KS, c->route_part);
+    hipLaunchKernelGGL(router_finish_small, dim3(1), dim3(1024), 0, s, c->route_part, T, E, KS, bias, k, logits, idx,
+                       w);
+    return hipGetLastError();
   }
+  hipLaunchKernelGGL(router_logits_gemm, dim3((E + kTn - 1) / kTn, (T + kTm - 1) / kTm), dim3(256), 0, s, x, T, d, wr,
+                     bias, E, logits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(router_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, idx, w);
