@@ -57,8 +57,8 @@ enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2 };
 typedef struct moe_ctx moe_ctx;
 
 typedef struct {
-  int32_t d_model;      /* multiple of 32, <= 8192 */
-  int32_t d_ff;         /* multiple of 32, <= 8192 */
+  int32_t d_model;      /* multiple of 64, <= 8192 (the blob format itself allows 32) */
+  int32_t d_ff;         /* multiple of 64, <= 8192 */
   int32_t n_experts;    /* routed experts per layer, 1..1024 */
   int32_t top_k;        /* 1..min(n_experts, 32) */
   int32_t n_layers;     /* >= 1 */

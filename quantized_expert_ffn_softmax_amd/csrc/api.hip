@@ -65,8 +65,10 @@ extern "C" moe_status moe_create(const moe_config *cfg, moe_ctx **out) {
   MOE_CHECK(cfg && out, MOE_ERR_INVALID, "moe_create: null cfg or out");
   *out = nullptr;
   const moe_config &k = *cfg;
-  MOE_CHECK(dims_ok(k.d_model, k.d_ff), MOE_ERR_INVALID,
-            "moe_create: d_model and d_ff must be multiples of 32 in [32, 8192]");
+  // the kernels copy a row's scales in 4-byte pieces: an even number of
+  // scale blocks per row keeps every row 4-byte aligned
+  MOE_CHECK(dims_ok(k.d_model, k.d_ff) && k.d_model % 64 == 0 && k.d_ff % 64 == 0, MOE_ERR_INVALID,
+            "moe_create: d_model and d_ff must be multiples of 64 in [64, 8192]");
   MOE_CHECK(k.n_experts >= 1 && k.n_experts <= 1024, MOE_ERR_INVALID, "moe_create: n_experts must be 1..1024");
   MOE_CHECK(k.top_k >= 1 && k.top_k <= k.n_experts && k.top_k <= 32, MOE_ERR_INVALID,
             "moe_create: top_k must be 1..min(n_experts, 32)");
@@ -91,8 +93,8 @@ extern "C" moe_status moe_create(const moe_config *cfg, moe_ctx **out) {
   c->bytes_h2d = 0;
   hipError_t e = hipGetDevice(&c->device);
   c->max_pairs = k.max_tokens * k.top_k;
-  c->max_work = c->max_pairs / 16 + (c->max_pairs < k.n_experts ? c->max_pairs : k.n_experts) +
-                k.max_tokens / 16 + 4;
+  c->max_work = c->max_pairs / moe::kEntryTokens + (c->max_pairs < k.n_experts ? c->max_pairs : k.n_experts) +
+                k.max_tokens / moe::kEntryTokens + 4;
   c->n_chunks_max = (c->max_pairs + 255) / 256;
   const int gsb = c->L.gate.nsb, dsb = c->L.down.nsb;
   const int64_t hrows = (int64_t)c->max_pairs + k.max_tokens;

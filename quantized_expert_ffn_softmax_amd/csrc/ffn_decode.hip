@@ -4,16 +4,20 @@
 // The pages' engine reads each touched expert once per step and shares that
 // read between the tokens that picked it (speculative verify batches several
 // tokens: "单卡5090跑125B 大模型 ...", section 2.3).  Here one wave handles up
-// to 16 tokens of one expert against 16 weight rows with
+// to 8 tokens of one expert against 16 weight rows with
 // v_mfma_f32_16x16x32_f16:
 //   A (16 rows x 32 K)  = dequantised weights fp16((q - 4) * s), built in
 //                         registers from the packed words;
-//   B (32 K x 16 tokens)= activations split into two fp16 halves (hi, lo),
-//                         so a pair of MFMAs keeps them at fp32 accuracy.
+//   B (32 K x 16 cols)  = activations split into two fp16 halves: column n < 8
+//                         holds token n's hi half, column n + 8 its lo half;
+//                         adding the two output columns keeps fp32 accuracy
+//                         with one MFMA per A tile.
 // The layout repeats every 160 columns (16 words, 5 scale blocks): lane group
 // g = lane / 16 takes superblock 4R + g, so every lane runs the same
 // instruction stream; the 80 code pairs (c, c+5) of a superblock are 20 MFMA
 // steps of 4 pairs.  Weights are read once; activations come from L2.
+#include <algorithm>
+
 #include "moe_internal.h"
 #include "record.h"
 
@@ -26,10 +30,6 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 // pair p (0..79) of a superblock: word p/5, slot p%5 (low half) and p%5+5
 // (high half); columns 10 (p/5) + p%5 and +5.
 using moe::pair_col;
-__host__ __device__ constexpr int pair_scale_idx(int p) {
-  // index into the 9 packed scale pairs (b, b) and (b, b+1)
-  return 2 * (pair_col(p) / 32) + ((pair_col(p) + 5) / 32 - pair_col(p) / 32);
-}
 
 struct DecodeParams {
   const moe::WorkEntry *work;
@@ -59,31 +59,24 @@ __device__ inline const uint8_t *entry_blob(const DecodeParams &P, const moe::Wo
   return P.slot_pool + (size_t)slot * P.stride;
 }
 
-// 16 words of superblock S of one row (zero where past the row's words)
-__device__ inline void load_words(const uint8_t *row_codes, int S, int wpr, bool act, uint32_t (&w)[16]) {
+// The 5 block scales of a superblock as R[b] = (s_b, s_b+1) for b < 4 and
+// R[4] = (s_4, s_4).  A code pair needs (s_lo, s_hi) = (s_b, s_b) or
+// (s_b, s_b+1): the first is R[b] read with its low half in both lanes
+// (v_pk_mul op_sel), the second is R[b] itself.  `raw` holds the 5 scales as
+// loaded (zero-extended fp16 bits).
+__device__ inline void pack_scales(const uint32_t (&raw)[5], h2 (&R)[5]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (act && 16 * S + 4 * i < wpr) v = *reinterpret_cast<const uint4 *>(row_codes + (size_t)(16 * S + 4 * i) * 4);
-    w[4 * i + 0] = v.x;
-    w[4 * i + 1] = v.y;
-    w[4 * i + 2] = v.z;
-    w[4 * i + 3] = v.w;
-  }
+  for (int b = 0; b < 4; ++b) R[b] = __builtin_bit_cast(h2, raw[b] | (raw[b + 1] << 16));
+  R[4] = __builtin_bit_cast(h2, raw[4] | (raw[4] << 16));
 }
 
-// the 5 block scales of superblock S, packed as the 9 pairs a code pair uses
-__device__ inline void load_scales(const uint8_t *row_scales, int S, int nblk, bool act, h2 (&sc)[9]) {
-  _Float16 s[5];
-#pragma unroll
-  for (int b = 0; b < 5; ++b) {
-    const int blk = 5 * S + b;
-    s[b] = (act && blk < nblk) ? *reinterpret_cast<const _Float16 *>(row_scales + (size_t)blk * 2) : (_Float16)0.f;
-  }
-#pragma unroll
-  for (int b = 0; b < 5; ++b) {
-    sc[2 * b] = (h2){s[b], s[b]};
-    if (b < 4) sc[2 * b + 1] = (h2){s[b], s[b + 1]};
+template <int p>
+__device__ inline h2 pair_scale(const h2 (&R)[5]) {
+  constexpr int blo = pair_col(p) / 32, bhi = (pair_col(p) + 5) / 32;
+  if constexpr (blo == bhi) {
+    return (h2){R[blo][0], R[blo][0]};
+  } else {
+    return R[blo];
   }
 }
 
@@ -120,69 +113,33 @@ __device__ inline h2 deq_pair(uint32_t src, const Consts &K, h2 sc) {
 }
 
 template <int p>
-__device__ inline h2 deq(const uint32_t (&w)[16], const uint32_t (&w9)[16], const Consts &K, const h2 (&sc)[9]) {
+__device__ inline h2 deq(const uint32_t (&w)[16], const Consts &K, const h2 (&sc)[5]) {
   constexpr int j = p % 5;
-  return deq_pair<j>(j < 3 ? w[p / 5] : w9[p / 5], K, sc[pair_scale_idx(p)]);
+  return deq_pair<j>(j < 3 ? w[p / 5] : (w[p / 5] >> 9), K, pair_scale<p>(sc));
 }
 
 template <int t>
-__device__ inline h8 build_a(const uint32_t (&w)[16], const uint32_t (&w9)[16], const Consts &K, const h2 (&sc)[9]) {
+__device__ inline h8 build_a(const uint32_t (&w)[16], const Consts &K, const h2 (&sc)[5]) {
   constexpr int p0 = 4 * t;
-  const h2 a0 = deq<p0 + 0>(w, w9, K, sc);
-  const h2 a1 = deq<p0 + 1>(w, w9, K, sc);
-  const h2 a2 = deq<p0 + 2>(w, w9, K, sc);
-  const h2 a3 = deq<p0 + 3>(w, w9, K, sc);
+  const h2 a0 = deq<p0 + 0>(w, K, sc);
+  const h2 a1 = deq<p0 + 1>(w, K, sc);
+  const h2 a2 = deq<p0 + 2>(w, K, sc);
+  const h2 a3 = deq<p0 + 3>(w, K, sc);
   return (h8){a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
 }
 
 __device__ inline f4 mfma(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 
-template <int t>
-__device__ inline void load_b(const uint16_t *xs, h8 &bhi, h8 &blo) {
-  // columns without a token point at an all-zero row: same address for all of
-  // them, so the loads coalesce and no register needs zeroing
-  bhi = *reinterpret_cast<const h8 *>(xs + t * 16);
-  blo = *reinterpret_cast<const h8 *>(xs + t * 16 + 8);
-}
-
-template <int t>
-__device__ inline void step2(const uint32_t (&wa)[16], const uint32_t (&wa9)[16], const h2 (&sa)[9],
-                             const uint32_t (&wb)[16], const uint32_t (&wb9)[16], const h2 (&sb)[9],
-                             const Consts &K, const uint16_t *xs, f4 &acca, f4 &accb) {
-  h8 bhi, blo;
-  load_b<t>(xs, bhi, blo);
-  const h8 a = build_a<t>(wa, wa9, K, sa);
-  const h8 b = build_a<t>(wb, wb9, K, sb);
-  acca = mfma(a, bhi, acca);
-  accb = mfma(b, bhi, accb);
-  acca = mfma(a, blo, acca);
-  accb = mfma(b, blo, accb);
-}
-
-template <int t>
-__device__ inline void step1(const uint32_t (&wa)[16], const uint32_t (&wa9)[16], const h2 (&sa)[9],
-                             const Consts &K, const uint16_t *xs, f4 &acc) {
-  h8 bhi, blo;
-  load_b<t>(xs, bhi, blo);
-  const h8 a = build_a<t>(wa, wa9, K, sa);
-  acc = mfma(a, bhi, acc);
-  acc = mfma(a, blo, acc);
-}
-
-__device__ inline void shift9(const uint32_t (&w)[16], uint32_t (&w9)[16]) {
-#pragma unroll
-  for (int i = 0; i < 16; ++i) w9[i] = w[i] >> 9;
-}
-
 using moe::rec_pos;
 
-// the record row (token of x, or pair / shared row of h) behind MFMA column n
 // a work entry is used only if it indexes inside this call's pairs / tokens
 __device__ inline bool entry_ok(const DecodeParams &P, const moe::WorkEntry &we) {
-  if (we.m < 1 || we.m > 16 || we.first < 0) return false;
+  if (we.m < 1 || we.m > moe::kEntryTokens || we.first < 0) return false;
   return we.expert >= 0 ? (we.expert < P.E && we.first + we.m <= P.T * P.k) : (we.first + we.m <= P.T);
 }
 
+// the token and the record row (pair, or T*k + token for the shared expert)
+// behind entry column n
 __device__ inline bool entry_token(const DecodeParams &P, const moe::WorkEntry &we, int n, int &tok, int &row) {
   if (we.expert >= 0) {
     const int pair = P.perm[we.first + n];
@@ -196,173 +153,310 @@ __device__ inline bool entry_token(const DecodeParams &P, const moe::WorkEntry &
   return true;
 }
 
-// One work item = one entry (<= 16 tokens of one expert) x 16 weight rows.
-// The K range is split over the WAVES waves of the workgroup: lane group g of
-// wave w takes superblocks S = 4w + g, 4w + g + 4*WAVES, ...; the partial
-// sums are added in LDS in wave order (deterministic).  MFMA columns without
-// a token issue no activation loads.
+// ---------------------------------------------------------------------------
+// Work decomposition.  A unit is one entry (<= 8 tokens of one expert) times
+// kWaves consecutive 16-row tiles; a workgroup of kWaves waves takes a unit,
+// each wave one tile over the whole K range, so no partial sums cross waves.
+// K is walked in rounds of 4 superblocks: in round R lane group g = lane / 16
+// owns superblock 4R + g (20 MFMA steps).  Per round:
+//   * weights: wave instruction i loads superblock 4R + i of the wave's 16
+//     rows, lane group g taking word quad g -- every row's 64 bytes in one
+//     instruction -- and four v_permlane32/16_swap passes transpose the 4x4
+//     (instruction, lane group) blocks so that lane group g holds the four
+//     quads of superblock 4R + g;
+//   * activations and scales, which the kWaves tiles share, are copied by the
+//     whole workgroup straight into LDS (global_load_lds), activations in the
+//     order [superblock][step][hi, lo][entry column] so that the 8 columns a
+//     read serves sit in 8 consecutive 16-byte slots;
+//   * everything for round R+1 is requested before round R is computed, into
+//     the other LDS buffer and the other register set; one barrier per round.
+// A lane group past the last superblock computes on the last superblock's
+// weights against zero activations and adds exactly 0.  Words of a partial
+// last superblock that lie past the row are read from the bytes that follow
+// it inside the blob (the next row, or the matrix's scale array, at least 64
+// bytes) and also meet zero activations; scale reads are clamped to the row.
+// ---------------------------------------------------------------------------
 
-template <int WAVES>
-__device__ inline void reduce_waves(float (*red)[64][8], int wave, int lane, f4 &a, f4 &b, int nv) {
-  if (WAVES == 1) return;
+constexpr int kWaves = 4;
+constexpr int kXBytes = 4 * moe::kSteps * 2 * 8 * 16;  // one round's activations: 20 KB
+constexpr int kXInst = kXBytes / 1024;                  // 16-byte-per-lane copies of them
+constexpr int kScRowBytes = 40;                         // one row's scales for one round (4 x 5 blocks)
+constexpr int kScInstPerMat = kWaves * 16 * kScRowBytes / 256;  // 4-byte-per-lane copies per matrix
+
+struct Unit {
+  const uint8_t *blob;  // the expert's blob (a readable stand-in when the entry is unusable)
+  int tile0;            // first 16-row tile of the unit
+  int m;                // entry columns in use (0 for an unusable entry)
+  int routed;
+  // this lane's entry column (lane % 8)
+  int has_tok, tok, rrow;
+};
+
+__device__ inline void unit_setup(const DecodeParams &P, int u, int tpu, int tcol, Unit &U) {
+  const moe::WorkEntry we = P.work[u / tpu];
+  U.tile0 = (u % tpu) * kWaves;
+  U.routed = we.expert >= 0;
+  const uint8_t *blob = entry_ok(P, we) ? entry_blob(P, we) : nullptr;
+  U.m = blob ? we.m : 0;
+  U.blob = blob ? blob : P.shared_pool + (size_t)P.layer * P.stride;
+  U.tok = 0;
+  U.rrow = 0;
+  U.has_tok = tcol < U.m && entry_token(P, we, tcol, U.tok, U.rrow);
+}
+
+// matrices of one kernel: gate and up (NMAT 2) or down (NMAT 1)
+template <int NMAT>
+struct Mats {
+  moe::MatLayout m[NMAT];
+  const uint16_t *rec, *zero;  // activation record and its all-zero row
+  int rec_h;
+};
+
+template <int NMAT>
+__device__ inline void stage_round(const DecodeParams &P, const Mats<NMAT> &Mt, const Unit &U, int R, int w, int lane,
+                                   uint8_t *lx, uint8_t *lsc) {
+  const int nsb = Mt.m[0].nsb, nblk = Mt.m[0].nblk, rows = Mt.m[0].rows;
+  // activations: slot p = ((sb * 20 + t) * 2 + half) * 8 + n, n = lane % 8
+  const uint16_t *mine = Mt.rec + (size_t)(NMAT == 2 ? U.tok : U.rrow) * Mt.rec_h + ((lane >> 3) & 1) * 8;
+  for (int q = w; q < kXInst; q += kWaves) {
+    const int p = 64 * q + lane;
+    const int t = (p >> 4) % moe::kSteps, S = 4 * R + (p >> 4) / moe::kSteps;
+    const uint16_t *src = (U.has_tok && S < nsb) ? mine + (size_t)S * moe::kSteps * 16 + t * 16 : Mt.zero;
+    __builtin_amdgcn_global_load_lds(src, lx + 1024 * q, 16, 0, 0);
+  }
+  // scales: dword j of row r of matrix mat at (mat * 64 + r) * 40 + 4 j
+  for (int q = w; q < NMAT * kScInstPerMat; q += kWaves) {
+    const int e = 64 * q + lane;
+    const int mat = e / (kWaves * 16 * 10), rl = (e / 10) % (kWaves * 16), j = e % 10;
+    const moe::MatLayout &M = Mt.m[NMAT == 2 ? mat : 0];
+    const int row = min(U.tile0 * 16 + rl, rows - 1);
+    const int off = min(kScRowBytes * R + 4 * j, 2 * nblk - 4);
+    __builtin_amdgcn_global_load_lds(U.blob + M.scale_off + (size_t)row * nblk * 2 + off, lsc + 256 * q, 4, 0, 0);
+  }
+}
+
+template <int NMAT>
+__device__ inline void load_round_words(const Mats<NMAT> &Mt, const Unit &U, int R, int w, int r16, int g,
+                                        uint4 (&A)[NMAT][4]) {
+  const int nsb = Mt.m[0].nsb, wpr = Mt.m[0].wpr;
+  const int row = min((U.tile0 + w) * 16 + r16, Mt.m[0].rows - 1);
+#pragma unroll
+  for (int mat = 0; mat < NMAT; ++mat) {
+    const uint8_t *base = U.blob + Mt.m[mat].code_off + (size_t)row * wpr * 4 + g * 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) A[mat][i] = *reinterpret_cast<const uint4 *>(base + (size_t)min(4 * R + i, nsb - 1) * 64);
+  }
+}
+
+__device__ inline void swap32(uint32_t &a, uint32_t &b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
+}
+__device__ inline void swap16(uint32_t &a, uint32_t &b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
+}
+
+// A[i] of lane group g = quad g of superblock i  ->  A[j] of lane group g =
+// quad j of superblock g.  permlane32_swap exchanges the upper half-wave of
+// its first operand with the lower half of its second; permlane16_swap the
+// odd 16-lane rows of the first with the even rows of the second.
+__device__ inline void transpose_quads(uint4 (&A)[4]) {
+  swap32(A[0].x, A[2].x); swap32(A[0].y, A[2].y); swap32(A[0].z, A[2].z); swap32(A[0].w, A[2].w);
+  swap32(A[1].x, A[3].x); swap32(A[1].y, A[3].y); swap32(A[1].z, A[3].z); swap32(A[1].w, A[3].w);
+  swap16(A[0].x, A[1].x); swap16(A[0].y, A[1].y); swap16(A[0].z, A[1].z); swap16(A[0].w, A[1].w);
+  swap16(A[2].x, A[3].x); swap16(A[2].y, A[3].y); swap16(A[2].z, A[3].z); swap16(A[2].w, A[3].w);
+}
+
+__device__ inline void words_of(const uint4 (&A)[4], uint32_t (&wd)[16]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    red[wave][lane][i] = a[i];
-    if (nv > 1) red[wave][lane][4 + i] = b[i];
+    wd[4 * i + 0] = A[i].x;
+    wd[4 * i + 1] = A[i].y;
+    wd[4 * i + 2] = A[i].z;
+    wd[4 * i + 3] = A[i].w;
   }
+}
+
+__device__ inline h8 lds_h8(const uint8_t *p) { return *reinterpret_cast<const h8 *>(p); }
+
+// step t: x operand from LDS (read two steps ahead), one MFMA per matrix
+template <int NMAT, int t>
+__device__ inline void lstep(const uint32_t (&wa)[16], const h2 (&sa)[5], const uint32_t (&wb)[16],
+                             const h2 (&sb)[5], const Consts &K, h8 (&xr)[2], const uint8_t *xb, f4 &acc0,
+                             f4 &acc1) {
+  const h8 x = xr[t & 1];
+  if constexpr (t + 2 < moe::kSteps) xr[t & 1] = lds_h8(xb + (t + 2) * 256);
+  if constexpr (NMAT == 2) {
+    acc0 = mfma(build_a<t>(wa, K, sa), x, acc0);
+    acc1 = mfma(build_a<t>(wb, K, sb), x, acc1);
+  } else if constexpr (t % 2 == 0) {
+    acc0 = mfma(build_a<t>(wa, K, sa), x, acc0);
+  } else {
+    acc1 = mfma(build_a<t>(wa, K, sa), x, acc1);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int... ts>
+struct StepSeq {};
+using AllSteps = StepSeq<0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19>;
+
+template <int NMAT, int... ts>
+__device__ inline void lsteps(StepSeq<ts...>, const uint32_t (&wa)[16], const h2 (&sa)[5], const uint32_t (&wb)[16],
+                              const h2 (&sb)[5], const Consts &K, h8 (&xr)[2], const uint8_t *xb, f4 &acc0,
+                              f4 &acc1) {
+  (lstep<NMAT, ts>(wa, sa, wb, sb, K, xr, xb, acc0, acc1), ...);
+}
+
+template <int NMAT>
+__device__ inline void compute_round(const uint4 (&A)[NMAT][4], const uint8_t *lx, const uint8_t *lsc, int w,
+                                     int lane, const Consts &K, f4 &acc0, f4 &acc1) {
+  const int r16 = lane & 15, g = lane >> 4, tcol = lane & 7, half = (lane >> 3) & 1;
+  uint32_t wa[16], wb[16];
+  h2 sa[5], sb[5];
+  words_of(A[0], wa);
+  uint32_t raw[5];
+  const uint8_t *sc = lsc + (w * 16 + r16) * kScRowBytes + g * 10;
+#pragma unroll
+  for (int k = 0; k < 5; ++k) raw[k] = *reinterpret_cast<const uint16_t *>(sc + 2 * k);
+  pack_scales(raw, sa);
+  if constexpr (NMAT == 2) {
+    words_of(A[1], wb);
+#pragma unroll
+    for (int k = 0; k < 5; ++k) raw[k] = *reinterpret_cast<const uint16_t *>(sc + kWaves * 16 * kScRowBytes + 2 * k);
+    pack_scales(raw, sb);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) wb[i] = 0;
+#pragma unroll
+    for (int k = 0; k < 5; ++k) sb[k] = sa[k];
+  }
+  const uint8_t *xb = lx + 16 * ((g * moe::kSteps * 2 + half) * 8 + tcol);
+  h8 xr[2] = {lds_h8(xb), lds_h8(xb + 256)};
+  lsteps<NMAT>(AllSteps{}, wa, sa, wb, sb, K, xr, xb, acc0, acc1);
+}
+
+// gate/up: h = silu(g) u into the h record; down: y
+template <int NMAT>
+__device__ inline void unit_epilogue(const DecodeParams &P, const Unit &U, int w, int lane, f4 acc0, f4 acc1) {
+  const int r16 = lane & 15, g = lane >> 4;
+  const int rows = NMAT == 2 ? P.d_ff : P.d_model;
+  const int rt = U.tile0 + w;
+  // D layout: lane holds rows 4g + i of the tile for MFMA column r16; the
+  // token's value is column r16 (hi) + column r16 + 8 (lo)
+  if constexpr (NMAT == 1) acc0 += acc1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc0[i] += __shfl_xor(acc0[i], 8, 64);
+    if constexpr (NMAT == 2) acc1[i] += __shfl_xor(acc1[i], 8, 64);
+  }
+  if (!(U.has_tok && r16 < 8 && rt * 16 < rows)) return;
+  if constexpr (NMAT == 2) {
+    uint16_t *hr = P.hrec + (size_t)U.rrow * P.hrec_h;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float gv = acc0[i], uv = acc1[i];
+      float inv_f;
+      const int pos = rec_pos(rt * 16 + 4 * g + i, inv_f);
+      const float h = gv / (1.0f + __expf(-gv)) * uv * inv_f;
+      const _Float16 hi = (_Float16)h;
+      const _Float16 lo = (_Float16)(h - (float)hi);
+      hr[pos] = __builtin_bit_cast(uint16_t, hi);
+      hr[pos + 8] = __builtin_bit_cast(uint16_t, lo);
+    }
+  } else {
+    float *y = U.routed ? P.y_pairs + (size_t)U.rrow * P.d_model : P.y_shared + (size_t)U.tok * P.d_model;
+    *reinterpret_cast<float4 *>(y + rt * 16 + 4 * g) = make_float4(acc0[0], acc0[1], acc0[2], acc0[3]);
+  }
+}
+
+__device__ inline void wait_loads_and_sync() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (wave == 0) {
-#pragma unroll
-    for (int w = 1; w < WAVES; ++w)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[i] += red[w][lane][i];
-        if (nv > 1) b[i] += red[w][lane][4 + i];
-      }
-  }
 }
 
-// gate and up for 16 rows of d_ff, then h = silu(g) * u into the h record
-template <int WAVES>
-__global__ void __launch_bounds__(64 * WAVES) ffn_gateup_kernel(DecodeParams P) {
-  __shared__ float red[WAVES][64][8];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r16 = lane & 15, g = lane >> 4;
-  const int ntile = P.d_ff / 16;
-  const int n_items = min(P.n_work[0], P.max_work) * ntile;
-  const int nsb = P.gate.nsb;
-  const int rounds = (nsb + 4 * WAVES - 1) / (4 * WAVES);
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const moe::WorkEntry we = P.work[item / ntile];
-    const int rt = item % ntile;
-    if (!entry_ok(P, we)) continue;
-    const uint8_t *blob = entry_blob(P, we);
-    if (!blob) continue;
-    int tok = 0, hrow = 0;
-    const bool has_tok = r16 < we.m && entry_token(P, we, r16, tok, hrow);
-    const int row = rt * 16 + r16;
-    const uint8_t *gcode = blob + P.gate.code_off + (size_t)row * P.gate.wpr * 4;
-    const uint8_t *ucode = blob + P.up.code_off + (size_t)row * P.up.wpr * 4;
-    const uint8_t *gsc = blob + P.gate.scale_off + (size_t)row * P.gate.nblk * 2;
-    const uint8_t *usc = blob + P.up.scale_off + (size_t)row * P.up.nblk * 2;
-    f4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-    const Consts K = make_consts();
-    for (int R = 0; R < rounds; ++R) {
-      const int S = 4 * WAVES * R + 4 * wave + g;
-      const bool act = S < nsb;
-      uint32_t gw[16], uw[16];
-      h2 gs[9], us[9];
-      load_words(gcode, S, P.gate.wpr, act, gw);
-      load_words(ucode, S, P.up.wpr, act, uw);
-      load_scales(gsc, S, P.gate.nblk, act, gs);
-      load_scales(usc, S, P.up.nblk, act, us);
-      uint32_t gw9[16], uw9[16];
-      shift9(gw, gw9);
-      shift9(uw, uw9);
-      const uint16_t *xs = (act && has_tok) ? P.xrec + (size_t)tok * P.xrec_h + (size_t)S * moe::kSteps * 16
-                                            : P.xrec_zero;
-      step2<0>(gw, gw9, gs, uw, uw9, us, K, xs, accg, accu);
-      step2<1>(gw, gw9, gs, uw, uw9, us, K, xs, accg, accu);
-      step2<2>(gw, gw9, gs, uw, uw9, us, K, xs, accg, accu);
-      step2<3>(gw, gw9, gs, uw, uw9, us, K, xs, accg, accu);
-      step2<4>(gw, gw9, gs, uw, uw9, us, K, xs, accg, accu);
-      step2<5>(gw, gw9, gs, uw, uw9, us, K, xs, accg, accu);
-      step2<6>(gw, gw9, gs, uw, uw9, us, K, xs, accg, accu);
-      step2<7>(gw, gw9, gs, uw, uw9, us, K, xs, accg, accu);
-      step2<8>(gw, gw9, gs, uw, uw9, us, K, xs, accg, accu);
-      step2<9>(gw, gw9, gs, uw, uw9, us, K, xs, accg, accu);
-      step2<10>(gw, gw9, gs, uw, uw9, us, K, xs, accg, accu);
-      step2<11>(gw, gw9, gs, uw, uw9, us, K, xs, accg, accu);
-      step2<12>(gw, gw9, gs, uw, uw9, us, K, xs, accg, accu);
-      step2<13>(gw, gw9, gs, uw, uw9, us, K, xs, accg, accu);
-      step2<14>(gw, gw9, gs, uw, uw9, us, K, xs, accg, accu);
-      step2<15>(gw, gw9, gs, uw, uw9, us, K, xs, accg, accu);
-      step2<16>(gw, gw9, gs, uw, uw9, us, K, xs, accg, accu);
-      step2<17>(gw, gw9, gs, uw, uw9, us, K, xs, accg, accu);
-      step2<18>(gw, gw9, gs, uw, uw9, us, K, xs, accg, accu);
-      step2<19>(gw, gw9, gs, uw, uw9, us, K, xs, accg, accu);
-    }
-    reduce_waves<WAVES>(red, wave, lane, accg, accu, 2);
-    // D layout: lane holds rows 4g + i of the tile for token column r16
-    if (wave == 0 && has_tok) {
-      uint16_t *hr = P.hrec + (size_t)hrow * P.hrec_h;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float gv = accg[i], uv = accu[i];
-        float inv_f;
-        const int pos = rec_pos(rt * 16 + 4 * g + i, inv_f);
-        const float h = gv / (1.0f + __expf(-gv)) * uv * inv_f;
-        const _Float16 hi = (_Float16)h;
-        const _Float16 lo = (_Float16)(h - (float)hi);
-        hr[pos] = __builtin_bit_cast(uint16_t, hi);
-        hr[pos + 8] = __builtin_bit_cast(uint16_t, lo);
-      }
-    }
-    if (WAVES > 1) __syncthreads();  // red is reused by the next item
+template <int NMAT>
+__device__ inline Mats<NMAT> mats_of(const DecodeParams &P) {
+  Mats<NMAT> Mt;
+  if constexpr (NMAT == 2) {
+    Mt.m[0] = P.gate;
+    Mt.m[1] = P.up;
+    Mt.rec = P.xrec;
+    Mt.zero = P.xrec_zero;
+    Mt.rec_h = P.xrec_h;
+  } else {
+    Mt.m[0] = P.down;
+    Mt.rec = P.hrec;
+    Mt.zero = P.hrec_zero;
+    Mt.rec_h = P.hrec_h;
   }
+  return Mt;
 }
 
-// down for 16 rows of d_model: y = W_d h
-template <int WAVES>
-__global__ void __launch_bounds__(64 * WAVES) ffn_down_kernel(DecodeParams P) {
-  __shared__ float red[WAVES][64][8];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// One round of the stream: request (un, Rn) into the other buffers, compute
+// (u, R) from the current ones, finish the unit after its last round.
+// Returns false when the stream ends.
+template <int NMAT>
+__device__ inline bool stream_round(const DecodeParams &P, const Mats<NMAT> &Mt, int tpu, int n_units, int rounds,
+                                    int w, int lane, int &u, int &R, Unit &U, uint8_t *lx_cur, uint8_t *lsc_cur,
+                                    uint8_t *lx_nxt, uint8_t *lsc_nxt, const uint4 (&Acur)[NMAT][4],
+                                    uint4 (&Anxt)[NMAT][4], const Consts &K, f4 &acc0, f4 &acc1) {
   const int r16 = lane & 15, g = lane >> 4;
-  const int ntile = P.d_model / 16;
-  const int n_items = min(P.n_work[0], P.max_work) * ntile;
-  const int nsb = P.down.nsb;
-  const int rounds = (nsb + 4 * WAVES - 1) / (4 * WAVES);
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const moe::WorkEntry we = P.work[item / ntile];
-    const int rt = item % ntile;
-    if (!entry_ok(P, we)) continue;
-    const uint8_t *blob = entry_blob(P, we);
-    if (!blob) continue;
-    int tok = 0, hrow = 0;
-    const bool has_tok = r16 < we.m && entry_token(P, we, r16, tok, hrow);
-    const int row = rt * 16 + r16;
-    const uint8_t *dcode = blob + P.down.code_off + (size_t)row * P.down.wpr * 4;
-    const uint8_t *dsc = blob + P.down.scale_off + (size_t)row * P.down.nblk * 2;
-    f4 acc = {0.f, 0.f, 0.f, 0.f}, unused = {0.f, 0.f, 0.f, 0.f};
-    const Consts K = make_consts();
-    for (int R = 0; R < rounds; ++R) {
-      const int S = 4 * WAVES * R + 4 * wave + g;
-      const bool act = S < nsb;
-      uint32_t dw[16];
-      h2 ds[9];
-      load_words(dcode, S, P.down.wpr, act, dw);
-      load_scales(dsc, S, P.down.nblk, act, ds);
-      uint32_t dw9[16];
-      shift9(dw, dw9);
-      const uint16_t *hs = (act && has_tok) ? P.hrec + (size_t)hrow * P.hrec_h + (size_t)S * moe::kSteps * 16
-                                            : P.hrec_zero;
-      step1<0>(dw, dw9, ds, K, hs, acc);
-      step1<1>(dw, dw9, ds, K, hs, acc);
-      step1<2>(dw, dw9, ds, K, hs, acc);
-      step1<3>(dw, dw9, ds, K, hs, acc);
-      step1<4>(dw, dw9, ds, K, hs, acc);
-      step1<5>(dw, dw9, ds, K, hs, acc);
-      step1<6>(dw, dw9, ds, K, hs, acc);
-      step1<7>(dw, dw9, ds, K, hs, acc);
-      step1<8>(dw, dw9, ds, K, hs, acc);
-      step1<9>(dw, dw9, ds, K, hs, acc);
-      step1<10>(dw, dw9, ds, K, hs, acc);
-      step1<11>(dw, dw9, ds, K, hs, acc);
-      step1<12>(dw, dw9, ds, K, hs, acc);
-      step1<13>(dw, dw9, ds, K, hs, acc);
-      step1<14>(dw, dw9, ds, K, hs, acc);
-      step1<15>(dw, dw9, ds, K, hs, acc);
-      step1<16>(dw, dw9, ds, K, hs, acc);
-      step1<17>(dw, dw9, ds, K, hs, acc);
-      step1<18>(dw, dw9, ds, K, hs, acc);
-      step1<19>(dw, dw9, ds, K, hs, acc);
-    }
-    reduce_waves<WAVES>(red, wave, lane, acc, unused, 1);
-    if (wave == 0 && has_tok) {
-      float *y = we.expert >= 0 ? P.y_pairs + (size_t)hrow * P.d_model : P.y_shared + (size_t)tok * P.d_model;
-      *reinterpret_cast<float4 *>(y + rt * 16 + 4 * g) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    }
-    if (WAVES > 1) __syncthreads();
+  const bool last = R + 1 == rounds;
+  const int un = last ? u + (int)gridDim.x : u;
+  const int Rn = last ? 0 : R + 1;
+  const bool more = un < n_units;
+  Unit Un = U;
+  if (last && more) unit_setup(P, un, tpu, lane & 7, Un);
+  if (more) {
+    stage_round<NMAT>(P, Mt, Un, Rn, w, lane, lx_nxt, lsc_nxt);
+    load_round_words<NMAT>(Mt, Un, Rn, w, r16, g, Anxt);
+  }
+  compute_round<NMAT>(Acur, lx_cur, lsc_cur, w, lane, K, acc0, acc1);
+  if (last) {
+    unit_epilogue<NMAT>(P, U, w, lane, acc0, acc1);
+    acc0 = acc1 = (f4){0.f, 0.f, 0.f, 0.f};
+  }
+  if (!more) return false;
+  wait_loads_and_sync();
+#pragma unroll
+  for (int mat = 0; mat < NMAT; ++mat) transpose_quads(Anxt[mat]);
+  u = un;
+  R = Rn;
+  U = Un;
+  return true;
+}
+
+template <int NMAT>
+__global__ void __launch_bounds__(64 * kWaves) ffn_decode_kernel(DecodeParams P) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lx[2][kXBytes];
+  __shared__ __attribute__((aligned(256))) uint8_t lsc[2][NMAT * kScInstPerMat * 256];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const Mats<NMAT> Mt = mats_of<NMAT>(P);
+  const int ntile = Mt.m[0].rows / 16;
+  const int tpu = (ntile + kWaves - 1) / kWaves;
+  const int rounds = (Mt.m[0].nsb + 3) / 4;
+  const int n_units = min(P.n_work[0], P.max_work) * tpu;
+  int u = blockIdx.x, R = 0;
+  if (u >= n_units) return;
+  Unit U;
+  unit_setup(P, u, tpu, lane & 7, U);
+  uint4 A0[NMAT][4], A1[NMAT][4];
+  stage_round<NMAT>(P, Mt, U, 0, w, lane, lx[0], lsc[0]);
+  load_round_words<NMAT>(Mt, U, 0, w, lane & 15, lane >> 4, A0);
+  wait_loads_and_sync();
+#pragma unroll
+  for (int mat = 0; mat < NMAT; ++mat) transpose_quads(A0[mat]);
+  const Consts K = make_consts();
+  f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  // the two register sets and LDS buffers alternate by round
+  while (stream_round<NMAT>(P, Mt, tpu, n_units, rounds, w, lane, u, R, U, lx[0], lsc[0], lx[1], lsc[1], A0, A1, K,
+                            acc0, acc1) &&
+         stream_round<NMAT>(P, Mt, tpu, n_units, rounds, w, lane, u, R, U, lx[1], lsc[1], lx[0], lsc[0], A1, A0, K,
+                            acc0, acc1)) {
   }
 }
 
@@ -386,25 +480,12 @@ namespace moe {
 hipError_t launch_bucket_ex(const moe_ctx *c, const int32_t *idx, int T, int32_t *offsets, int32_t *perm, bool build,
                             int entry_m, const float *x, uint16_t *xrec, int xrec_h, hipStream_t s);
 
-template <int WAVES>
-static void launch_pair(int g1, int g2, int waves_down, const DecodeParams &P, hipStream_t s) {
-  hipLaunchKernelGGL(ffn_gateup_kernel<WAVES>, dim3(g1), dim3(64 * WAVES), 0, s, P);
-  if (waves_down == 1)
-    hipLaunchKernelGGL(ffn_down_kernel<1>, dim3(g2), dim3(64), 0, s, P);
-  else if (waves_down == 2)
-    hipLaunchKernelGGL(ffn_down_kernel<2>, dim3(g2), dim3(128), 0, s, P);
-  else
-    hipLaunchKernelGGL(ffn_down_kernel<4>, dim3(g2), dim3(256), 0, s, P);
-}
-
-static int waves_for(int nsb) { return nsb <= 4 ? 1 : (nsb <= 8 ? 2 : 4); }
-
 hipError_t launch_ffn_decode(const moe_ctx *c, int layer, const float *x, int T, const int32_t *idx,
                              const int32_t *slot_of_pair, float *y_pairs, float *y_shared, hipStream_t s) {
   const moe_config &k = c->cfg;
   const int xh = xrec_halves(c->L.gate.nsb);
   // bucketing, work list and (on the single-workgroup path) the x record in one launch
-  hipError_t e = launch_bucket_ex(c, idx, T, c->offsets_ws, c->perm_ws, true, 16, x, c->xrec, xh, s);
+  hipError_t e = launch_bucket_ex(c, idx, T, c->offsets_ws, c->perm_ws, true, moe::kEntryTokens, x, c->xrec, xh, s);
   if (e != hipSuccess) return e;
   if (T * k.top_k > 1024) {
     const int n = T * c->L.gate.nsb * kSteps * 8;
@@ -438,17 +519,14 @@ hipError_t launch_ffn_decode(const moe_ctx *c, int layer, const float *x, int T,
   P.y_shared = y_shared;
   P.d_model = k.d_model;
   P.d_ff = k.d_ff;
-  const int ents = max_entries(T, k.top_k, k.n_experts, 16);
-  const int items1 = ents * (k.d_ff / 16), items2 = ents * (k.d_model / 16);
-  const int cap = 4096;  // persistent grid: workgroups loop over items
-  const int g1 = items1 < cap ? items1 : cap, g2 = items2 < cap ? items2 : cap;
-  const int w1 = waves_for(c->L.gate.nsb), w2 = waves_for(c->L.down.nsb);
-  if (w1 == 1)
-    launch_pair<1>(g1, g2, w2, P, s);
-  else if (w1 == 2)
-    launch_pair<2>(g1, g2, w2, P, s);
-  else
-    launch_pair<4>(g1, g2, w2, P, s);
+  const int ents = max_entries(T, k.top_k, k.n_experts, moe::kEntryTokens);
+  // one unit (entry x 4 tiles) per workgroup while that fits; beyond,
+  // workgroups loop over units and overlap one unit's start with the previous
+  // unit's last round
+  const int cap = 768;
+  const int u1 = ents * ((k.d_ff / 16 + kWaves - 1) / kWaves), u2 = ents * ((k.d_model / 16 + kWaves - 1) / kWaves);
+  hipLaunchKernelGGL(ffn_decode_kernel<2>, dim3(std::min(u1, cap)), dim3(64 * kWaves), 0, s, P);
+  hipLaunchKernelGGL(ffn_decode_kernel<1>, dim3(std::min(u2, cap)), dim3(64 * kWaves), 0, s, P);
   return hipGetLastError();
 }
 

@@ -68,12 +68,14 @@ inline BlobLayout make_layout(int d_model, int d_ff) {
 // being (c, c+5) with c = 160 S + 10 (p / 5) + p % 5.
 inline int xrec_halves(int nsb) { return nsb * kSteps * 16; }
 
-// One unit of decode work: up to 16 tokens of one expert (or of the shared
-// expert) in one layer.
+// One unit of decode work: up to kEntryTokens tokens of one expert (or of the
+// shared expert) in one layer.  The decode kernels put a token's hi half in
+// MFMA column n and its lo half in column n + 8, hence 8.
+constexpr int kEntryTokens = 8;
 struct WorkEntry {
   int32_t expert;  // routed expert index, or -1 for the shared expert
   int32_t first;   // routed: index into perm of the first pair; shared: first token
-  int32_t m;       // tokens in this entry, 1..16
+  int32_t m;       // tokens in this entry, 1..kEntryTokens
   int32_t pad;
 };
 

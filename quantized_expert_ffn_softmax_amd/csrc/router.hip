@@ -166,20 +166,65 @@ __global__ void __launch_bounds__(64 * kRouteWaves) router_logits_mfma(const flo
   }
 }
 
-// logits = sum of the KS slices (in order) + bias, then top-k, one wave per token
+// One workgroup per token: logits = sum of the KS slices (in order) + bias,
+// then the top-k by rank, where an expert's rank is the number of experts
+// ordered before it by (logit desc, index asc).  Two passes: each wave ranks
+// its 64 experts among themselves; an expert of global rank < k has wave rank
+// < k, so only those candidates (k per wave) are ranked against each other,
+// and for a candidate in the global top-k that rank is its global rank (every
+// expert ordered before it is a candidate too).  Weights: softmax of the k
+// chosen logits.
+__device__ inline bool before(float u, int ou, float v, int ov) { return u > v || (u == v && ou < ov); }
+
 __global__ void __launch_bounds__(1024) router_finish_small(const float *__restrict__ part, int T, int E, int KS,
                                                             const float *__restrict__ bias, int k,
                                                             float *__restrict__ logits, int32_t *__restrict__ idx,
                                                             float *__restrict__ w) {
-  for (int i = threadIdx.x; i < T * E; i += blockDim.x) {
-    const int t = i / E, ee = i - t * E;
-    float v = part[(size_t)t * E + ee];
-    for (int q = 1; q < KS; ++q) v += part[((size_t)q * T + t) * E + ee];
-    logits[i] = v + (bias ? bias[ee] : 0.f);
+  __shared__ float lg[1024];
+  __shared__ float cv[16 * 32];
+  __shared__ int ci[16 * 32];
+  __shared__ float top[32];
+  const int t = blockIdx.x, e = threadIdx.x, wave = e >> 6;
+  float v = -INFINITY;
+  if (e < E) {
+    v = part[(size_t)t * E + e];
+    for (int q = 1; q < KS; ++q) v += part[((size_t)q * T + t) * E + e];
+    v += bias ? bias[e] : 0.f;
+    logits[(size_t)t * E + e] = v;
+  }
+  lg[e] = v;
+  __syncthreads();
+  // pass 1: rank inside the wave
+  int r1 = 0;
+  for (int o = wave * 64; o < wave * 64 + 64; ++o) r1 += before(lg[o], o, v, e);
+  const int nw = blockDim.x / 64;
+  for (int i = e; i < nw * k; i += blockDim.x) ci[i] = -1;
+  __syncthreads();
+  if (e < E && r1 < k) {
+    cv[wave * k + r1] = v;
+    ci[wave * k + r1] = e;
   }
   __syncthreads();
-  const int wave = threadIdx.x >> 6;
-  for (int t = wave; t < T; t += 16) topk_row(logits + (size_t)t * E, E, k, idx + (size_t)t * k, w + (size_t)t * k);
+  // pass 2: rank among the candidates
+  if (e < E && r1 < k) {
+    int r = 0;
+    for (int i = 0; i < nw * k; ++i) {
+      const int o = ci[i];
+      if (o >= 0) r += before(cv[i], o, v, e);
+    }
+    r1 = r;  // global rank when < k
+    if (r < k) top[r] = v;
+  } else {
+    r1 = k;
+  }
+  __syncthreads();
+  if (e < E && r1 < k) {
+    const float m = top[0];
+    float sum = 0.f;
+    for (int j = 0; j < k; ++j) sum += expf(top[j] - m);
+    idx[(size_t)t * k + r1] = e;
+    w[(size_t)t * k + r1] = expf(v - m) / sum;
+  }
 }
 
 }  // namespace
@@ -193,8 +238,8 @@ hipError_t launch_router(const moe_ctx *c, const float *x, int T, const float *w
     const int KS = c->route_ks;
     hipLaunchKernelGGL(router_logits_mfma, dim3(((E + 15) / 16) * KS), dim3(64 * kRouteWaves), 0, s, x, T, d, wr, E,
                        KS, c->route_part);
-    hipLaunchKernelGGL(router_finish_small, dim3(1), dim3(1024), 0, s, c->route_part, T, E, KS, bias, k, logits, idx,
-                       w);
+    hipLaunchKernelGGL(router_finish_small, dim3(T), dim3((E + 63) / 64 * 64), 0, s, c->route_part, T, E, KS, bias,
+                       k, logits, idx, w);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(router_logits_gemm, dim3((E + kTn - 1) / kTn, (T + kTm - 1) / kTm), dim3(256), 0, s, x, T, d, wr,

@@ -56,6 +56,7 @@ def _cfg(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(d_model=33), B.MOE_ERR_INVALID),
+    (dict(d_model=96), B.MOE_ERR_INVALID),   # a valid blob shape, but rows of an odd number of scale blocks
     (dict(d_ff=8200), B.MOE_ERR_INVALID),
     (dict(n_experts=0), B.MOE_ERR_INVALID),
     (dict(n_experts=2000), B.MOE_ERR_INVALID),
