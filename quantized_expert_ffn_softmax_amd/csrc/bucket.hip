@@ -81,8 +81,15 @@ __global__ void __launch_bounds__(kBucketThreads) bucket_small(const int32_t *__
   if (tid <= E) offsets[tid] = off[tid];
   if (tid < n && ex[tid] >= 0) {
     const int e = ex[tid];
+    // stable rank among the pairs of expert e; 16 LDS reads in flight at once
     int r = 0;
-    for (int q = 0; q < tid; ++q) r += ex[q] == e;  // same address for all lanes: broadcast
+    for (int q0 = 0; q0 < tid; q0 += 16) {
+      int v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = ex[min(q0 + i, kSmallMax - 1)];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) r += (q0 + i < tid) && v[i] == e;
+    }
     perm[off[e] + r] = tid;
   }
   if (build) build_work(cnt, off, E, T, entry_m, work, n_work, sh);

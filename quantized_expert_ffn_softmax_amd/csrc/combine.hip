@@ -9,23 +9,35 @@
 namespace {
 
 // out[t][c..c+3] = sum_j w[t][j] * y_pairs[t*k+j][c..c+3] + y_shared[t][c..c+3]
-__global__ void __launch_bounds__(256) combine_kernel(const float *__restrict__ y_pairs, const float *__restrict__ w,
+// The k rows are requested 8 at a time before any is used (k <= 32), and the
+// sum runs in ascending j with the shared row added last.
+__global__ void __launch_bounds__(64) combine_kernel(const float *__restrict__ y_pairs, const float *__restrict__ w,
                                                       const float *__restrict__ y_shared, int T, int k, int d,
                                                       float *__restrict__ out) {
   const int d4 = d / 4;
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= T * d4) return;
   const int t = i / d4, c4 = i % d4;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; ++j) {
-    const float wj = w[(size_t)t * k + j];
-    const float4 y = reinterpret_cast<const float4 *>(y_pairs + ((size_t)t * k + j) * d)[c4];
-    acc.x = fmaf(wj, y.x, acc.x);
-    acc.y = fmaf(wj, y.y, acc.y);
-    acc.z = fmaf(wj, y.z, acc.z);
-    acc.w = fmaf(wj, y.w, acc.w);
-  }
+  const float4 *yp = reinterpret_cast<const float4 *>(y_pairs + (size_t)t * k * d) + c4;
   const float4 s = reinterpret_cast<const float4 *>(y_shared + (size_t)t * d)[c4];
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    float4 y[8];
+    float wj[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool ok = j0 + j < k;
+      y[j] = ok ? yp[(size_t)(j0 + j) * d4] : make_float4(0.f, 0.f, 0.f, 0.f);
+      wj[j] = ok ? w[(size_t)t * k + j0 + j] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      acc.x = fmaf(wj[j], y[j].x, acc.x);
+      acc.y = fmaf(wj[j], y[j].y, acc.y);
+      acc.z = fmaf(wj[j], y[j].z, acc.z);
+      acc.w = fmaf(wj[j], y[j].w, acc.w);
+    }
+  }
   acc.x += s.x;
   acc.y += s.y;
   acc.z += s.z;
@@ -45,21 +57,42 @@ __device__ inline float block_sum_256(float v, float *part) {
   return tot;
 }
 
+// The row is read once into registers (d <= 8192: at most 8 float4 per
+// thread), then reduced twice and written.
 __global__ void __launch_bounds__(256) chain_norm_kernel(const float *__restrict__ out, int d,
                                                          float *__restrict__ x_next) {
   __shared__ float part[4];
   const int t = blockIdx.x;
-  const float *row = out + (size_t)t * d;
+  const int d4 = d / 4;
+  const float4 *row = reinterpret_cast<const float4 *>(out + (size_t)t * d);
+  float4 v[8];
   float s = 0.f;
-  for (int c = threadIdx.x; c < d; c += blockDim.x) s += row[c];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    v[i] = c < d4 ? row[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
   const float mean = block_sum_256(s, part) / (float)d;
   float ss = 0.f;
-  for (int c = threadIdx.x; c < d; c += blockDim.x) {
-    const float v = row[c] - mean;
-    ss = fmaf(v, v, ss);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (threadIdx.x + 256 * i < d4) {
+      v[i].x -= mean;
+      v[i].y -= mean;
+      v[i].z -= mean;
+      v[i].w -= mean;
+      ss = fmaf(v[i].x, v[i].x, fmaf(v[i].y, v[i].y, fmaf(v[i].z, v[i].z, fmaf(v[i].w, v[i].w, ss))));
+    }
   }
   const float inv = 1.0f / sqrtf(block_sum_256(ss, part) / (float)d + 1e-6f);
-  for (int c = threadIdx.x; c < d; c += blockDim.x) x_next[(size_t)t * d + c] = (row[c] - mean) * inv;
+  float4 *o = reinterpret_cast<float4 *>(x_next + (size_t)t * d);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    if (c < d4) o[c] = make_float4(v[i].x * inv, v[i].y * inv, v[i].z * inv, v[i].w * inv);
+  }
 }
 
 }  // namespace
@@ -68,8 +101,9 @@ namespace moe {
 
 hipError_t launch_combine(const float *y_pairs, const float *w, const float *y_shared, int T, int k, int d, float *out,
                           hipStream_t s) {
+  // one wave per workgroup: few tokens still spread their rows over many CUs
   const int n = T * (d / 4);
-  hipLaunchKernelGGL(combine_kernel, dim3((n + 255) / 256), dim3(256), 0, s, y_pairs, w, y_shared, T, k, d, out);
+  hipLaunchKernelGGL(combine_kernel, dim3((n + 63) / 64), dim3(64), 0, s, y_pairs, w, y_shared, T, k, d, out);
   return hipGetLastError();
 }
 

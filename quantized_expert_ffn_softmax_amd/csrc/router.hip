@@ -187,8 +187,15 @@ __global__ void __launch_bounds__(1024) router_finish_small(const float *__restr
   const int t = blockIdx.x, e = threadIdx.x, wave = e >> 6;
   float v = -INFINITY;
   if (e < E) {
-    v = part[(size_t)t * E + e];
-    for (int q = 1; q < KS; ++q) v += part[((size_t)q * T + t) * E + e];
+    // the KS partial sums, requested 8 at a time and added in slice order
+    v = 0.f;
+    for (int q0 = 0; q0 < KS; q0 += 8) {
+      float p[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p[i] = q0 + i < KS ? part[((size_t)(q0 + i) * T + t) * E + e] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v += p[i];
+    }
     v += bias ? bias[e] : 0.f;
     logits[(size_t)t * E + e] = v;
   }
@@ -207,10 +214,18 @@ __global__ void __launch_bounds__(1024) router_finish_small(const float *__restr
   __syncthreads();
   // pass 2: rank among the candidates
   if (e < E && r1 < k) {
+    // candidates read 16 at a time so the LDS reads overlap
     int r = 0;
-    for (int i = 0; i < nw * k; ++i) {
-      const int o = ci[i];
-      if (o >= 0) r += before(cv[i], o, v, e);
+    for (int i0 = 0; i0 < nw * k; i0 += 16) {
+      int o[16];
+      float c[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        o[i] = i0 + i < nw * k ? ci[i0 + i] : -1;
+        c[i] = i0 + i < nw * k ? cv[i0 + i] : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) r += (o[i] >= 0) && before(c[i], o[i], v, e);
     }
     r1 = r;  // global rank when < k
     if (r < k) top[r] = v;
