@@ -32,12 +32,10 @@ project's design notes):
 * expert: y = W_d (silu(W_g x) * W_u x); the shared expert is ungated (weight 1)
   and is added after the k routed terms, taken in ascending j;
 * cache: LRU with the tie rules documented on ``LRUCache``;
-* precision: 'exact' is float64 on the exactly dequantised weights; the
-  reduced modes model where the GPU paths round operands to fp16, with all
-  arithmetic after the rounding still in float64: 'fp16_weights' rounds each
-  weight (q - 4) s; 'fp16_qs' rounds the product q s and subtracts 4 s
-  exactly (the same weight, split at a different place); 'fp16_operands'
-  rounds x, W and h.
+* precision: 'exact' is float64 on the exactly dequantised weights; the two
+  reduced modes model where the GPU paths round operands to fp16
+  ('fp16_weights': W rounded; 'fp16_operands': x, W and h rounded), with all
+  arithmetic after the rounding still in float64.
 """
 from __future__ import annotations
 
@@ -91,30 +89,25 @@ def unpack_codes(words: np.ndarray, cols: int) -> np.ndarray:
 
 
 def dequant_matrix(blob: np.ndarray, rows: int, cols: int, code_off: int, scale_off: int,
-                   fp16_round=False) -> np.ndarray:
+                   fp16_round: bool = False) -> np.ndarray:
     """W[r][c] = (q[r][c] - 4) * scale[r][c // 32], exact in float64.
 
-    ``fp16_round`` True (or "product") rounds each product once to fp16 (round
-    to nearest even); "code_product" rounds q * s to fp16 instead and then
-    subtracts 4 s exactly.
+    With ``fp16_round`` each product is rounded once to fp16 (round to
+    nearest even), the operand the GPU's MFMA paths consume.
     """
     wpr = words_per_row(cols)
     words = np.frombuffer(blob, dtype=np.uint32, count=rows * wpr, offset=code_off).reshape(rows, wpr)
     scales = np.frombuffer(blob, dtype=np.float16, count=rows * (cols // SCALE_BLOCK),
                            offset=scale_off).reshape(rows, cols // SCALE_BLOCK).astype(np.float64)
     q = unpack_codes(words, cols)
-    s_full = np.repeat(scales, SCALE_BLOCK, axis=1)
-    if fp16_round == "code_product":
-        return (q.astype(np.float64) * s_full).astype(np.float16).astype(np.float64) - 4.0 * s_full
-    w = (q - 4).astype(np.float64) * s_full
+    w = (q - 4).astype(np.float64) * np.repeat(scales, SCALE_BLOCK, axis=1)
     if fp16_round:
         w = w.astype(np.float16).astype(np.float64)
     return w
 
 
-def expert_weights(blob: np.ndarray, d_model: int, d_ff: int, fp16_round=False):
-    """(W_gate [f][d], W_up [f][d], W_down [d][f]) as float64 (rounding as in
-    ``dequant_matrix``)."""
+def expert_weights(blob: np.ndarray, d_model: int, d_ff: int, fp16_round: bool = False):
+    """(W_gate [f][d], W_up [f][d], W_down [d][f]) as float64."""
     secs, stride = blob_sections(d_model, d_ff)
     if blob.size < stride:
         raise ValueError("blob shorter than its layout")
@@ -309,8 +302,6 @@ def expert_ffn(x_rows: np.ndarray, weights, precision: str = "exact") -> np.ndar
     ``weights`` are the float64 matrices from ``expert_weights`` (already
     fp16-rounded for the reduced modes).  'fp16_operands' also rounds x and h.
     """
-    if precision not in ("exact", "fp16_weights", "fp16_qs", "fp16_operands"):
-        raise ValueError(f"unknown precision {precision!r}")
     wg, wu, wd = weights
     x = np.asarray(x_rows, dtype=np.float64)
     if precision == "fp16_operands":
@@ -360,12 +351,11 @@ def moe_layer(x, w_router, bias, k, blob_of_expert, shared_blob, d_model, d_ff,
     w = np.asarray(w, dtype=np.float64)
     y_pairs = np.zeros((T * k, d_model), dtype=np.float64)
     flat = idx.reshape(-1)
-    rounding = {"exact": False, "fp16_qs": "code_product"}.get(precision, True)
     for e in sorted(set(int(v) for v in flat)):
         pairs = np.nonzero(flat == e)[0]
-        wts = expert_weights(blob_of_expert(e), d_model, d_ff, fp16_round=rounding)
+        wts = expert_weights(blob_of_expert(e), d_model, d_ff, fp16_round=(precision != "exact"))
         y_pairs[pairs] = expert_ffn(x[pairs // k], wts, precision)
-    wts = expert_weights(shared_blob, d_model, d_ff, fp16_round=rounding)
+    wts = expert_weights(shared_blob, d_model, d_ff, fp16_round=(precision != "exact"))
     y_shared = expert_ffn(x, wts, precision)
     out = combine(y_pairs, w, y_shared)
     return dict(logits=lg, idx=idx, w=w, y_pairs=y_pairs, y_shared=y_shared, out=out.astype(np.float32),

@@ -98,31 +98,6 @@ def test_fp16_modes_equal_exact_when_operands_representable():
     assert np.array_equal(ex, fw)
 
 
-def test_fp16_qs_rounds_the_code_product():
-    # 'fp16_qs' keeps every weight within half an fp16 ulp of q*s of the exact
-    # value, w + 4 s lies on the fp16 grid, and it is exact whenever q*s is.
-    d, f = 64, 32
-    rng = np.random.default_rng(15)
-    blob, codes, scales = _blob_from_codes(d, f, rng)
-    sec = oracle.blob_sections(d, f)[0]
-    for (_n, rows, cols, co, so), q, sc in zip(sec, codes, scales):
-        ex = oracle.dequant_matrix(blob, rows, cols, co, so)
-        qs = oracle.dequant_matrix(blob, rows, cols, co, so, "code_product")
-        s_full = np.repeat(sc.astype(np.float64), 32, axis=1)
-        qsv = q * s_full
-        assert np.all(np.abs(qs - ex) <= np.abs(qsv) * 2.0 ** -11)
-        on_grid = qs + 4.0 * s_full
-        assert np.array_equal(on_grid.astype(np.float16).astype(np.float64), on_grid)
-        pw2 = oracle.dequant_matrix(blob, rows, cols, co, so, "product")
-        assert not np.array_equal(qs, pw2)  # the two splits round differently
-    # power-of-two scales: q*s is exact, so the mode equals 'exact'
-    blob2, _, _ = _blob_from_codes(d, f, rng, scale=0.0625)
-    x = rng.standard_normal((2, d)).astype(np.float32)
-    ex = oracle.expert_ffn(x, oracle.expert_weights(blob2, d, f), "exact")
-    qs = oracle.expert_ffn(x, oracle.expert_weights(blob2, d, f, "code_product"), "fp16_qs")
-    assert np.array_equal(ex, qs)
-
-
 def _layer_inputs(d, f, E, T, seed=0):
     rng = np.random.default_rng(seed)
     blobs = [moe_synth.gen_blob(seed, 0, e, d, f) for e in range(E)]
