@@ -180,8 +180,9 @@ __device__ inline bool entry_token(const DecodeParams &P, const moe::WorkEntry &
 constexpr int kWaves = 4;
 constexpr int kXBytes = 4 * moe::kSteps * 2 * 8 * 16;  // one round's activations: 20 KB
 constexpr int kXInst = kXBytes / 1024;                  // 16-byte-per-lane copies of them
-constexpr int kScRowBytes = 40;                         // one row's scales for one round (4 x 5 blocks)
-constexpr int kScInstPerMat = kWaves * 16 * kScRowBytes / 256;  // 4-byte-per-lane copies per matrix
+constexpr int kScDwords = 10;                           // one row's scales for one round: 4 x 5 blocks, 40 bytes
+constexpr int kScBytesPerMat = kScDwords * kWaves * 16 * 4;
+static_assert(kXInst % kWaves == 0, "activation copies split evenly over the waves");
 
 struct Unit {
   const uint8_t *blob;  // the expert's blob (a readable stand-in when the entry is unusable)
@@ -190,10 +191,17 @@ struct Unit {
   int routed;
   // this lane's entry column (lane % 8)
   int has_tok, tok, rrow;
+  // byte offsets inside a matrix: this lane's weight row (+ its quad) and,
+  // for the scale copies, row tile0 * 16 + lane
+  uint32_t w_off, s_off;
 };
 
-__device__ inline void unit_setup(const DecodeParams &P, int u, int tpu, int tcol, Unit &U) {
+template <int NMAT>
+struct Mats;
+
+__device__ inline void unit_setup(const DecodeParams &P, const moe::MatLayout &M0, int u, int tpu, int lane, Unit &U) {
   const moe::WorkEntry we = P.work[u / tpu];
+  const int w = threadIdx.x >> 6, r16 = lane & 15, g = lane >> 4;
   U.tile0 = (u % tpu) * kWaves;
   U.routed = we.expert >= 0;
   const uint8_t *blob = entry_ok(P, we) ? entry_blob(P, we) : nullptr;
@@ -201,7 +209,11 @@ __device__ inline void unit_setup(const DecodeParams &P, int u, int tpu, int tco
   U.blob = blob ? blob : P.shared_pool + (size_t)P.layer * P.stride;
   U.tok = 0;
   U.rrow = 0;
-  U.has_tok = tcol < U.m && entry_token(P, we, tcol, U.tok, U.rrow);
+  U.has_tok = (lane & 7) < U.m && entry_token(P, we, lane & 7, U.tok, U.rrow);
+  const int wrow = min((U.tile0 + w) * 16 + r16, M0.rows - 1);
+  U.w_off = (uint32_t)wrow * M0.wpr * 4 + g * 16;
+  const int srow = min(U.tile0 * 16 + lane, M0.rows - 1);
+  U.s_off = (uint32_t)srow * M0.nblk * 2;
 }
 
 // matrices of one kernel: gate and up (NMAT 2) or down (NMAT 1)
@@ -212,40 +224,47 @@ struct Mats {
   int rec_h;
 };
 
+// Activation copy i of wave w moves slots p = 64 (w + 4 i) + lane, slot
+// p = ((sb * 20 + t) * 2 + half) * 8 + n with n = lane % 8; since the record
+// is contiguous in (superblock, step), the source is step m = 16 i + 4 w +
+// lane / 16 counted from the round's first superblock.
+// Scale copy q = mat * 10 + j moves dword j of the round's 40 scale bytes of
+// rows tile0 * 16 + lane; LDS holds them as [mat][j][64 rows].
 template <int NMAT>
-__device__ inline void stage_round(const DecodeParams &P, const Mats<NMAT> &Mt, const Unit &U, int R, int w, int lane,
-                                   uint8_t *lx, uint8_t *lsc) {
-  const int nsb = Mt.m[0].nsb, nblk = Mt.m[0].nblk, rows = Mt.m[0].rows;
-  // activations: slot p = ((sb * 20 + t) * 2 + half) * 8 + n, n = lane % 8
-  const uint16_t *mine = Mt.rec + (size_t)(NMAT == 2 ? U.tok : U.rrow) * Mt.rec_h + ((lane >> 3) & 1) * 8;
-  for (int q = w; q < kXInst; q += kWaves) {
-    const int p = 64 * q + lane;
-    const int t = (p >> 4) % moe::kSteps, S = 4 * R + (p >> 4) / moe::kSteps;
-    const uint16_t *src = (U.has_tok && S < nsb) ? mine + (size_t)S * moe::kSteps * 16 + t * 16 : Mt.zero;
-    __builtin_amdgcn_global_load_lds(src, lx + 1024 * q, 16, 0, 0);
+__device__ inline void stage_round(const Mats<NMAT> &Mt, const Unit &U, int R, int w, int lane, uint8_t *lx,
+                                   uint8_t *lsc) {
+  const int nsb = Mt.m[0].nsb, nblk = Mt.m[0].nblk;
+  const uint16_t *mine = Mt.rec + (size_t)(NMAT == 2 ? U.tok : U.rrow) * Mt.rec_h + ((lane >> 3) & 1) * 8 +
+                         (size_t)R * 4 * moe::kSteps * 16;
+  const int m0 = 4 * w + (lane >> 4);
+  const int lim = U.has_tok ? moe::kSteps * (nsb - 4 * R) : 0;  // steps of the round that exist
+#pragma unroll
+  for (int i = 0; i < kXInst / kWaves; ++i) {
+    const int m = 16 * i + m0;
+    const uint16_t *src = m < lim ? mine + m * 16 : Mt.zero;
+    __builtin_amdgcn_global_load_lds(src, lx + 1024 * (w + kWaves * i), 16, 0, 0);
   }
-  // scales: dword j of row r of matrix mat at (mat * 64 + r) * 40 + 4 j
-  for (int q = w; q < NMAT * kScInstPerMat; q += kWaves) {
-    const int e = 64 * q + lane;
-    const int mat = e / (kWaves * 16 * 10), rl = (e / 10) % (kWaves * 16), j = e % 10;
-    const moe::MatLayout &M = Mt.m[NMAT == 2 ? mat : 0];
-    const int row = min(U.tile0 * 16 + rl, rows - 1);
-    const int off = min(kScRowBytes * R + 4 * j, 2 * nblk - 4);
-    __builtin_amdgcn_global_load_lds(U.blob + M.scale_off + (size_t)row * nblk * 2 + off, lsc + 256 * q, 4, 0, 0);
+#pragma unroll
+  for (int i = 0; i < (NMAT * kScDwords + kWaves - 1) / kWaves; ++i) {
+    const int q = w + kWaves * i;
+    if (q < NMAT * kScDwords) {
+      const int mat = q / kScDwords, j = q % kScDwords;
+      const uint32_t off = Mt.m[NMAT == 2 ? mat : 0].scale_off + min(kScDwords * 4 * R + 4 * j, 2 * nblk - 4);
+      __builtin_amdgcn_global_load_lds(U.blob + off + U.s_off, lsc + 256 * q, 4, 0, 0);
+    }
   }
 }
 
 template <int NMAT>
-__device__ inline void load_round_words(const Mats<NMAT> &Mt, const Unit &U, int R, int w, int r16, int g,
-                                        uint4 (&A)[NMAT][4]) {
-  const int nsb = Mt.m[0].nsb, wpr = Mt.m[0].wpr;
-  const int row = min((U.tile0 + w) * 16 + r16, Mt.m[0].rows - 1);
+__device__ inline void load_round_words(const Mats<NMAT> &Mt, const Unit &U, int R, uint4 (&A)[NMAT][4]) {
+  const int nsb = Mt.m[0].nsb;
 #pragma unroll
-  for (int mat = 0; mat < NMAT; ++mat) {
-    const uint8_t *base = U.blob + Mt.m[mat].code_off + (size_t)row * wpr * 4 + g * 16;
+  for (int mat = 0; mat < NMAT; ++mat)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) A[mat][i] = *reinterpret_cast<const uint4 *>(base + (size_t)min(4 * R + i, nsb - 1) * 64);
-  }
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t off = Mt.m[mat].code_off + min(4 * R + i, nsb - 1) * 64;
+      A[mat][i] = *reinterpret_cast<const uint4 *>(U.blob + off + U.w_off);
+    }
 }
 
 __device__ inline void swap32(uint32_t &a, uint32_t &b) {
@@ -318,15 +337,22 @@ __device__ inline void compute_round(const uint4 (&A)[NMAT][4], const uint8_t *l
   uint32_t wa[16], wb[16];
   h2 sa[5], sb[5];
   words_of(A[0], wa);
+  // block 5 g + k of the round sits in dword (5 g + k) / 2, half (5 g + k) % 2
   uint32_t raw[5];
-  const uint8_t *sc = lsc + (w * 16 + r16) * kScRowBytes + g * 10;
+  const uint8_t *sc = lsc + (w * 16 + r16) * 4;
 #pragma unroll
-  for (int k = 0; k < 5; ++k) raw[k] = *reinterpret_cast<const uint16_t *>(sc + 2 * k);
+  for (int k = 0; k < 5; ++k) {
+    const int b = 5 * g + k;
+    raw[k] = *reinterpret_cast<const uint16_t *>(sc + (b >> 1) * 256 + (b & 1) * 2);
+  }
   pack_scales(raw, sa);
   if constexpr (NMAT == 2) {
     words_of(A[1], wb);
 #pragma unroll
-    for (int k = 0; k < 5; ++k) raw[k] = *reinterpret_cast<const uint16_t *>(sc + kWaves * 16 * kScRowBytes + 2 * k);
+    for (int k = 0; k < 5; ++k) {
+      const int b = 5 * g + k;
+      raw[k] = *reinterpret_cast<const uint16_t *>(sc + kScBytesPerMat + (b >> 1) * 256 + (b & 1) * 2);
+    }
     pack_scales(raw, sb);
   } else {
 #pragma unroll
@@ -404,16 +430,15 @@ __device__ inline bool stream_round(const DecodeParams &P, const Mats<NMAT> &Mt,
                                     int w, int lane, int &u, int &R, Unit &U, uint8_t *lx_cur, uint8_t *lsc_cur,
                                     uint8_t *lx_nxt, uint8_t *lsc_nxt, const uint4 (&Acur)[NMAT][4],
                                     uint4 (&Anxt)[NMAT][4], const Consts &K, f4 &acc0, f4 &acc1) {
-  const int r16 = lane & 15, g = lane >> 4;
   const bool last = R + 1 == rounds;
   const int un = last ? u + (int)gridDim.x : u;
   const int Rn = last ? 0 : R + 1;
   const bool more = un < n_units;
   Unit Un = U;
-  if (last && more) unit_setup(P, un, tpu, lane & 7, Un);
+  if (last && more) unit_setup(P, Mt.m[0], un, tpu, lane, Un);
   if (more) {
-    stage_round<NMAT>(P, Mt, Un, Rn, w, lane, lx_nxt, lsc_nxt);
-    load_round_words<NMAT>(Mt, Un, Rn, w, r16, g, Anxt);
+    stage_round<NMAT>(Mt, Un, Rn, w, lane, lx_nxt, lsc_nxt);
+    load_round_words<NMAT>(Mt, Un, Rn, Anxt);
   }
   compute_round<NMAT>(Acur, lx_cur, lsc_cur, w, lane, K, acc0, acc1);
   if (last) {
@@ -431,9 +456,9 @@ __device__ inline bool stream_round(const DecodeParams &P, const Mats<NMAT> &Mt,
 }
 
 template <int NMAT>
-__global__ void __launch_bounds__(64 * kWaves) ffn_decode_kernel(DecodeParams P) {
+__global__ void __launch_bounds__(64 * kWaves, 3) ffn_decode_kernel(DecodeParams P) {
   __shared__ __attribute__((aligned(1024))) uint8_t lx[2][kXBytes];
-  __shared__ __attribute__((aligned(256))) uint8_t lsc[2][NMAT * kScInstPerMat * 256];
+  __shared__ __attribute__((aligned(256))) uint8_t lsc[2][NMAT * kScBytesPerMat];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const Mats<NMAT> Mt = mats_of<NMAT>(P);
   const int ntile = Mt.m[0].rows / 16;
@@ -443,10 +468,10 @@ __global__ void __launch_bounds__(64 * kWaves) ffn_decode_kernel(DecodeParams P)
   int u = blockIdx.x, R = 0;
   if (u >= n_units) return;
   Unit U;
-  unit_setup(P, u, tpu, lane & 7, U);
+  unit_setup(P, Mt.m[0], u, tpu, lane, U);
   uint4 A0[NMAT][4], A1[NMAT][4];
-  stage_round<NMAT>(P, Mt, U, 0, w, lane, lx[0], lsc[0]);
-  load_round_words<NMAT>(Mt, U, 0, w, lane & 15, lane >> 4, A0);
+  stage_round<NMAT>(Mt, U, 0, w, lane, lx[0], lsc[0]);
+  load_round_words<NMAT>(Mt, U, 0, A0);
   wait_loads_and_sync();
 #pragma unroll
   for (int mat = 0; mat < NMAT; ++mat) transpose_quads(A0[mat]);
