@@ -38,6 +38,25 @@ def algo_blob_bytes(d_model, d_ff):
     return weights * (3.2 + 0.5) / 8.0
 
 
+def recorded_traffic():
+    """HBM bytes per decode moe_expert_ffn call from the committed counter
+    summary, or None when the summary is missing or the kernel sources it was
+    taken on have changed since (their sha256 is stored with the figure)."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "decode_ffn_T15_traffic.md")
+    try:
+        text = open(path).read()
+        rec = json.loads(re.search(r"```json\n(.*?)```", text, re.S).group(1))
+        h = hashlib.sha256()
+        for f in rec["sources"]:
+            with open(os.path.join(ROOT, "quantized_expert_ffn_softmax_amd", "csrc", f), "rb") as fh:
+                h.update(fh.read())
+        return int(rec["traffic"]) if h.hexdigest() == rec["sha256"] else None
+    except (OSError, ValueError, KeyError, AttributeError):
+        return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,7 +208,8 @@ def main():
                    "seed": seed},
         "roofline": {"bound": "hbm", "kernel": "moe_expert_ffn (decode path)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "bytes_per_launch": round(bytes_per_call), "avg_launch_us": round(ffn_avg_ms * 1e3, 2),
                      "distinct_experts_per_layer": round(uniq / calls, 2),
                      "measured_in": "eager timed region (HIP events around each moe_expert_ffn call)",

@@ -170,14 +170,15 @@ __device__ inline bool entry_token(const DecodeParams &P, const moe::WorkEntry &
 //     read serves sit in 8 consecutive 16-byte slots;
 //   * everything for round R+1 is requested before round R is computed, into
 //     the other LDS buffer and the other register set; one barrier per round.
-// A lane group past the last superblock computes on the last superblock's
-// weights against zero activations and adds exactly 0.  Words of a partial
+// A lane group past the last superblock computes on zero words against zero
+// activations and adds exactly 0.  Words of a partial
 // last superblock that lie past the row are read from the bytes that follow
 // it inside the blob (the next row, or the matrix's scale array, at least 64
 // bytes) and also meet zero activations; scale reads are clamped to the row.
 // ---------------------------------------------------------------------------
 
 constexpr int kWaves = 4;
+constexpr int kXcds = 8;  // accelerator dies of MI355X, each with its own L2
 constexpr int kXBytes = 4 * moe::kSteps * 2 * 8 * 16;  // one round's activations: 20 KB
 constexpr int kXInst = kXBytes / 1024;                  // 16-byte-per-lane copies of them
 constexpr int kScDwords = 10;                           // one row's scales for one round: 4 x 5 blocks, 40 bytes
@@ -262,8 +263,10 @@ __device__ inline void load_round_words(const Mats<NMAT> &Mt, const Unit &U, int
   for (int mat = 0; mat < NMAT; ++mat)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t off = Mt.m[mat].code_off + min(4 * R + i, nsb - 1) * 64;
-      A[mat][i] = *reinterpret_cast<const uint4 *>(U.blob + off + U.w_off);
+      // past the last superblock: no load (the activations there are zero)
+      A[mat][i] = make_uint4(0u, 0u, 0u, 0u);
+      if (4 * R + i < nsb)
+        A[mat][i] = *reinterpret_cast<const uint4 *>(U.blob + Mt.m[mat].code_off + (4 * R + i) * 64 + U.w_off);
     }
 }
 
@@ -426,14 +429,15 @@ __device__ inline Mats<NMAT> mats_of(const DecodeParams &P) {
 // (u, R) from the current ones, finish the unit after its last round.
 // Returns false when the stream ends.
 template <int NMAT>
-__device__ inline bool stream_round(const DecodeParams &P, const Mats<NMAT> &Mt, int tpu, int n_units, int rounds,
+__device__ inline bool stream_round(const DecodeParams &P, const Mats<NMAT> &Mt, int tpu, int u_end, int u_step,
+                                    int rounds,
                                     int w, int lane, int &u, int &R, Unit &U, uint8_t *lx_cur, uint8_t *lsc_cur,
                                     uint8_t *lx_nxt, uint8_t *lsc_nxt, const uint4 (&Acur)[NMAT][4],
                                     uint4 (&Anxt)[NMAT][4], const Consts &K, f4 &acc0, f4 &acc1) {
   const bool last = R + 1 == rounds;
-  const int un = last ? u + (int)gridDim.x : u;
+  const int un = last ? u + u_step : u;
   const int Rn = last ? 0 : R + 1;
-  const bool more = un < n_units;
+  const bool more = un < u_end;
   Unit Un = U;
   if (last && more) unit_setup(P, Mt.m[0], un, tpu, lane, Un);
   if (more) {
@@ -465,8 +469,15 @@ __global__ void __launch_bounds__(64 * kWaves, 3) ffn_decode_kernel(DecodeParams
   const int tpu = (ntile + kWaves - 1) / kWaves;
   const int rounds = (Mt.m[0].nsb + 3) / 4;
   const int n_units = min(P.n_work[0], P.max_work) * tpu;
-  int u = blockIdx.x, R = 0;
-  if (u >= n_units) return;
+  // Workgroup b runs on XCD b % 8 (round-robin dispatch).  Each XCD takes a
+  // contiguous range of units, so the tiles of neighbouring entries -- both
+  // entries of an expert with more than 8 tokens, or of the shared expert --
+  // stream through one L2 and the second read of a blob hits it.
+  const int per = (n_units + kXcds - 1) / kXcds;
+  const int xcd = blockIdx.x % kXcds, u_step = gridDim.x / kXcds;
+  const int u_end = min((xcd + 1) * per, n_units);
+  int u = xcd * per + blockIdx.x / kXcds, R = 0;
+  if (u >= u_end) return;
   Unit U;
   unit_setup(P, Mt.m[0], u, tpu, lane, U);
   uint4 A0[NMAT][4], A1[NMAT][4];
@@ -478,10 +489,10 @@ __global__ void __launch_bounds__(64 * kWaves, 3) ffn_decode_kernel(DecodeParams
   const Consts K = make_consts();
   f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   // the two register sets and LDS buffers alternate by round
-  while (stream_round<NMAT>(P, Mt, tpu, n_units, rounds, w, lane, u, R, U, lx[0], lsc[0], lx[1], lsc[1], A0, A1, K,
-                            acc0, acc1) &&
-         stream_round<NMAT>(P, Mt, tpu, n_units, rounds, w, lane, u, R, U, lx[1], lsc[1], lx[0], lsc[0], A1, A0, K,
-                            acc0, acc1)) {
+  while (stream_round<NMAT>(P, Mt, tpu, u_end, u_step, rounds, w, lane, u, R, U, lx[0], lsc[0], lx[1], lsc[1], A0,
+                            A1, K, acc0, acc1) &&
+         stream_round<NMAT>(P, Mt, tpu, u_end, u_step, rounds, w, lane, u, R, U, lx[1], lsc[1], lx[0], lsc[0], A1,
+                            A0, K, acc0, acc1)) {
   }
 }
 
@@ -548,10 +559,11 @@ hipError_t launch_ffn_decode(const moe_ctx *c, int layer, const float *x, int T,
   // one unit (entry x 4 tiles) per workgroup while that fits; beyond,
   // workgroups loop over units and overlap one unit's start with the previous
   // unit's last round
-  const int cap = 768;
+  const int cap = 768;  // three workgroups per CU; a multiple of kXcds
+  auto grid = [&](int units) { return (std::min(units, cap) + kXcds - 1) / kXcds * kXcds; };
   const int u1 = ents * ((k.d_ff / 16 + kWaves - 1) / kWaves), u2 = ents * ((k.d_model / 16 + kWaves - 1) / kWaves);
-  hipLaunchKernelGGL(ffn_decode_kernel<2>, dim3(std::min(u1, cap)), dim3(64 * kWaves), 0, s, P);
-  hipLaunchKernelGGL(ffn_decode_kernel<1>, dim3(std::min(u2, cap)), dim3(64 * kWaves), 0, s, P);
+  hipLaunchKernelGGL(ffn_decode_kernel<2>, dim3(grid(u1)), dim3(64 * kWaves), 0, s, P);
+  hipLaunchKernelGGL(ffn_decode_kernel<1>, dim3(grid(u2)), dim3(64 * kWaves), 0, s, P);
   return hipGetLastError();
 }
 

@@ -65,15 +65,18 @@ __device__ inline bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
-// top-k of one token by one wave; lane l holds the logits of experts l, l+64,
-// ... in v (-inf past E)
-__device__ void topk_vals(const float (&v)[kMaxPerLane], int E, int k, int32_t *__restrict__ idx_row,
-                          float *__restrict__ w_row) {
+// top-k of one token's row by one wave
+__device__ void topk_row(const float *__restrict__ row, int E, int k, int32_t *__restrict__ idx_row,
+                         float *__restrict__ w_row) {
   const int lane = threadIdx.x & 63;
+  float v[kMaxPerLane];
   uint32_t taken = 0;
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i)
-    if (lane + i * kWave >= E) taken |= 1u << i;
+  for (int i = 0; i < kMaxPerLane; ++i) {
+    const int e = lane + i * kWave;
+    v[i] = e < E ? row[e] : -INFINITY;
+    if (e >= E) taken |= 1u << i;
+  }
   float top_v = 0.f;
   float my_v = 0.f;
   int my_i = -1;
@@ -104,20 +107,6 @@ __device__ void topk_vals(const float (&v)[kMaxPerLane], int E, int k, int32_t *
     idx_row[lane] = my_i;
     w_row[lane] = ex / sum;
   }
-}
-
-
-// top-k of one token's row (global memory) by one wave
-__device__ void topk_row(const float *__restrict__ row, int E, int k, int32_t *__restrict__ idx_row,
-                         float *__restrict__ w_row) {
-  const int lane = threadIdx.x & 63;
-  float v[kMaxPerLane];
-#pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
-    const int e = lane + i * kWave;
-    v[i] = e < E ? row[e] : -INFINITY;
-  }
-  topk_vals(v, E, k, idx_row, w_row);
 }
 
 __global__ void __launch_bounds__(256) router_topk(const float *__restrict__ logits, int T, int E, int k,
@@ -177,42 +166,80 @@ __global__ void __launch_bounds__(64 * kRouteWaves) router_logits_mfma(const flo
   }
 }
 
-// One wave per token: logits = the KS slices added in slice order, plus the
-// bias; written out, then the wave's top-k (as for large batches).
-__global__ void __launch_bounds__(64) router_finish_small(const float *__restrict__ part, int T, int E, int KS,
-                                                          const float *__restrict__ bias, int k,
-                                                          float *__restrict__ logits, int32_t *__restrict__ idx,
-                                                          float *__restrict__ w) {
-  const int t = blockIdx.x, lane = threadIdx.x;
-  float v[kMaxPerLane];
+// One workgroup per token: logits = sum of the KS slices (in order) + bias,
+// then the top-k by rank, where an expert's rank is the number of experts
+// ordered before it by (logit desc, index asc).  Two passes: each wave ranks
+// its 64 experts among themselves; an expert of global rank < k has wave rank
+// < k, so only those candidates (k per wave) are ranked against each other,
+// and for a candidate in the global top-k that rank is its global rank (every
+// expert ordered before it is a candidate too).  Weights: softmax of the k
+// chosen logits.
+__device__ inline bool before(float u, int ou, float v, int ov) { return u > v || (u == v && ou < ov); }
+
+__global__ void __launch_bounds__(1024) router_finish_small(const float *__restrict__ part, int T, int E, int KS,
+                                                            const float *__restrict__ bias, int k,
+                                                            float *__restrict__ logits, int32_t *__restrict__ idx,
+                                                            float *__restrict__ w) {
+  __shared__ float lg[1024];
+  __shared__ float cv[16 * 32];
+  __shared__ int ci[16 * 32];
+  __shared__ float top[32];
+  const int t = blockIdx.x, e = threadIdx.x, wave = e >> 6;
+  float v = -INFINITY;
+  if (e < E) {
+    // the KS partial sums, requested 8 at a time and added in slice order
+    v = 0.f;
+    for (int q0 = 0; q0 < KS; q0 += 8) {
+      float p[8];
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) v[i] = 0.f;
-  // four slices per batch of loads: 4 x 16 requests in flight per lane
-  for (int q0 = 0; q0 < KS; q0 += 4) {
-    float p[4][kMaxPerLane];
+      for (int i = 0; i < 8; ++i) p[i] = q0 + i < KS ? part[((size_t)(q0 + i) * T + t) * E + e] : 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int i = 0; i < 8; ++i) v += p[i];
+    }
+    v += bias ? bias[e] : 0.f;
+    logits[(size_t)t * E + e] = v;
+  }
+  lg[e] = v;
+  __syncthreads();
+  // pass 1: rank inside the wave
+  int r1 = 0;
+  for (int o = wave * 64; o < wave * 64 + 64; ++o) r1 += before(lg[o], o, v, e);
+  const int nw = blockDim.x / 64;
+  for (int i = e; i < nw * k; i += blockDim.x) ci[i] = -1;
+  __syncthreads();
+  if (e < E && r1 < k) {
+    cv[wave * k + r1] = v;
+    ci[wave * k + r1] = e;
+  }
+  __syncthreads();
+  // pass 2: rank among the candidates
+  if (e < E && r1 < k) {
+    // candidates read 16 at a time so the LDS reads overlap
+    int r = 0;
+    for (int i0 = 0; i0 < nw * k; i0 += 16) {
+      int o[16];
+      float c[16];
 #pragma unroll
-      for (int i = 0; i < kMaxPerLane; ++i) {
-        const int e = lane + i * kWave;
-        p[j][i] = (q0 + j < KS && e < E) ? part[((size_t)(q0 + j) * T + t) * E + e] : 0.f;
+      for (int i = 0; i < 16; ++i) {
+        o[i] = i0 + i < nw * k ? ci[i0 + i] : -1;
+        c[i] = i0 + i < nw * k ? cv[i0 + i] : 0.f;
       }
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < kMaxPerLane; ++i) v[i] += p[j][i];
-  }
-#pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
-    const int e = lane + i * kWave;
-    if (e < E) {
-      v[i] += bias ? bias[e] : 0.f;
-      logits[(size_t)t * E + e] = v[i];
-    } else {
-      v[i] = -INFINITY;
+      for (int i = 0; i < 16; ++i) r += (o[i] >= 0) && before(c[i], o[i], v, e);
     }
+    r1 = r;  // global rank when < k
+    if (r < k) top[r] = v;
+  } else {
+    r1 = k;
   }
-  topk_vals(v, E, k, idx + (size_t)t * k, w + (size_t)t * k);
+  __syncthreads();
+  if (e < E && r1 < k) {
+    const float m = top[0];
+    float sum = 0.f;
+    for (int j = 0; j < k; ++j) sum += expf(top[j] - m);
+    idx[(size_t)t * k + r1] = e;
+    w[(size_t)t * k + r1] = expf(v - m) / sum;
+  }
 }
 
 }  // namespace
@@ -226,8 +253,8 @@ hipError_t launch_router(const moe_ctx *c, const float *x, int T, const float *w
     const int KS = c->route_ks;
     hipLaunchKernelGGL(router_logits_mfma, dim3(((E + 15) / 16) * KS), dim3(64 * kRouteWaves), 0, s, x, T, d, wr, E,
                        KS, c->route_part);
-    hipLaunchKernelGGL(router_finish_small, dim3(T), dim3(64), 0, s, c->route_part, T, E, KS, bias, k, logits, idx,
-                       w);
+    hipLaunchKernelGGL(router_finish_small, dim3(T), dim3((E + 63) / 64 * 64), 0, s, c->route_part, T, E, KS, bias,
+                       k, logits, idx, w);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(router_logits_gemm, dim3((E + kTn - 1) / kTn, (T + kTm - 1) / kTm), dim3(256), 0, s, x, T, d, wr,
