@@ -68,6 +68,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-layer", action="store_true", help="skip the single-layer T=5 decode measurement")
+    ap.add_argument("--no-lru", action="store_true", help="skip the T=1 stack through the 8,445-slot LRU cache")
+    ap.add_argument("--lru-steps", type=int, default=256)
+    ap.add_argument("--lru-warmup", type=int, default=64)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -185,6 +189,7 @@ def main():
             gev[s_][1].record()
         torch.cuda.synchronize()
         graph_ms = float(np.mean([a.elapsed_time(b) for a, b in gev]))
+        del graph
         log(f"[bench] decode stack (graph): {graph_ms:.3f} ms/step, {T / (graph_ms * 1e-3):.0f} tok/s")
     ms_per_step = graph_ms if graph_ms is not None else eager_ms
     value = T / (ms_per_step * 1e-3)
@@ -248,10 +253,142 @@ def main():
         log(f"[bench] prefill chunk: layer {layer_ms:.2f} ms ({prefill_T / (layer_ms * 1e-3):.0f} tok/s), "
             f"FFN {ffn_p_ms:.2f} ms = {tflops:.1f} TFLOP/s")
 
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(seed, d, f, E, k, T, alpha, xs[W].cpu().numpy(), args.cpu_sample_layers)
+    if not args.no_layer:
+        result["decode_layer"] = bench_decode_layer(ctx, routers[0], seed, d, f, E, k)
+    cpu_x = xs[W].cpu().numpy()
     ctx.close()
+    del ctx, slot_pool, buf, xs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if not args.no_lru:
+        result["decode_lru"] = bench_lru(seed, d, f, E, k, L, routers, biases, shared_pool, args.lru_warmup,
+                                         args.lru_steps)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(seed, d, f, E, k, T, alpha, cpu_x, args.cpu_sample_layers)
     print(json.dumps(result), flush=True)
+
+
+def bench_decode_layer(ctx, router, seed, d, f, E, k, reps=200):
+    """One real layer at T = 5 (one request: 1 + 4 draft tokens), no router
+    bias, a fresh x per repetition: route -> resolve -> expert FFN -> combine."""
+    import numpy as np
+    import torch
+
+    import moe_synth
+    from quantized_expert_ffn_softmax_amd import binding as B
+    wl = moe_synth.WORKLOADS["decode_layer"]
+    T = wl["n_tokens"]
+    c = ctx.ctx
+    xs = [torch.from_numpy(moe_synth.gen_x(seed, 200000 + r, T, d)).cuda() for r in range(reps + 10)]
+    buf = ctx.buffers(T)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps + 10)]
+    st0 = None
+    for r in range(reps + 10):
+        if r == 10:
+            torch.cuda.synchronize()
+            st0 = B.moe_get_stats(c)
+        e = ev[r]
+        e[0].record()
+        B.moe_route(c, 0, xs[r], T, router, None, None, buf["idx"], buf["w"])
+        B.moe_cache_resolve(c, 0, buf["idx"], T, None)
+        e[1].record()
+        B.moe_expert_ffn(c, 0, xs[r], T, buf["idx"], None, buf["y_pairs"], buf["y_shared"], B.MOE_PATH_DECODE)
+        e[2].record()
+        B.moe_combine(c, buf["y_pairs"], buf["w"], buf["y_shared"], T, buf["out"])
+    torch.cuda.synchronize()
+    st1 = B.moe_get_stats(c)
+    layer_us = float(np.mean([ev[r][0].elapsed_time(ev[r][2]) for r in range(10, reps + 10)])) * 1e3
+    ffn_us = float(np.mean([ev[r][1].elapsed_time(ev[r][2]) for r in range(10, reps + 10)])) * 1e3
+    uniq = (st1["lookups"] - st0["lookups"]) / reps
+    gbs = (uniq + 1) * algo_blob_bytes(d, f) / (ffn_us * 1e-6) / 1e9
+    log(f"[bench] decode layer T={T}: route+resolve+ffn {layer_us:.1f} us, ffn {ffn_us:.1f} us for "
+        f"{uniq:.1f} + 1 experts -> {gbs:.0f} GB/s")
+    return {"workload": "decode_layer", "tokens": T, "reps": reps, "route_resolve_ffn_us": round(layer_us, 2),
+            "ffn_us": round(ffn_us, 2), "distinct_experts": round(uniq, 2), "ffn_hbm_gbs": round(gbs, 1),
+            "ffn_hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def bench_lru(seed, d, f, E, k, L, routers, biases, shared_pool, warmup, steps):
+    """The 48-layer stack at T = 1 through an LRU cache of 8,445 slots; all
+    24,576 blobs in pinned host memory, misses copied on the library's side
+    stream.  Cold start: the cache begins empty."""
+    import numpy as np
+    import torch
+
+    import moe_synth
+    from moe_synth.harness import fill_pool
+    from quantized_expert_ffn_softmax_amd import binding as B
+    from quantized_expert_ffn_softmax_amd.runtime import MoeContext
+    wl = moe_synth.WORKLOADS["decode_stack_lru"]
+    T, S = wl["n_tokens"], wl["n_slots"]
+    t0 = time.time()
+    stride = B.moe_expert_bytes(d, f)
+    log(f"[bench] lru: pinning {L * E} blobs ({L * E * stride / 1e9:.1f} GB) in host memory, {S} slots in HBM")
+    host = torch.empty((L * E, stride), dtype=torch.uint8, pin_memory=True)
+    for l0 in range(0, L, 8):
+        fill_pool(host[l0 * E:(l0 + 8) * E], list(range(l0 * E, (l0 + 8) * E)), seed, d, f, E, chunk=512)
+    slot_pool = torch.empty((S, stride), dtype=torch.uint8, device="cuda")
+    ctx = MoeContext(d, f, E, k, L, S, T, host_store=host, slot_pool=slot_pool, shared_pool=shared_pool)
+    c = ctx.ctx
+    buf = ctx.buffers(T)
+    xa = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    xb = torch.empty_like(xa)
+    # pinned H2D peak for reference: 256 MiB, host -> device
+    hsrc = host[:(1 << 28) // stride].reshape(-1)
+    dst = torch.empty(hsrc.numel(), dtype=torch.uint8, device="cuda")
+    dst.copy_(hsrc, non_blocking=True)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(3):
+        dst.copy_(hsrc, non_blocking=True)
+    b.record()
+    torch.cuda.synchronize()
+    h2d_peak = 3 * hsrc.numel() / (a.elapsed_time(b) * 1e-3) / 1e9
+    del dst
+    log(f"[bench] lru: setup {time.time() - t0:.0f}s; pinned H2D peak {h2d_peak:.1f} GB/s")
+
+    def step(x0):
+        x = x0
+        for l in range(L):
+            B.moe_route(c, l, x, T, routers[l], biases[l], None, buf["idx"], buf["w"])
+            B.moe_cache_resolve(c, l, buf["idx"], T, buf["slot"])
+            B.moe_expert_ffn(c, l, x, T, buf["idx"], buf["slot"], buf["y_pairs"], buf["y_shared"],
+                             B.MOE_PATH_DECODE)
+            B.moe_combine(c, buf["y_pairs"], buf["w"], buf["y_shared"], T, buf["out"])
+            xn = xa if (l % 2 == 0) else xb
+            B.moe_chain_norm(c, buf["out"], T, xn)
+            x = xn
+
+    xs = [torch.from_numpy(moe_synth.gen_x(seed, 300000 + s, T, d)).cuda() for s in range(warmup + steps)]
+    torch.cuda.synchronize()
+    st0 = B.moe_get_stats(c)
+    for s_ in range(warmup):
+        step(xs[s_])
+    torch.cuda.synchronize()
+    st1 = B.moe_get_stats(c)
+    t1 = time.time()
+    for s_ in range(steps):
+        step(xs[warmup + s_])
+    torch.cuda.synchronize()
+    wall = time.time() - t1
+    st2 = B.moe_get_stats(c)
+    cold = (st1["hits"] - st0["hits"]) / max(1, st1["lookups"] - st0["lookups"])
+    lookups, hits = st2["lookups"] - st1["lookups"], st2["hits"] - st1["hits"]
+    h2d = st2["bytes_h2d"] - st1["bytes_h2d"]
+    hit_bytes = (lookups + L * steps) * algo_blob_bytes(d, f)
+    out = {"workload": "decode_stack_lru", "tokens_per_step": T, "layers": L, "slots": S, "steps": steps,
+           "warmup": warmup, "tok_per_s": round(T * steps / wall, 2), "ms_per_step": round(wall / steps * 1e3, 3),
+           "hit_rate": round(hits / max(1, lookups), 4), "cold_start_hit_rate": round(cold, 4),
+           "misses_per_token": round((lookups - hits) / (T * steps), 2),
+           "h2d_gbs": round(h2d / wall / 1e9, 2), "h2d_peak_gbs": round(h2d_peak, 2),
+           "hit_path_hbm_gbs": round(hit_bytes / wall / 1e9, 1),
+           "timing": "host wall clock (a capped resolve waits for its kernel to read the miss list)"}
+    log(f"[bench] lru: {out['tok_per_s']} tok/s ({out['ms_per_step']} ms/step), hit rate {out['hit_rate']:.4f} "
+        f"(cold start {cold:.4f}), {out['misses_per_token']} misses/token, H2D {out['h2d_gbs']} GB/s "
+        f"(peak {h2d_peak:.1f})")
+    ctx.close()
+    del host, slot_pool
+    return out
 
 
 def cpu_baseline(seed, d, f, E, k, T, alpha, x0, n_layers):
