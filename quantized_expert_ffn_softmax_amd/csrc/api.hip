@@ -117,8 +117,9 @@ extern "C" moe_status moe_create(const moe_config *cfg, moe_ctx **out) {
   const size_t hrec_n = (size_t)(hrows + 1) * moe::xrec_halves(dsb);
   TRY(dalloc(&c->xrec, xrec_n));
   TRY(dalloc(&c->hrec, hrec_n));
-  TRY(dalloc(&c->x16, (size_t)k.max_tokens * k.d_model));
-  TRY(dalloc(&c->h16, (size_t)hrows * k.d_ff));
+  // prefill operands in pair order, rows padded to whole superblocks
+  TRY(dalloc(&c->x16, (size_t)k.max_tokens * gsb * moe::kSbCols));
+  TRY(dalloc(&c->h16, (size_t)hrows * dsb * moe::kSbCols));
   c->max_tiles = (int)((hrows + 127) / 128 + k.n_experts + 2);
   TRY(dalloc(&c->tile_ws, (size_t)c->max_tiles * 4 + 4));
   TRY(dalloc(&c->slot_ws, c->max_pairs));
@@ -145,6 +146,7 @@ extern "C" moe_status moe_create(const moe_config *cfg, moe_ctx **out) {
   // record positions past a matrix's columns are never written: they stay zero
   TRY(hipMemset(c->xrec, 0, xrec_n * sizeof(uint16_t)));
   TRY(hipMemset(c->hrec, 0, hrec_n * sizeof(uint16_t)));
+  TRY(hipMemset(c->h16, 0, (size_t)hrows * dsb * moe::kSbCols * sizeof(uint16_t)));  // pad slots stay zero
   TRY(hipDeviceSynchronize());
 #undef TRY
   if (e != hipSuccess) {

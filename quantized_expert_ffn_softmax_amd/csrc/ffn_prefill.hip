@@ -11,17 +11,37 @@
 // once; products and sums are fp32 (v_mfma_f32_16x16x32_f16).
 // Work: tiles of (up to 64 tokens of one expert) x (64 weight rows); K runs
 // in blocks of 32 columns, one scale block each, dequantised into LDS.
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-constexpr int kTM = 64;   // tokens per tile
-constexpr int kTN = 64;   // weight rows per tile
-constexpr int kKB = 32;   // K per block (one scale block)
-constexpr int kLd = kKB + 8;  // LDS row pitch in halves (16-byte aligned, spreads banks)
+// ---------------------------------------------------------------------------
+// Tiles: 128 tokens of one expert x 64 weight rows (gate/up: 32 rows of each
+// matrix, so one tile yields h for 32 rows; down: 64 rows).  K runs in steps
+// of 80 slots -- half a 160-column superblock, 8 packed words -- in "pair
+// order": inside each superblock, slot 2p + e holds column c_p + 5 e with
+// c_p = 10 (p / 5) + p % 5, i.e. the two codes that share the two halves of a
+// packed word sit side by side.  The fp16 copies of x and h are stored in
+// that order (zero at slots past the last column), so one v_and_or_b32 +
+// v_pk_add + v_pk_mul dequantises two adjacent K slots in place, and any K
+// order is the same contraction.
+// Per step every thread copies 80 bytes of activations and dequantises two
+// words of one weight row into LDS (double-buffered); the next step's global
+// loads are in flight while the MFMAs of this one run: one barrier per step.
+// MFMA: v_mfma_f32_16x16x32_f16 twice and v_mfma_f32_16x16x16_f16 once per
+// 16 x 16 output tile per step; D[token][row].
+// ---------------------------------------------------------------------------
+constexpr int kPM = 128;       // tokens per tile (work entries hold <= kPM tokens)
+constexpr int kPN = 64;        // weight rows per tile
+constexpr int kPK = 80;        // K slots per step
+constexpr int kPld = kPK + 8;  // LDS pitch in halves: rows 176 B apart, 8 consecutive rows on 8 bank groups
 
 struct PrefillParams {
   const moe::WorkEntry *work;
@@ -35,8 +55,9 @@ struct PrefillParams {
   int n_slots;
   int max_work;  // bound on n_work[0] (workspace size)
   moe::MatLayout gate, up, down;
-  const _Float16 *x16;  // [T][d_model]
-  _Float16 *h16;        // [T*k + T][d_ff]
+  const _Float16 *x16;  // [T][kp_model], pair order
+  _Float16 *h16;        // [T*k + T][kp_ff], pair order
+  int kp_model, kp_ff;  // padded row lengths: superblocks x 160
   float *y_pairs, *y_shared;
   int d_model, d_ff;
 };
@@ -50,7 +71,7 @@ __device__ inline const uint8_t *entry_blob(const PrefillParams &P, const moe::W
 
 // a work entry is used only if it indexes inside this call's pairs / tokens
 __device__ inline bool entry_ok(const PrefillParams &P, const moe::WorkEntry &we) {
-  if (we.m < 1 || we.m > kTM || we.first < 0) return false;
+  if (we.m < 1 || we.m > kPM || we.first < 0) return false;
   return we.expert >= 0 ? (we.expert < P.E && we.first + we.m <= P.T * P.k) : (we.first + we.m <= P.T);
 }
 
@@ -67,39 +88,86 @@ __device__ inline bool entry_token(const PrefillParams &P, const moe::WorkEntry 
   return true;
 }
 
-// 16 dequantised weights of one row, columns c0..c0+15 (c0 % 16 == 0), into LDS
-__device__ inline void deq16(const uint8_t *blob, const moe::MatLayout &M, int row, int c0, _Float16 *dst) {
-  const uint32_t *codes = reinterpret_cast<const uint32_t *>(blob + M.code_off) + (size_t)row * M.wpr;
-  const _Float16 s = *reinterpret_cast<const _Float16 *>(blob + M.scale_off + ((size_t)row * M.nblk + c0 / 32) * 2);
-  const int w0 = c0 / 10;
-  uint32_t w[3];
-#pragma unroll
-  for (int i = 0; i < 3; ++i) w[i] = (w0 + i < M.wpr) ? codes[w0 + i] : 0u;
-  _Float16 out[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int c = c0 + i;
-    const int wi = c / 10 - w0, j = c % 10;
-    const uint32_t word = wi == 0 ? w[0] : (wi == 1 ? w[1] : w[2]);
-    const int sh = j < 5 ? 3 * j : 16 + 3 * (j - 5);
-    const int q = (int)((word >> sh) & 7u);
-    out[i] = (_Float16)(q - 4) * s;
-  }
-#pragma unroll
-  for (int i = 0; i < 16; i += 8)
-    *reinterpret_cast<h8 *>(dst + i) =
-        (h8){out[i], out[i + 1], out[i + 2], out[i + 3], out[i + 4], out[i + 5], out[i + 6], out[i + 7]};
+// column -> pair-order slot, and back
+__host__ __device__ inline int pair_slot(int c) {
+  const int S = c / moe::kSbCols, lc = c - S * moe::kSbCols, w = lc / 10, j = lc - 10 * w;
+  return S * moe::kSbCols + 2 * (5 * w + j % 5) + j / 5;
+}
+__host__ __device__ inline int slot_col(int s) {
+  const int S = s / moe::kSbCols, r = s - S * moe::kSbCols, p = r >> 1;
+  return S * moe::kSbCols + 10 * (p / 5) + p % 5 + 5 * (r & 1);
 }
 
-__device__ inline f4 mfma(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
+__device__ inline f4 mfma32(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
+__device__ inline f4 mfma16(h4 a, h4 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0); }
 
-// gate & up for one tile, h = silu(g) * u -> h16
-__global__ void __launch_bounds__(256) prefill_gateup_kernel(PrefillParams P) {
-  __shared__ _Float16 xs[kTM][kLd];
-  __shared__ _Float16 wg[kTN][kLd];
-  __shared__ _Float16 wu[kTN][kLd];
-  __shared__ int tok_sh[kTM], row_sh[kTM];
-  const int ntile = P.d_ff / kTN;
+// Weight part of one thread: row `brow` of the tile's B rows, words 2u, 2u+1
+// of each 8-word step.
+struct WSrc {
+  const uint8_t *codes;   // the row's words
+  const uint8_t *scales;  // the row's scales
+  int nblk;
+};
+
+// raw loads of step s for this thread: 2 words and the 2 scale blocks they touch
+struct WRaw {
+  uint2 w;
+  uint32_t s0, s1;
+};
+
+__device__ inline void load_w(const WSrc &W, int s, int u, WRaw &r) {
+  const int S = s >> 1, hh = s & 1;
+  r.w = *reinterpret_cast<const uint2 *>(W.codes + (size_t)(S * 16 + 8 * hh + 2 * u) * 4);
+  const int b0 = 5 * S + (80 * hh + 20 * u) / 32;
+  r.s0 = *reinterpret_cast<const uint16_t *>(W.scales + (size_t)min(b0, W.nblk - 1) * 2);
+  r.s1 = *reinterpret_cast<const uint16_t *>(W.scales + (size_t)min(b0 + 1, W.nblk - 1) * 2);
+}
+
+// dequantise the thread's 10 code pairs into 20 consecutive K slots (40 B)
+__device__ inline void deq_w(const WRaw &r, int s, int u, _Float16 *dst) {
+  const int hh = s & 1;
+  // superblock-relative column of the thread's first code, and the first
+  // column of its second scale block, relative to it
+  const int c0 = 80 * hh + 20 * u;
+  const int thr = ((c0 / 32) + 1) * 32 - c0;
+  const h2 S0 = __builtin_bit_cast(h2, r.s0 | (r.s0 << 16));
+  const h2 S1 = __builtin_bit_cast(h2, r.s1 | (r.s1 << 16));
+  const h2 S01 = __builtin_bit_cast(h2, r.s0 | (r.s1 << 16));
+  const uint32_t magic = 0x64006400u;
+  h2 out[10];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const uint32_t word = a ? r.w.y : r.w.x;
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+      const int jj = j % 3;
+      const uint32_t src = j < 3 ? word : (word >> 9);
+      const uint32_t mask = 0x00070007u << (3 * jj);
+      const float f = jj == 0 ? 1.0f : (jj == 1 ? 8.0f : 64.0f);
+      const h2 v = __builtin_bit_cast(h2, (src & mask) | magic);
+      const h2 o = {(_Float16)(1024.0f + 4.0f * f), (_Float16)(1024.0f + 4.0f * f)};
+      const h2 inv = {(_Float16)(1.0f / f), (_Float16)(1.0f / f)};
+      const int lc = 10 * a + j;  // column of the low code, relative to c0
+      const h2 sc = (lc + 5 >= thr) ? ((lc >= thr) ? S1 : S01) : S0;
+      // (v - o) = f (q - 4) exactly; / f exactly; one rounding in the scale product
+      out[5 * a + j] = ((v - o) * inv) * sc;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const uint2 pk = make_uint2(__builtin_bit_cast(uint32_t, out[2 * i]), __builtin_bit_cast(uint32_t, out[2 * i + 1]));
+    *reinterpret_cast<uint2 *>(dst + 4 * i) = pk;
+  }
+}
+
+template <int NMAT>
+__global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams P) {
+  __shared__ __attribute__((aligned(16))) _Float16 xs[2][kPM][kPld];
+  __shared__ __attribute__((aligned(16))) _Float16 ws[2][kPN][kPld];
+  __shared__ int row_sh[kPM], tok_sh[kPM];
+  const int rows_out = NMAT == 2 ? P.d_ff : P.d_model;
+  const int tile_rows = NMAT == 2 ? kPN / 2 : kPN;  // output rows per tile
+  const int ntile = rows_out / tile_rows;
   const int item = blockIdx.x;
   if (item >= min(P.n_work[0], P.max_work) * ntile) return;
   const moe::WorkEntry we = P.work[item / ntile];
@@ -108,135 +176,129 @@ __global__ void __launch_bounds__(256) prefill_gateup_kernel(PrefillParams P) {
   const uint8_t *blob = entry_blob(P, we);
   if (!blob) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid < kTM) {
+  if (tid < kPM) {
     int tok = -1, row = -1;
     if (tid < we.m && !entry_token(P, we, tid, tok, row)) tok = row = -1;
     tok_sh[tid] = tok;
     row_sh[tid] = row;
   }
   __syncthreads();
-  const int wm = wave >> 1, wn = wave & 1;  // 2 x 2 waves, 32 x 32 each
-  f4 ag[2][2], au[2][2];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      ag[a][b] = (f4){0.f, 0.f, 0.f, 0.f};
-      au[a][b] = (f4){0.f, 0.f, 0.f, 0.f};
-    }
-  // loader roles: x rows (64 x 4 chunks of 8 halves); weights (2 mats x 64 rows x 2 halves of 16)
-  const int xr = tid >> 2, xc = (tid & 3) * 8;
-  const int wmat = tid >> 7, wrow = (tid >> 1) & 63, wh = tid & 1;
-  const moe::MatLayout &WM = wmat == 0 ? P.gate : P.up;
-  _Float16(*wdst)[kLd] = wmat == 0 ? wg : wu;
-  for (int k0 = 0; k0 < P.d_model; k0 += kKB) {
-    {
-      const int tk = tok_sh[xr];
-      h8 v = (h8){0, 0, 0, 0, 0, 0, 0, 0};
-      if (tk >= 0) v = *reinterpret_cast<const h8 *>(P.x16 + (size_t)tk * P.d_model + k0 + xc);
-      *reinterpret_cast<h8 *>(&xs[xr][xc]) = v;
-    }
-    deq16(blob, WM, nt * kTN + wrow, k0 + 16 * wh, &wdst[wrow][16 * wh]);
-    __syncthreads();
-    const int r = lane & 15, kg = (lane >> 4) * 8;
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const h8 A = *reinterpret_cast<const h8 *>(&xs[wm * 32 + a * 16 + r][kg]);
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const h8 Bg = *reinterpret_cast<const h8 *>(&wg[wn * 32 + b * 16 + r][kg]);
-        const h8 Bu = *reinterpret_cast<const h8 *>(&wu[wn * 32 + b * 16 + r][kg]);
-        ag[a][b] = mfma(A, Bg, ag[a][b]);
-        au[a][b] = mfma(A, Bu, au[a][b]);
-      }
-    }
-    __syncthreads();
+  const int m = we.m;
+  const int kp = NMAT == 2 ? P.kp_model : P.kp_ff;
+  const int nsteps = kp / kPK;
+  // activation copy role: row xr, 40 slots starting at 40 xh
+  const int xr = tid >> 1, xh = tid & 1;
+  const bool xact = xr < m && row_sh[xr] >= 0;
+  const _Float16 *xsrc = nullptr;
+  if (xact) xsrc = NMAT == 2 ? P.x16 + (size_t)tok_sh[xr] * kp : P.h16 + (size_t)row_sh[xr] * kp;
+  // weight role: B row brow, word pair u
+  const int brow = tid >> 2, u = tid & 3;
+  WSrc W;
+  {
+    const moe::MatLayout &M = NMAT == 2 ? (brow < kPN / 2 ? P.gate : P.up) : P.down;
+    const int wrow = NMAT == 2 ? nt * (kPN / 2) + (brow & (kPN / 2 - 1)) : nt * kPN + brow;
+    W.codes = blob + M.code_off + (size_t)wrow * M.wpr * 4;
+    W.scales = blob + M.scale_off + (size_t)wrow * M.nblk * 2;
+    W.nblk = M.nblk;
   }
-  // D: lane holds tokens 4*(lane/16)+i (of the 16-row subtile) for column lane%16
+  uint4 xv0, xv1, xv2, xv3, xv4;
+  WRaw wr;
+#define PF_LOAD_STEP(s_)                                                                   \
+  do {                                                                                     \
+    if (xact) {                                                                            \
+      const uint4 *src_ = reinterpret_cast<const uint4 *>(xsrc + (s_) * kPK + 40 * xh);    \
+      xv0 = src_[0];                                                                       \
+      xv1 = src_[1];                                                                       \
+      xv2 = src_[2];                                                                       \
+      xv3 = src_[3];                                                                       \
+      xv4 = src_[4];                                                                       \
+    }                                                                                      \
+    load_w(W, (s_), u, wr);                                                                \
+  } while (0)
+  const int wm = wave & 1, wn = wave >> 1;
+  // output tiles of this wave: M tiles mt (16 tokens each), N tiles nb
+  f4 acc[4][2];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = wm * 32 + a * 16 + 4 * (lane >> 4) + i;
-        const int col = nt * kTN + wn * 32 + b * 16 + (lane & 15);
-        const int hrow = row_sh[m];
-        if (hrow < 0) continue;
-        const float gv = ag[a][b][i], uv = au[a][b][i];
-        const float h = gv / (1.0f + __expf(-gv)) * uv;
-        P.h16[(size_t)hrow * P.d_ff + col] = (_Float16)h;
-      }
-}
-
-// down for one tile: y = W_d h
-__global__ void __launch_bounds__(256) prefill_down_kernel(PrefillParams P) {
-  __shared__ _Float16 hs[kTM][kLd];
-  __shared__ _Float16 wd[kTN][kLd];
-  __shared__ int row_sh[kTM], tok_sh[kTM];
-  const int ntile = P.d_model / kTN;
-  const int item = blockIdx.x;
-  if (item >= min(P.n_work[0], P.max_work) * ntile) return;
-  const moe::WorkEntry we = P.work[item / ntile];
-  const int nt = item % ntile;
-  if (!entry_ok(P, we)) return;
-  const uint8_t *blob = entry_blob(P, we);
-  if (!blob) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid < kTM) {
-    int tok = -1, row = -1;
-    if (tid < we.m && !entry_token(P, we, tid, tok, row)) tok = row = -1;
-    tok_sh[tid] = tok;
-    row_sh[tid] = row;
-  }
-  __syncthreads();
-  const int wm = wave >> 1, wn = wave & 1;
-  f4 acc[2][2];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = (f4){0.f, 0.f, 0.f, 0.f};
-  const int xr = tid >> 2, xc = (tid & 3) * 8;
-  const int wrow = tid >> 1, wh = tid & 1;  // 128 loaders for 64 rows x 2 halves
-  for (int k0 = 0; k0 < P.d_ff; k0 += kKB) {
-    {
-      const int hr = row_sh[xr];
-      h8 v = (h8){0, 0, 0, 0, 0, 0, 0, 0};
-      if (hr >= 0) v = *reinterpret_cast<const h8 *>(P.h16 + (size_t)hr * P.d_ff + k0 + xc);
-      *reinterpret_cast<h8 *>(&hs[xr][xc]) = v;
+  // B rows of N tile nb: gate/up -> 16 wn (+32 for up); down -> 32 wn + 16 nb
+  const int bro0 = NMAT == 2 ? 16 * wn : 32 * wn, bro1 = NMAT == 2 ? kPN / 2 + 16 * wn : 32 * wn + 16;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int mt_active = min(4, max(0, (m - 64 * wm + 15) / 16));  // M tiles holding tokens
+  PF_LOAD_STEP(0);
+  for (int s = 0; s < nsteps; ++s) {
+    const int buf = s & 1;
+    if (xact) {
+      uint4 *dst = reinterpret_cast<uint4 *>(&xs[buf][xr][40 * xh]);
+      dst[0] = xv0;
+      dst[1] = xv1;
+      dst[2] = xv2;
+      dst[3] = xv3;
+      dst[4] = xv4;
     }
-    if (tid < 2 * kTN) deq16(blob, P.down, nt * kTN + wrow, k0 + 16 * wh, &wd[wrow][16 * wh]);
+    deq_w(wr, s, u, &ws[buf][brow][20 * u]);
+    if (s + 1 < nsteps) PF_LOAD_STEP(s + 1);
     __syncthreads();
-    const int r = lane & 15, kg = (lane >> 4) * 8;
+    // B fragments for the two N tiles
+    h8 b32[2][2];
+    h4 b16[2];
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const h8 A = *reinterpret_cast<const h8 *>(&hs[wm * 32 + a * 16 + r][kg]);
+    for (int nb = 0; nb < 2; ++nb) {
+      const _Float16 *wrow = &ws[buf][(nb ? bro1 : bro0) + r16][0];
+      b32[nb][0] = *reinterpret_cast<const h8 *>(wrow + 8 * g);
+      b32[nb][1] = *reinterpret_cast<const h8 *>(wrow + 32 + 8 * g);
+      b16[nb] = *reinterpret_cast<const h4 *>(wrow + 64 + 4 * g);
+    }
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const h8 B = *reinterpret_cast<const h8 *>(&wd[wn * 32 + b * 16 + r][kg]);
-        acc[a][b] = mfma(A, B, acc[a][b]);
+    for (int mt = 0; mt < 4; ++mt) {
+      if (mt < mt_active) {
+        const _Float16 *xrow = &xs[buf][64 * wm + 16 * mt + r16][0];
+        const h8 a0 = *reinterpret_cast<const h8 *>(xrow + 8 * g);
+        const h8 a1 = *reinterpret_cast<const h8 *>(xrow + 32 + 8 * g);
+        const h4 a2 = *reinterpret_cast<const h4 *>(xrow + 64 + 4 * g);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          acc[mt][nb] = mfma32(a0, b32[nb][0], acc[mt][nb]);
+          acc[mt][nb] = mfma32(a1, b32[nb][1], acc[mt][nb]);
+          acc[mt][nb] = mfma16(a2, b16[nb], acc[mt][nb]);
+        }
       }
     }
-    __syncthreads();
   }
+#undef PF_LOAD_STEP
+  // D: lane holds tokens 4 g + i of the M tile for column r16 of the N tile
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int i = 0; i < 4; ++i) {
+      const int mm = 64 * wm + 16 * mt + 4 * g + i;
+      if (mm >= m) continue;
+      const int hrow = row_sh[mm];
+      if (hrow < 0) continue;
+      if constexpr (NMAT == 2) {
+        const int col = nt * (kPN / 2) + 16 * wn + r16;
+        const float gv = acc[mt][0][i], uv = acc[mt][1][i];
+        // h is rounded to fp16 here, so the division is kept exact
+        const float h = gv / (1.0f + __expf(-gv)) * uv;
+        P.h16[(size_t)hrow * P.kp_ff + pair_slot(col)] = (_Float16)h;
+      } else {
+        float *y = we.expert >= 0 ? P.y_pairs + (size_t)hrow * P.d_model : P.y_shared + (size_t)tok_sh[mm] * P.d_model;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = wm * 32 + a * 16 + 4 * (lane >> 4) + i;
-        const int col = nt * kTN + wn * 32 + b * 16 + (lane & 15);
-        const int hrow = row_sh[m];
-        if (hrow < 0) continue;
-        float *y = we.expert >= 0 ? P.y_pairs + (size_t)hrow * P.d_model : P.y_shared + (size_t)tok_sh[m] * P.d_model;
-        y[col] = acc[a][b][i];
+        for (int nb = 0; nb < 2; ++nb) y[nt * kPN + 32 * wn + 16 * nb + r16] = acc[mt][nb][i];
       }
+    }
 }
 
-__global__ void __launch_bounds__(256) to_fp16_kernel(const float *__restrict__ x, size_t n, _Float16 *__restrict__ y) {
-  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) y[i] = (_Float16)x[i];
+// x [T][d] fp32 -> fp16 in pair order, rows of kp slots (zero past column d)
+__global__ void __launch_bounds__(256) to_fp16_pairs_kernel(const float *__restrict__ x, int T, int d, int kp,
+                                                            _Float16 *__restrict__ y) {
+  const size_t n = (size_t)T * kp;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    const int t = (int)(i / kp), sl = (int)(i - (size_t)t * kp);
+    const int c = slot_col(sl);
+    y[i] = c < d ? (_Float16)x[(size_t)t * d + c] : (_Float16)0.f;
+  }
 }
 
 }  // namespace
@@ -249,11 +311,16 @@ hipError_t launch_bucket_ex(const moe_ctx *c, const int32_t *idx, int T, int32_t
 hipError_t launch_ffn_prefill(const moe_ctx *c, int layer, const float *x, int T, const int32_t *idx,
                               const int32_t *slot_of_pair, float *y_pairs, float *y_shared, hipStream_t s) {
   const moe_config &k = c->cfg;
-  if (k.d_ff % kTN || k.d_model % kTN) return hipErrorInvalidValue;
-  hipError_t e = launch_bucket_ex(c, idx, T, c->offsets_ws, c->perm_ws, true, kTM, nullptr, nullptr, 0, s);
+  if (k.d_ff % kPN || k.d_model % kPN) return hipErrorInvalidValue;
+  hipError_t e = launch_bucket_ex(c, idx, T, c->offsets_ws, c->perm_ws, true, kPM, nullptr, nullptr, 0, s);
   if (e != hipSuccess) return e;
-  const size_t nx = (size_t)T * k.d_model;
-  hipLaunchKernelGGL(to_fp16_kernel, dim3((unsigned)((nx + 255) / 256)), dim3(256), 0, s, x, nx, (_Float16 *)c->x16);
+  const int kpm = c->L.gate.nsb * moe::kSbCols, kpf = c->L.down.nsb * moe::kSbCols;
+  {
+    const size_t nx = (size_t)T * kpm;
+    const size_t blocks = std::min<size_t>((nx + 255) / 256, 8192);
+    hipLaunchKernelGGL(to_fp16_pairs_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, T, k.d_model, kpm,
+                       (_Float16 *)c->x16);
+  }
   PrefillParams P;
   P.work = c->work;
   P.n_work = c->n_work;
@@ -273,15 +340,17 @@ hipError_t launch_ffn_prefill(const moe_ctx *c, int layer, const float *x, int T
   P.down = c->L.down;
   P.x16 = (const _Float16 *)c->x16;
   P.h16 = (_Float16 *)c->h16;
+  P.kp_model = kpm;
+  P.kp_ff = kpf;
   P.y_pairs = y_pairs;
   P.y_shared = y_shared;
   P.d_model = k.d_model;
   P.d_ff = k.d_ff;
-  // entries hold <= 64 tokens: at most pairs/64 + min(E, pairs) routed ones + the shared ones
+  // entries hold <= kPM tokens: at most pairs/kPM + min(E, pairs) routed ones + the shared ones
   const int pairs = T * k.top_k;
-  const int ents = pairs / kTM + (pairs < k.n_experts ? pairs : k.n_experts) + (T + kTM - 1) / kTM;
-  hipLaunchKernelGGL(prefill_gateup_kernel, dim3(ents * (k.d_ff / kTN)), dim3(256), 0, s, P);
-  hipLaunchKernelGGL(prefill_down_kernel, dim3(ents * (k.d_model / kTN)), dim3(256), 0, s, P);
+  const int ents = pairs / kPM + (pairs < k.n_experts ? pairs : k.n_experts) + (T + kPM - 1) / kPM;
+  hipLaunchKernelGGL(prefill_kernel<2>, dim3(ents * (k.d_ff / (kPN / 2))), dim3(256), 0, s, P);
+  hipLaunchKernelGGL(prefill_kernel<1>, dim3(ents * (k.d_model / kPN)), dim3(256), 0, s, P);
   return hipGetLastError();
 }
 
