@@ -101,8 +101,8 @@ __host__ __device__ inline int slot_col(int s) {
 __device__ inline f4 mfma32(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 __device__ inline f4 mfma16(h4 a, h4 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0); }
 
-// Weight part of one thread: row `brow` of the tile's B rows, words 2u, 2u+1
-// of each 8-word step.
+// Weight part of one thread: B row brow = tid / 4, words 2u, 2u+1 (u = tid %
+// 4) of each 8-word step, so the 4 lanes of a row read its 32 bytes together.
 struct WSrc {
   const uint8_t *codes;   // the row's words
   const uint8_t *scales;  // the row's scales
@@ -123,17 +123,39 @@ __device__ inline void load_w(const WSrc &W, int s, int u, WRaw &r) {
   r.s1 = *reinterpret_cast<const uint16_t *>(W.scales + (size_t)min(b0 + 1, W.nblk - 1) * 2);
 }
 
-// dequantise the thread's 10 code pairs into 20 consecutive K slots (40 B)
-__device__ inline void deq_w(const WRaw &r, int s, int u, _Float16 *dst) {
-  const int hh = s & 1;
-  // superblock-relative column of the thread's first code, and the first
-  // column of its second scale block, relative to it
+struct PConsts {
+  uint32_t mask[3];  // 0x00070007 << 3 j', kept in VGPRs so v_and_or_b32 can be used
+  uint32_t magic;    // fp16 1024 in both halves
+};
+
+// Byte selectors for v_perm_b32(s1, s0, sel): which of the thread's two scale
+// blocks each half of code pair (a, j) uses.  With c0 = 80 hh + 20 u the
+// superblock-relative column of the thread's first code, column c0 + lc uses
+// the second block when lc >= 32 (c0 / 32 + 1) - c0.
+struct PairSel {
+  uint32_t sel[10];
+};
+
+__device__ inline void make_sel(int hh, int u, PairSel &P) {
   const int c0 = 80 * hh + 20 * u;
-  const int thr = ((c0 / 32) + 1) * 32 - c0;
-  const h2 S0 = __builtin_bit_cast(h2, r.s0 | (r.s0 << 16));
-  const h2 S1 = __builtin_bit_cast(h2, r.s1 | (r.s1 << 16));
-  const h2 S01 = __builtin_bit_cast(h2, r.s0 | (r.s1 << 16));
-  const uint32_t magic = 0x64006400u;
+  const int thr = (c0 / 32 + 1) * 32 - c0;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+      const int lc = 10 * a + j;
+      const uint32_t lo = lc >= thr ? 0x0504u : 0x0100u;      // bytes of s1 (src0) or s0 (src1)
+      const uint32_t hi = lc + 5 >= thr ? 0x0504u : 0x0100u;
+      P.sel[5 * a + j] = lo | (hi << 16);
+    }
+}
+
+// Dequantise the thread's 10 code pairs into 20 consecutive K slots (40 B).
+// Per pair: one v_and_or_b32 (fp16 1024 + f q), one v_pk_add (- (1024 + 4 f),
+// exact), one v_pk_mul by 1/f (exact), one v_perm_b32 (the pair's scales),
+// one v_pk_mul by them (one rounding: fp16((q - 4) s), the oracle's fp16
+// reading).
+__device__ inline void deq_w(const WRaw &r, const PairSel &P, const PConsts &K, _Float16 *dst) {
   h2 out[10];
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
@@ -142,14 +164,11 @@ __device__ inline void deq_w(const WRaw &r, int s, int u, _Float16 *dst) {
     for (int j = 0; j < 5; ++j) {
       const int jj = j % 3;
       const uint32_t src = j < 3 ? word : (word >> 9);
-      const uint32_t mask = 0x00070007u << (3 * jj);
       const float f = jj == 0 ? 1.0f : (jj == 1 ? 8.0f : 64.0f);
-      const h2 v = __builtin_bit_cast(h2, (src & mask) | magic);
+      const h2 v = __builtin_bit_cast(h2, (src & K.mask[jj]) | K.magic);
       const h2 o = {(_Float16)(1024.0f + 4.0f * f), (_Float16)(1024.0f + 4.0f * f)};
       const h2 inv = {(_Float16)(1.0f / f), (_Float16)(1.0f / f)};
-      const int lc = 10 * a + j;  // column of the low code, relative to c0
-      const h2 sc = (lc + 5 >= thr) ? ((lc >= thr) ? S1 : S01) : S0;
-      // (v - o) = f (q - 4) exactly; / f exactly; one rounding in the scale product
+      const h2 sc = __builtin_bit_cast(h2, __builtin_amdgcn_perm(r.s1, r.s0, P.sel[5 * a + j]));
       out[5 * a + j] = ((v - o) * inv) * sc;
     }
   }
@@ -157,6 +176,61 @@ __device__ inline void deq_w(const WRaw &r, int s, int u, _Float16 *dst) {
   for (int i = 0; i < 5; ++i) {
     const uint2 pk = make_uint2(__builtin_bit_cast(uint32_t, out[2 * i]), __builtin_bit_cast(uint32_t, out[2 * i + 1]));
     *reinterpret_cast<uint2 *>(dst + 4 * i) = pk;
+  }
+}
+
+// One K step: store the prefetched activations and dequantised weights into
+// buffer B, request step s + 1, barrier, then the wave's MFMAs on buffer B.
+template <int B>
+__device__ inline void prefill_step(int s, int nsteps, bool xact, uint4 &xv0, uint4 &xv1, uint4 &xv2, uint4 &xv3,
+                                    uint4 &xv4, _Float16 *xdst, WRaw &wr, const PairSel &sel, const PConsts &K,
+                                    _Float16 *wdst, const WSrc &W, int u, const _Float16 *xsrc, int xh,
+                                    const _Float16 (*wsb)[kPld], const _Float16 (*xsb)[kPld], int bro0, int bro1,
+                                    int r16, int g, int wm, int mt_active, f4 (&acc)[4][2]) {
+  if (xact) {
+    uint4 *dst = reinterpret_cast<uint4 *>(xdst);
+    dst[0] = xv0;
+    dst[1] = xv1;
+    dst[2] = xv2;
+    dst[3] = xv3;
+    dst[4] = xv4;
+  }
+  deq_w(wr, sel, K, wdst);
+  if (s + 1 < nsteps) {
+    if (xact) {
+      const uint4 *src = reinterpret_cast<const uint4 *>(xsrc + (s + 1) * kPK + 40 * xh);
+      xv0 = src[0];
+      xv1 = src[1];
+      xv2 = src[2];
+      xv3 = src[3];
+      xv4 = src[4];
+    }
+    load_w(W, s + 1, u, wr);
+  }
+  __syncthreads();
+  h8 b32[2][2];
+  h4 b16[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const _Float16 *wrow = wsb[(nb ? bro1 : bro0) + r16];
+    b32[nb][0] = *reinterpret_cast<const h8 *>(wrow + 8 * g);
+    b32[nb][1] = *reinterpret_cast<const h8 *>(wrow + 32 + 8 * g);
+    b16[nb] = *reinterpret_cast<const h4 *>(wrow + 64 + 4 * g);
+  }
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    if (mt < mt_active) {
+      const _Float16 *xrow = xsb[64 * wm + 16 * mt + r16];
+      const h8 a0 = *reinterpret_cast<const h8 *>(xrow + 8 * g);
+      const h8 a1 = *reinterpret_cast<const h8 *>(xrow + 32 + 8 * g);
+      const h4 a2 = *reinterpret_cast<const h4 *>(xrow + 64 + 4 * g);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        acc[mt][nb] = mfma32(a0, b32[nb][0], acc[mt][nb]);
+        acc[mt][nb] = mfma32(a1, b32[nb][1], acc[mt][nb]);
+        acc[mt][nb] = mfma16(a2, b16[nb], acc[mt][nb]);
+      }
+    }
   }
 }
 
@@ -186,7 +260,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams P) {
   const int m = we.m;
   const int kp = NMAT == 2 ? P.kp_model : P.kp_ff;
   const int nsteps = kp / kPK;
-  // activation copy role: row xr, 40 slots starting at 40 xh
+  // activation copy role: row xr, the 40 slots starting at 40 xh
   const int xr = tid >> 1, xh = tid & 1;
   const bool xact = xr < m && row_sh[xr] >= 0;
   const _Float16 *xsrc = nullptr;
@@ -201,20 +275,17 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams P) {
     W.scales = blob + M.scale_off + (size_t)wrow * M.nblk * 2;
     W.nblk = M.nblk;
   }
+  PairSel sel0, sel1;  // even and odd steps
+  make_sel(0, u, sel0);
+  make_sel(1, u, sel1);
+  PConsts K;
+  K.mask[0] = 0x00070007u;
+  K.mask[1] = 0x00380038u;
+  K.mask[2] = 0x01c001c0u;
+  K.magic = 0x64006400u;
+  asm volatile("" : "+v"(K.mask[0]), "+v"(K.mask[1]), "+v"(K.mask[2]), "+s"(K.magic));
   uint4 xv0, xv1, xv2, xv3, xv4;
   WRaw wr;
-#define PF_LOAD_STEP(s_)                                                                   \
-  do {                                                                                     \
-    if (xact) {                                                                            \
-      const uint4 *src_ = reinterpret_cast<const uint4 *>(xsrc + (s_) * kPK + 40 * xh);    \
-      xv0 = src_[0];                                                                       \
-      xv1 = src_[1];                                                                       \
-      xv2 = src_[2];                                                                       \
-      xv3 = src_[3];                                                                       \
-      xv4 = src_[4];                                                                       \
-    }                                                                                      \
-    load_w(W, (s_), u, wr);                                                                \
-  } while (0)
   const int wm = wave & 1, wn = wave >> 1;
   // output tiles of this wave: M tiles mt (16 tokens each), N tiles nb
   f4 acc[4][2];
@@ -226,47 +297,22 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams P) {
   const int bro0 = NMAT == 2 ? 16 * wn : 32 * wn, bro1 = NMAT == 2 ? kPN / 2 + 16 * wn : 32 * wn + 16;
   const int r16 = lane & 15, g = lane >> 4;
   const int mt_active = min(4, max(0, (m - 64 * wm + 15) / 16));  // M tiles holding tokens
-  PF_LOAD_STEP(0);
-  for (int s = 0; s < nsteps; ++s) {
-    const int buf = s & 1;
-    if (xact) {
-      uint4 *dst = reinterpret_cast<uint4 *>(&xs[buf][xr][40 * xh]);
-      dst[0] = xv0;
-      dst[1] = xv1;
-      dst[2] = xv2;
-      dst[3] = xv3;
-      dst[4] = xv4;
-    }
-    deq_w(wr, s, u, &ws[buf][brow][20 * u]);
-    if (s + 1 < nsteps) PF_LOAD_STEP(s + 1);
-    __syncthreads();
-    // B fragments for the two N tiles
-    h8 b32[2][2];
-    h4 b16[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const _Float16 *wrow = &ws[buf][(nb ? bro1 : bro0) + r16][0];
-      b32[nb][0] = *reinterpret_cast<const h8 *>(wrow + 8 * g);
-      b32[nb][1] = *reinterpret_cast<const h8 *>(wrow + 32 + 8 * g);
-      b16[nb] = *reinterpret_cast<const h4 *>(wrow + 64 + 4 * g);
-    }
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      if (mt < mt_active) {
-        const _Float16 *xrow = &xs[buf][64 * wm + 16 * mt + r16][0];
-        const h8 a0 = *reinterpret_cast<const h8 *>(xrow + 8 * g);
-        const h8 a1 = *reinterpret_cast<const h8 *>(xrow + 32 + 8 * g);
-        const h4 a2 = *reinterpret_cast<const h4 *>(xrow + 64 + 4 * g);
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          acc[mt][nb] = mfma32(a0, b32[nb][0], acc[mt][nb]);
-          acc[mt][nb] = mfma32(a1, b32[nb][1], acc[mt][nb]);
-          acc[mt][nb] = mfma16(a2, b16[nb], acc[mt][nb]);
-        }
-      }
-    }
+  if (xact) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(xsrc + 40 * xh);
+    xv0 = src[0];
+    xv1 = src[1];
+    xv2 = src[2];
+    xv3 = src[3];
+    xv4 = src[4];
   }
-#undef PF_LOAD_STEP
+  load_w(W, 0, u, wr);
+  // steps come in (even, odd) pairs: buffer and scale selectors are static
+  for (int s = 0; s < nsteps; s += 2) {
+    prefill_step<0>(s, nsteps, xact, xv0, xv1, xv2, xv3, xv4, xs[0][xr] + 40 * xh, wr, sel0, K, ws[0][brow] + 20 * u,
+                    W, u, xsrc, xh, ws[0], xs[0], bro0, bro1, r16, g, wm, mt_active, acc);
+    prefill_step<1>(s + 1, nsteps, xact, xv0, xv1, xv2, xv3, xv4, xs[1][xr] + 40 * xh, wr, sel1, K,
+                    ws[1][brow] + 20 * u, W, u, xsrc, xh, ws[1], xs[1], bro0, bro1, r16, g, wm, mt_active, acc);
+  }
   // D: lane holds tokens 4 g + i of the M tile for column r16 of the N tile
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
