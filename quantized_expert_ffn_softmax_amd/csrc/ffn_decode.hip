@@ -170,8 +170,9 @@ __device__ inline bool entry_token(const DecodeParams &P, const moe::WorkEntry &
 //     read serves sit in 8 consecutive 16-byte slots;
 //   * everything for round R+1 is requested before round R is computed, into
 //     the other LDS buffer and the other register set; one barrier per round.
-// A lane group past the last superblock computes on zero words against zero
-// activations and adds exactly 0.  Words of a partial
+// In gate/up, a lane group past the last superblock computes on zero words
+// against zero activations and adds exactly 0; the down kernel splits its
+// last round instead (below).  Words of a partial
 // last superblock that lie past the row are read from the bytes that follow
 // it inside the blob (the next row, or the matrix's scale array, at least 64
 // bytes) and also meet zero activations; scale reads are clamped to the row.
@@ -250,7 +251,9 @@ __device__ inline void stage_round(const Mats<NMAT> &Mt, const Unit &U, int R, i
     const int q = w + kWaves * i;
     if (q < NMAT * kScDwords) {
       const int mat = q / kScDwords, j = q % kScDwords;
-      const uint32_t off = Mt.m[NMAT == 2 ? mat : 0].scale_off + min(kScDwords * 4 * R + 4 * j, 2 * nblk - 4);
+      // select, not index: a runtime index into Mt.m would put it in scratch memory
+      const uint32_t base = mat == 0 ? Mt.m[0].scale_off : Mt.m[NMAT - 1].scale_off;
+      const uint32_t off = base + min(kScDwords * 4 * R + 4 * j, 2 * nblk - 4);
       __builtin_amdgcn_global_load_lds(U.blob + off + U.s_off, lsc + 256 * q, 4, 0, 0);
     }
   }
@@ -336,6 +339,8 @@ __device__ inline void lsteps(StepSeq<ts...>, const uint32_t (&wa)[16], const h2
 template <int NMAT>
 __device__ inline void compute_round(const uint4 (&A)[NMAT][4], const uint8_t *lx, const uint8_t *lsc, int w,
                                      int lane, const Consts &K, f4 &acc0, f4 &acc1) {
+  // per-lane offsets computed here, not held in registers across the loop
+  asm volatile("" : "+v"(lane), "+v"(w));
   const int r16 = lane & 15, g = lane >> 4, tcol = lane & 7, half = (lane >> 3) & 1;
   uint32_t wa[16], wb[16];
   h2 sa[5], sb[5];
@@ -366,6 +371,125 @@ __device__ inline void compute_round(const uint4 (&A)[NMAT][4], const uint8_t *l
   const uint8_t *xb = lx + 16 * ((g * moe::kSteps * 2 + half) * 8 + tcol);
   h8 xr[2] = {lds_h8(xb), lds_h8(xb + 256)};
   lsteps<NMAT>(AllSteps{}, wa, sa, wb, sb, K, xr, xb, acc0, acc1);
+}
+
+// ---------------------------------------------------------------------------
+// Split last round.  When the last round holds r < 4 superblocks, lane groups
+// past r would compute a whole round on zeros.  Instead the words are left as
+// loaded (lane group g holds word quad g of superblock 4R + i in A[i]) and
+// each superblock is 5 MFMA steps: lane group g takes steps 5 g .. 5 g + 4 of
+// it, i.e. pairs 20 g .. 20 g + 19 (quad g), whose activations are the
+// record's steps 5 g + t'.  Quad g spans blocks g and g + 1 of the
+// superblock (its first column is 40 g, and 40 g / 32 = g); a pair's two
+// columns are (g, g), (g, g + 1) or (g + 1, g + 1), which depends on g, so the
+// scale register of each pair is picked per lane with v_cndmask.
+// ---------------------------------------------------------------------------
+
+// scale class of local pair q (0..19) of quad g: 0 = both columns in block g,
+// 2 = low in g and high in g + 1, 3 = both in g + 1
+constexpr int quad_cls(int g, int q) {
+  const int col = 40 * g + pair_col(q);
+  return (col / 32 - g) + 2 * ((col + 5) / 32 - g);
+}
+
+struct QuadScales {
+  h2 s00, s01, s11;
+};
+
+__device__ inline h2 cls_reg(const QuadScales &S, int c) { return c == 0 ? S.s00 : (c == 2 ? S.s01 : S.s11); }
+
+// the class only grows with g (the quad's offset inside its first block is
+// 0, 8, 16, 24), so one select per change of class; ge[k] = (g >= k)
+template <int q>
+__device__ inline h2 tail_scale(const QuadScales &S, const bool (&ge)[4]) {
+  constexpr int c0 = quad_cls(0, q), c1 = quad_cls(1, q), c2 = quad_cls(2, q), c3 = quad_cls(3, q);
+  static_assert(c0 <= c1 && c1 <= c2 && c2 <= c3, "class grows with the lane group");
+  h2 r = cls_reg(S, c0);
+  if constexpr (c1 != c0) r = ge[1] ? cls_reg(S, c1) : r;
+  if constexpr (c2 != c1) r = ge[2] ? cls_reg(S, c2) : r;
+  if constexpr (c3 != c2) r = ge[3] ? cls_reg(S, c3) : r;
+  return r;
+}
+
+// scales of blocks b and b + 1 of this lane's row (LDS [dword][row] copy)
+__device__ inline QuadScales quad_scales(const uint8_t *sc, int b) {
+  const uint32_t r0 = *reinterpret_cast<const uint16_t *>(sc + (b >> 1) * 256 + (b & 1) * 2);
+  const uint32_t r1 = *reinterpret_cast<const uint16_t *>(sc + ((b + 1) >> 1) * 256 + ((b + 1) & 1) * 2);
+  QuadScales S;
+  S.s00 = __builtin_bit_cast(h2, r0 | (r0 << 16));
+  S.s01 = __builtin_bit_cast(h2, r0 | (r1 << 16));
+  S.s11 = __builtin_bit_cast(h2, r1 | (r1 << 16));
+  return S;
+}
+
+template <int q>
+__device__ inline h2 tail_deq(const uint32_t (&w)[4], const Consts &K, const QuadScales &S, const bool (&ge)[4]) {
+  constexpr int j = q % 5;
+  return deq_pair<j>(j < 3 ? w[q / 5] : (w[q / 5] >> 9), K, tail_scale<q>(S, ge));
+}
+
+template <int t>
+__device__ inline h8 tail_a(const uint32_t (&w)[4], const Consts &K, const QuadScales &S, const bool (&ge)[4]) {
+  const h2 a0 = tail_deq<4 * t + 0>(w, K, S, ge);
+  const h2 a1 = tail_deq<4 * t + 1>(w, K, S, ge);
+  const h2 a2 = tail_deq<4 * t + 2>(w, K, S, ge);
+  const h2 a3 = tail_deq<4 * t + 3>(w, K, S, ge);
+  return (h8){a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+}
+
+template <int NMAT, int t>
+__device__ inline void tail_step(const uint32_t (&wa)[4], const QuadScales &Sa, const uint32_t (&wb)[4],
+                                 const QuadScales &Sb, const Consts &K, const bool (&ge)[4], const uint8_t *xb,
+                                 f4 &acc0, f4 &acc1) {
+  const h8 x = lds_h8(xb + t * 256);
+  if constexpr (NMAT == 2) {
+    acc0 = mfma(tail_a<t>(wa, K, Sa, ge), x, acc0);
+    acc1 = mfma(tail_a<t>(wb, K, Sb, ge), x, acc1);
+  } else if constexpr (t % 2 == 0) {
+    acc0 = mfma(tail_a<t>(wa, K, Sa, ge), x, acc0);
+  } else {
+    acc1 = mfma(tail_a<t>(wa, K, Sa, ge), x, acc1);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// superblock i of a split round
+template <int NMAT, int i>
+__device__ inline void tail_superblock(const uint4 (&A)[NMAT][4], const uint8_t *lx, const uint8_t *lsc, int w,
+                                       int lane, const Consts &K, const bool (&ge)[4], f4 &acc0, f4 &acc1) {
+  const int r16 = lane & 15, g = lane >> 4, tcol = lane & 7, half = (lane >> 3) & 1;
+  const uint8_t *sc = lsc + (w * 16 + r16) * 4;
+  const uint32_t wa[4] = {A[0][i].x, A[0][i].y, A[0][i].z, A[0][i].w};
+  const QuadScales Sa = quad_scales(sc, 5 * i + g);
+  uint32_t wb[4] = {0u, 0u, 0u, 0u};
+  QuadScales Sb = Sa;
+  if constexpr (NMAT == 2) {
+    wb[0] = A[NMAT - 1][i].x;
+    wb[1] = A[NMAT - 1][i].y;
+    wb[2] = A[NMAT - 1][i].z;
+    wb[3] = A[NMAT - 1][i].w;
+    Sb = quad_scales(sc + kScBytesPerMat, 5 * i + g);
+  }
+  const uint8_t *xb = lx + 16 * ((((i * moe::kSteps + 5 * g) * 2) + half) * 8 + tcol);
+  tail_step<NMAT, 0>(wa, Sa, wb, Sb, K, ge, xb, acc0, acc1);
+  tail_step<NMAT, 1>(wa, Sa, wb, Sb, K, ge, xb, acc0, acc1);
+  tail_step<NMAT, 2>(wa, Sa, wb, Sb, K, ge, xb, acc0, acc1);
+  tail_step<NMAT, 3>(wa, Sa, wb, Sb, K, ge, xb, acc0, acc1);
+  tail_step<NMAT, 4>(wa, Sa, wb, Sb, K, ge, xb, acc0, acc1);
+}
+
+// a split round of r (1..3) superblocks
+template <int NMAT>
+__device__ inline void compute_tail(const uint4 (&A)[NMAT][4], int r, const uint8_t *lx, const uint8_t *lsc, int w,
+                                    int lane, const Consts &K, f4 &acc0, f4 &acc1) {
+  // opaque copy: keeps the tail's per-lane addresses and masks from being
+  // hoisted out of the stream loop, where they would hold registers all along
+  asm volatile("" : "+v"(lane), "+v"(w));
+  const int g = lane >> 4;
+  const bool ge[4] = {true, g >= 1, g >= 2, g >= 3};
+  tail_superblock<NMAT, 0>(A, lx, lsc, w, lane, K, ge, acc0, acc1);
+  if (r > 1) tail_superblock<NMAT, 1>(A, lx, lsc, w, lane, K, ge, acc0, acc1);
+  if (r > 2) tail_superblock<NMAT, 2>(A, lx, lsc, w, lane, K, ge, acc0, acc1);
 }
 
 // gate/up: h = silu(g) u into the h record; down: y
@@ -430,7 +554,7 @@ __device__ inline Mats<NMAT> mats_of(const DecodeParams &P) {
 // Returns false when the stream ends.
 template <int NMAT>
 __device__ inline bool stream_round(const DecodeParams &P, const Mats<NMAT> &Mt, int tpu, int u_end, int u_step,
-                                    int rounds,
+                                    int rounds, int split_r,
                                     int w, int lane, int &u, int &R, Unit &U, uint8_t *lx_cur, uint8_t *lsc_cur,
                                     uint8_t *lx_nxt, uint8_t *lsc_nxt, const uint4 (&Acur)[NMAT][4],
                                     uint4 (&Anxt)[NMAT][4], const Consts &K, f4 &acc0, f4 &acc1) {
@@ -444,15 +568,19 @@ __device__ inline bool stream_round(const DecodeParams &P, const Mats<NMAT> &Mt,
     stage_round<NMAT>(Mt, Un, Rn, w, lane, lx_nxt, lsc_nxt);
     load_round_words<NMAT>(Mt, Un, Rn, Anxt);
   }
-  compute_round<NMAT>(Acur, lx_cur, lsc_cur, w, lane, K, acc0, acc1);
+  if (last && split_r)
+    compute_tail<NMAT>(Acur, split_r, lx_cur, lsc_cur, w, lane, K, acc0, acc1);
+  else
+    compute_round<NMAT>(Acur, lx_cur, lsc_cur, w, lane, K, acc0, acc1);
   if (last) {
     unit_epilogue<NMAT>(P, U, w, lane, acc0, acc1);
     acc0 = acc1 = (f4){0.f, 0.f, 0.f, 0.f};
   }
   if (!more) return false;
   wait_loads_and_sync();
+  if (!(split_r && Rn + 1 == rounds))
 #pragma unroll
-  for (int mat = 0; mat < NMAT; ++mat) transpose_quads(Anxt[mat]);
+    for (int mat = 0; mat < NMAT; ++mat) transpose_quads(Anxt[mat]);
   u = un;
   R = Rn;
   U = Un;
@@ -468,6 +596,11 @@ __global__ void __launch_bounds__(64 * kWaves, 3) ffn_decode_kernel(DecodeParams
   const int ntile = Mt.m[0].rows / 16;
   const int tpu = (ntile + kWaves - 1) / kWaves;
   const int rounds = (Mt.m[0].nsb + 3) / 4;
+  // superblocks of a split last round (0: none).  Down only: 768 columns are
+  // 5 superblocks, so a whole second round would be 3/4 idle.  Gate/up keeps
+  // whole rounds (13 superblocks, the last round 1/4 used): with both paths
+  // in that kernel the register allocator spills and the kernel ran slower.
+  const int split_r = NMAT == 1 ? Mt.m[0].nsb % 4 : 0;
   const int n_units = min(P.n_work[0], P.max_work) * tpu;
   // Workgroup b runs on XCD b % 8 (round-robin dispatch).  Each XCD takes a
   // contiguous range of units, so the tiles of neighbouring entries -- both
@@ -484,14 +617,15 @@ __global__ void __launch_bounds__(64 * kWaves, 3) ffn_decode_kernel(DecodeParams
   stage_round<NMAT>(Mt, U, 0, w, lane, lx[0], lsc[0]);
   load_round_words<NMAT>(Mt, U, 0, A0);
   wait_loads_and_sync();
+  if (!(split_r && rounds == 1))
 #pragma unroll
-  for (int mat = 0; mat < NMAT; ++mat) transpose_quads(A0[mat]);
+    for (int mat = 0; mat < NMAT; ++mat) transpose_quads(A0[mat]);
   const Consts K = make_consts();
   f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   // the two register sets and LDS buffers alternate by round
-  while (stream_round<NMAT>(P, Mt, tpu, u_end, u_step, rounds, w, lane, u, R, U, lx[0], lsc[0], lx[1], lsc[1], A0,
+  while (stream_round<NMAT>(P, Mt, tpu, u_end, u_step, rounds, split_r, w, lane, u, R, U, lx[0], lsc[0], lx[1], lsc[1], A0,
                             A1, K, acc0, acc1) &&
-         stream_round<NMAT>(P, Mt, tpu, u_end, u_step, rounds, w, lane, u, R, U, lx[1], lsc[1], lx[0], lsc[0], A1,
+         stream_round<NMAT>(P, Mt, tpu, u_end, u_step, rounds, split_r, w, lane, u, R, U, lx[1], lsc[1], lx[0], lsc[0], A1,
                             A0, K, acc0, acc1)) {
   }
 }
