@@ -77,6 +77,8 @@ typedef struct {
   int64_t misses;       /* copied in from the host store */
   uint64_t bytes_h2d;   /* bytes copied host -> device for misses */
   int64_t resolve_calls;
+  int64_t failed_calls; /* calls that could not pin their working set (moe_cache_resolve_async
+                           reports its capacity failures only here) */
 } moe_resolve_info;
 
 /* Bytes between consecutive blobs: the layout above rounded up to 256.
@@ -123,6 +125,22 @@ moe_status moe_route(moe_ctx *ctx, int32_t layer, const float *x, int32_t T,
  * call's counts. */
 moe_status moe_cache_resolve(moe_ctx *ctx, int32_t layer, const int32_t *idx, int32_t T,
                              int32_t *slot_of_pair, moe_resolve_info *info, void *stream);
+
+/* The same slot assignment with no host round trip, so that a whole decode
+ * step can be enqueued (or captured in a HIP graph) without synchronising:
+ * the resolve kernel is followed on `stream` by a fill kernel that copies each
+ * missed blob from host_store[id] to slot_pool[slot] by reading the pinned host
+ * store directly (zero-copy over the host link).  host_store must be mapped
+ * into the device address space (memory from hipHostMalloc is); otherwise the
+ * call returns MOE_ERR_INVALID and enqueues nothing.  The clock and the slot
+ * table live in device memory and are shared with moe_cache_resolve: the two
+ * may be mixed on one context, and give the same slots call for call.  A call
+ * that touches more identities than n_slots changes no table entry, writes -1
+ * to every slot_of_pair entry (moe_expert_ffn then writes no output for those
+ * pairs) and counts one failed call in moe_get_stats; nothing else reports it.
+ * Calls on one context must not overlap; they are ordered by `stream`. */
+moe_status moe_cache_resolve_async(moe_ctx *ctx, int32_t layer, const int32_t *idx, int32_t T,
+                                   int32_t *slot_of_pair, void *stream);
 
 /* Expert FFNs of one layer:  for every pair p = t*top_k + j,
  *   y_pairs[p] = W_d (silu(W_g x_t) * (W_u x_t))  with the expert blob at

@@ -48,6 +48,7 @@ class moe_resolve_info(ctypes.Structure):
         ("misses", ctypes.c_int64),
         ("bytes_h2d", ctypes.c_uint64),
         ("resolve_calls", ctypes.c_int64),
+        ("failed_calls", ctypes.c_int64),
     ]
 
     def as_dict(self):
@@ -68,6 +69,7 @@ _SIGS = {
     "moe_destroy": (_I, [_P]),
     "moe_route": (_I, [_P, _I, _P, _I, _P, _P, _P, _P, _P, _P]),
     "moe_cache_resolve": (_I, [_P, _I, _P, _I, _P, ctypes.POINTER(moe_resolve_info), _P]),
+    "moe_cache_resolve_async": (_I, [_P, _I, _P, _I, _P, _P]),
     "moe_expert_ffn": (_I, [_P, _I, _P, _I, _P, _P, _P, _P, _I, _P]),
     "moe_combine": (_I, [_P, _P, _P, _P, _I, _P, _P]),
     "moe_bucket": (_I, [_P, _P, _I, _P, _P, _P]),
@@ -162,6 +164,11 @@ def moe_cache_resolve(ctx, layer, idx, T, slot_of_pair, info=None, stream=None):
                                     ctypes.byref(ri) if ri is not None else None, _stream(stream)),
            "moe_cache_resolve")
     return ri.as_dict() if ri is not None else None
+
+
+def moe_cache_resolve_async(ctx, layer, idx, T, slot_of_pair, stream=None):
+    _check(load().moe_cache_resolve_async(ctx, layer, _ptr(idx), T, _ptr(slot_of_pair), _stream(stream)),
+           "moe_cache_resolve_async")
 
 
 def moe_expert_ffn(ctx, layer, x, T, idx, slot_of_pair, y_pairs, y_shared, path=MOE_PATH_AUTO, stream=None):

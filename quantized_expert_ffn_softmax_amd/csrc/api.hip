@@ -89,8 +89,7 @@ extern "C" moe_status moe_create(const moe_config *cfg, moe_ctx **out) {
   c->cfg = k;
   c->L = moe::make_layout(k.d_model, k.d_ff);
   c->resident = resident;
-  c->clock = 0;
-  c->bytes_h2d = 0;
+  c->host_dev = nullptr;
   hipError_t e = hipGetDevice(&c->device);
   c->max_pairs = k.max_tokens * k.top_k;
   c->max_work = c->max_pairs / moe::kEntryTokens + (c->max_pairs < k.n_experts ? c->max_pairs : k.n_experts) +
@@ -137,6 +136,15 @@ extern "C" moe_status moe_create(const moe_config *cfg, moe_ctx **out) {
   TRY(hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking));
   TRY(hipEventCreateWithFlags(&c->ev_main, hipEventDisableTiming));
   TRY(hipEventCreateWithFlags(&c->ev_copy, hipEventDisableTiming));
+  if (e == hipSuccess && k.host_store) {
+    // the zero-copy miss fill needs the store mapped into the device address
+    // space (pinned memory from hipHostMalloc is); otherwise only the copying
+    // path is available
+    void *dp = nullptr;
+    if (hipHostGetDevicePointer(&dp, const_cast<void *>(k.host_store), 0) == hipSuccess && dp)
+      c->host_dev = static_cast<const uint8_t *>(dp);
+    (void)hipGetLastError();
+  }
   // empty cache: every identity unmapped, every slot free
   TRY(hipMemset(c->slot_of, 0xff, ids * sizeof(int32_t)));
   TRY(hipMemset(c->id_of, 0xff, (size_t)k.n_slots * sizeof(int32_t)));
@@ -187,7 +195,7 @@ extern "C" moe_status moe_cache_resolve(moe_ctx *c, int32_t layer, const int32_t
   MOE_CHECK(idx, MOE_ERR_INVALID, "moe_cache_resolve: null idx");
   MOE_CHECK(c->resident || slot_of_pair, MOE_ERR_INVALID, "moe_cache_resolve: a capped cache needs slot_of_pair");
   hipStream_t s = as_stream(stream);
-  hipError_t e = moe::launch_resolve(c, layer, idx, T, slot_of_pair, s);
+  hipError_t e = moe::launch_resolve(c, layer, idx, T, slot_of_pair, false, s);
   if (e != hipSuccess) return moe_fail(MOE_ERR_HIP, std::string("moe_cache_resolve: ") + hipGetErrorString(e));
   if (c->resident) {
     if (info) {
@@ -199,6 +207,7 @@ extern "C" moe_status moe_cache_resolve(moe_ctx *c, int32_t layer, const int32_t
       info->misses = 0;
       info->bytes_h2d = 0;
       info->resolve_calls = 1;
+      info->failed_calls = 0;
     }
     return MOE_OK;
   }
@@ -212,7 +221,6 @@ extern "C" moe_status moe_cache_resolve(moe_ctx *c, int32_t layer, const int32_t
                                           " identities but the pool has " + std::to_string(c->cfg.n_slots) + " slots");
   }
   if (err) return moe_fail(MOE_ERR_CAPACITY, "moe_cache_resolve: no eligible slot; call moe_cache_reset");
-  c->clock += 1;
   const size_t stride = c->L.stride;
   if (nmiss > 0) {
     // the work already on `s` (which may read evicted slots) has completed:
@@ -232,14 +240,29 @@ extern "C" moe_status moe_cache_resolve(moe_ctx *c, int32_t layer, const int32_t
     MOE_HIP(hipEventRecord(c->ev_copy, c->side));
     MOE_HIP(hipStreamWaitEvent(s, c->ev_copy, 0));
   }
-  c->bytes_h2d += (uint64_t)nmiss * stride;
   if (info) {
     info->lookups = nuniq;
     info->hits = nuniq - nmiss;
     info->misses = nmiss;
     info->bytes_h2d = (uint64_t)nmiss * stride;
     info->resolve_calls = 1;
+    info->failed_calls = 0;
   }
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_cache_resolve_async(moe_ctx *c, int32_t layer, const int32_t *idx, int32_t T,
+                                              int32_t *slot_of_pair, void *stream) {
+  MOE_CHECK(c, MOE_ERR_INVALID, "moe_cache_resolve_async: null ctx");
+  MOE_CHECK(layer >= 0 && layer < c->cfg.n_layers, MOE_ERR_INVALID, "moe_cache_resolve_async: layer out of range");
+  MOE_CHECK(T >= 1 && T <= c->cfg.max_tokens, MOE_ERR_INVALID, "moe_cache_resolve_async: T must be 1..max_tokens");
+  MOE_CHECK(idx, MOE_ERR_INVALID, "moe_cache_resolve_async: null idx");
+  MOE_CHECK(c->resident || slot_of_pair, MOE_ERR_INVALID, "moe_cache_resolve_async: a capped cache needs slot_of_pair");
+  MOE_CHECK(c->resident || c->host_dev, MOE_ERR_INVALID,
+            "moe_cache_resolve_async: host_store is not mapped into the device address space (allocate it with "
+            "hipHostMalloc)");
+  hipError_t e = moe::launch_resolve(c, layer, idx, T, slot_of_pair, true, as_stream(stream));
+  if (e != hipSuccess) return moe_fail(MOE_ERR_HIP, std::string("moe_cache_resolve_async: ") + hipGetErrorString(e));
   return MOE_OK;
 }
 
@@ -321,8 +344,6 @@ extern "C" moe_status moe_cache_reset(moe_ctx *c) {
   MOE_HIP(hipMemset(c->stamp, 0, (size_t)c->cfg.n_slots * sizeof(uint32_t)));
   MOE_HIP(hipMemset(c->dstats, 0, 8 * sizeof(int64_t)));
   MOE_HIP(hipDeviceSynchronize());
-  c->clock = 0;
-  c->bytes_h2d = 0;
   return MOE_OK;
 }
 
@@ -335,7 +356,8 @@ extern "C" moe_status moe_get_stats(moe_ctx *c, moe_resolve_info *cum) {
   cum->hits = st[1];
   cum->misses = st[2];
   cum->resolve_calls = st[3];
-  cum->bytes_h2d = c->bytes_h2d;
+  cum->bytes_h2d = (uint64_t)st[2] * c->L.stride;  // every miss brings in one blob
+  cum->failed_calls = st[4];
   return MOE_OK;
 }
 

@@ -12,6 +12,15 @@
 // where a free slot s has key s and an occupied eligible slot has key
 // 2^56 + stamp * 2^24 + s.  So one pass finds them all.  Every miss finds a
 // slot iff |U| <= n_slots; otherwise nothing changes and the call fails.
+// The clock lives in device memory (stats[5]) so that a call needs no host
+// state and can sit in a captured graph; it advances only on success.
+//
+// Misses are filled either by the host (hipMemcpyAsync of each missed blob
+// after it has read the miss list back) or, with no host round trip, by
+// fill_kernel: each workgroup copies one chunk of one missed blob from the
+// pinned host store (mapped into the device address space; the reads cross
+// the host link) into its slot.  The pages name the link as the bottleneck
+// of a miss; the zero-copy fill removes the per-layer host synchronisation.
 #include "device_util.h"
 #include "moe_internal.h"
 
@@ -40,8 +49,10 @@ __device__ uint64_t block_min_u64(uint64_t v, uint64_t *sh) {
   return r;
 }
 
+// stats: [0] unique identities, [1] hits, [2] misses, [3] calls, [4] calls that
+// could not pin their working set, [5] the clock
 __global__ void __launch_bounds__(kThreads) resolve_kernel(const int32_t *__restrict__ idx, int n, int layer, int E,
-                                                           int S, int resident, uint32_t clock,
+                                                           int S, int resident, int clear_on_fail,
                                                            int32_t *__restrict__ slot_of, int32_t *__restrict__ id_of,
                                                            uint32_t *__restrict__ stamp,
                                                            int32_t *__restrict__ slot_of_pair,
@@ -53,6 +64,7 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(const int32_t *__rest
   __shared__ int nuniq_sh;
   __shared__ uint64_t shred[17];
   const int tid = threadIdx.x;
+  const uint32_t clock = (uint32_t)stats[5] + 1u;  // written back (by thread 0, last) only on success
   mark[tid] = 0;
   if (tid == 0) nuniq_sh = 0;
   __syncthreads();
@@ -89,10 +101,13 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(const int32_t *__rest
   const int mpos = moe::block_excl_scan_1024(is_miss, &nmiss, scan_sh);
   if (is_miss) miss_e[mpos] = tid;
   if (nuniq > S) {  // cannot pin this call's working set: change nothing
+    if (clear_on_fail)  // no host reads the error: the call's pairs get no slot (no output)
+      for (int p = tid; p < n; p += kThreads) slot_of_pair[p] = -1;
     if (tid == 0) {
       dmiss[0] = nuniq;
       dmiss[1] = 0;
       dmiss[2] = 1;
+      stats[4] += 1;
     }
     return;
   }
@@ -117,10 +132,13 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(const int32_t *__rest
     }
     best = block_min_u64(best, shred);
     if (best == kNone) {  // cannot happen on a consistent table; never write out of range
+      if (clear_on_fail)
+        for (int p = tid; p < n; p += kThreads) slot_of_pair[p] = -1;
       if (tid == 0) {
         dmiss[0] = nuniq;
         dmiss[1] = 0;
         dmiss[2] = 2;
+        stats[4] += 1;
       }
       return;
     }
@@ -155,18 +173,58 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(const int32_t *__rest
     stats[1] += nuniq - nmiss;
     stats[2] += nmiss;
     stats[3] += 1;
+    stats[5] = clock;
   }
+}
+
+// Zero-copy miss fill: workgroup b copies chunk b % kFillChunks of miss
+// b / kFillChunks (if that miss exists) from the mapped host store into its
+// slot.  16-byte loads and stores; the blob stride is a multiple of 256.
+constexpr int kFillChunks = 64;
+constexpr int kFillThreads = 256;
+
+__global__ void __launch_bounds__(kFillThreads) fill_kernel(const int32_t *__restrict__ dmiss,
+                                                            const uint8_t *__restrict__ host_store,
+                                                            uint8_t *__restrict__ slot_pool, uint64_t stride,
+                                                            int64_t n_ids, int n_slots) {
+  const int i = blockIdx.x / kFillChunks, chunk = blockIdx.x % kFillChunks;
+  if (i >= dmiss[1]) return;
+  const int64_t id = dmiss[3 + 2 * i];
+  const int slot = dmiss[4 + 2 * i];
+  if (id < 0 || id >= n_ids || slot < 0 || slot >= n_slots) return;  // never copy out of range
+  const uint64_t n16 = stride / 16, per = (n16 + kFillChunks - 1) / kFillChunks;
+  const uint64_t b0 = chunk * per, b1 = b0 + per < n16 ? b0 + per : n16;
+  const uint4 *src = reinterpret_cast<const uint4 *>(host_store + (uint64_t)id * stride);
+  uint4 *dst = reinterpret_cast<uint4 *>(slot_pool + (uint64_t)slot * stride);
+  // four loads in flight per thread before the stores
+  uint64_t q = b0 + threadIdx.x;
+  for (; q + 3 * kFillThreads < b1; q += 4 * kFillThreads) {
+    const uint4 a0 = src[q], a1 = src[q + kFillThreads], a2 = src[q + 2 * kFillThreads], a3 = src[q + 3 * kFillThreads];
+    dst[q] = a0;
+    dst[q + kFillThreads] = a1;
+    dst[q + 2 * kFillThreads] = a2;
+    dst[q + 3 * kFillThreads] = a3;
+  }
+  for (; q < b1; q += kFillThreads) dst[q] = src[q];
 }
 
 }  // namespace
 
 namespace moe {
 
-hipError_t launch_resolve(moe_ctx *c, int layer, const int32_t *idx, int T, int32_t *slot_of_pair, hipStream_t s) {
+hipError_t launch_resolve(moe_ctx *c, int layer, const int32_t *idx, int T, int32_t *slot_of_pair, bool fill,
+                          hipStream_t s) {
   const int n = T * c->cfg.top_k;
   hipLaunchKernelGGL(resolve_kernel, dim3(1), dim3(kThreads), 0, s, idx, n, layer, c->cfg.n_experts, c->cfg.n_slots,
-                     c->resident ? 1 : 0, c->clock + 1, c->slot_of, c->id_of, c->stamp, slot_of_pair, c->dmiss,
+                     c->resident ? 1 : 0, fill ? 1 : 0, c->slot_of, c->id_of, c->stamp, slot_of_pair, c->dmiss,
                      c->dstats);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || c->resident || !fill) return e;
+  // at most min(pairs, experts) misses per call
+  const int n_miss = n < c->cfg.n_experts ? n : c->cfg.n_experts;
+  hipLaunchKernelGGL(fill_kernel, dim3(n_miss * kFillChunks), dim3(kFillThreads), 0, s, c->dmiss, c->host_dev,
+                     (uint8_t *)c->cfg.slot_pool, (uint64_t)c->L.stride,
+                     (int64_t)c->cfg.n_layers * c->cfg.n_experts, c->cfg.n_slots);
   return hipGetLastError();
 }
 

@@ -91,9 +91,8 @@ struct moe_ctx {
   int32_t *slot_of;   // [n_layers * n_experts]
   int32_t *id_of;     // [n_slots]
   uint32_t *stamp;    // [n_slots]
-  uint32_t clock;
+  const uint8_t *host_dev;  // host_store as mapped into the device address space (null: not mapped)
   int64_t *dstats;    // device: lookups, hits, misses, calls
-  uint64_t bytes_h2d; // host-side (misses are copied by the host)
 
   // workspace (device)
   float *logits_ws;      // [max_tokens][n_experts]
@@ -141,7 +140,7 @@ hipError_t launch_router(const moe_ctx *c, const float *x, int T, const float *w
                          float *logits, int32_t *idx, float *w, hipStream_t s);
 hipError_t launch_bucket(const moe_ctx *c, const int32_t *idx, int T, int32_t *offsets, int32_t *perm,
                          bool build_work, hipStream_t s);
-hipError_t launch_resolve(moe_ctx *c, int layer, const int32_t *idx, int T, int32_t *slot_of_pair,
+hipError_t launch_resolve(moe_ctx *c, int layer, const int32_t *idx, int T, int32_t *slot_of_pair, bool fill,
                           hipStream_t s);
 hipError_t launch_ffn_decode(const moe_ctx *c, int layer, const float *x, int T, const int32_t *idx,
                              const int32_t *slot_of_pair, float *y_pairs, float *y_shared, hipStream_t s);

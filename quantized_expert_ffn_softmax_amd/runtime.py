@@ -59,13 +59,20 @@ class MoeContext:
             out=torch.empty((T, d), dtype=torch.float32, device=dev),
         )
 
-    def layer(self, layer, x, w_router, bias, buf, path=B.MOE_PATH_AUTO, stream=None, logits=True, info=False):
-        """route -> cache_resolve -> expert_ffn -> combine for one layer."""
+    def layer(self, layer, x, w_router, bias, buf, path=B.MOE_PATH_AUTO, stream=None, logits=True, info=False,
+              async_resolve=False):
+        """route -> cache_resolve -> expert_ffn -> combine for one layer.  With
+        ``async_resolve`` the slots come from moe_cache_resolve_async (no host
+        round trip; misses filled by a kernel reading the pinned host store)."""
         T = x.shape[0]
         B.moe_route(self.ctx, layer, x, T, w_router, bias, buf["logits"] if logits else None, buf["idx"], buf["w"],
                     stream)
         slot = buf["slot"] if (not self.resident or logits) else None
-        ri = B.moe_cache_resolve(self.ctx, layer, buf["idx"], T, slot, info, stream)
+        if async_resolve:
+            B.moe_cache_resolve_async(self.ctx, layer, buf["idx"], T, slot, stream)
+            ri = None
+        else:
+            ri = B.moe_cache_resolve(self.ctx, layer, buf["idx"], T, slot, info, stream)
         B.moe_expert_ffn(self.ctx, layer, x, T, buf["idx"], slot, buf["y_pairs"], buf["y_shared"], path, stream)
         B.moe_combine(self.ctx, buf["y_pairs"], buf["w"], buf["y_shared"], T, buf["out"], stream)
         return ri
