@@ -70,6 +70,7 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-layer", action="store_true", help="skip the single-layer T=5 decode measurement")
     ap.add_argument("--no-lru", action="store_true", help="skip the T=1 stack through the 8,445-slot LRU cache")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the speculative-verify batch sweep")
     ap.add_argument("--lru-steps", type=int, default=256)
     ap.add_argument("--lru-warmup", type=int, default=64)
     args = ap.parse_args()
@@ -194,6 +195,8 @@ def main():
     ms_per_step = graph_ms if graph_ms is not None else eager_ms
     value = T / (ms_per_step * 1e-3)
 
+    sweep = None if args.no_sweep else verify_sweep(ctx, routers, biases, seed, d, f, L)
+
     result = {
         "metric": "MoE decode tok/s (48 layers) + prefill tok/s; % of HBM BW / MFMA peak",
         "value": round(value, 1),
@@ -253,6 +256,8 @@ def main():
         log(f"[bench] prefill chunk: layer {layer_ms:.2f} ms ({prefill_T / (layer_ms * 1e-3):.0f} tok/s), "
             f"FFN {ffn_p_ms:.2f} ms = {tflops:.1f} TFLOP/s")
 
+    if sweep is not None:
+        result["verify_sweep"] = sweep
     if not args.no_layer:
         result["decode_layer"] = bench_decode_layer(ctx, routers[0], seed, d, f, E, k)
     cpu_x = xs[W].cpu().numpy()
@@ -428,6 +433,71 @@ def bench_lru(seed, d, f, E, k, L, routers, biases, shared_pool, warmup, steps):
     ctx.close()
     del host, slot_pool
     return out
+
+
+def verify_sweep(ctx, routers, biases, seed, d, f, L, reps=5, warm=2):
+    """Speculative verify as a batch: `slots` requests each verify 1 + `spec`
+    tokens in one pass, T = slots * (1 + spec) tokens per step, for spec 1..6
+    and slots 1..4.  Each T: the 48-layer resident stack captured in a HIP
+    graph, replayed on fresh inputs; reports tok/s and the expert bytes each
+    token costs (touched routed experts + the shared one, per layer)."""
+    import numpy as np
+    import torch
+
+    import moe_synth
+    from quantized_expert_ffn_softmax_amd import binding as B
+    c, k = ctx.ctx, ctx.k
+    blob = algo_blob_bytes(d, f)
+    rows = []
+    for slots in range(1, 5):
+        for spec in range(1, 7):
+            T = slots * (1 + spec)
+            buf = ctx.buffers(T)
+            xin = torch.empty((T, d), dtype=torch.float32, device="cuda")
+            xa, xb = torch.empty_like(xin), torch.empty_like(xin)
+
+            def step():
+                x = xin
+                for l in range(L):
+                    B.moe_route(c, l, x, T, routers[l], biases[l], None, buf["idx"], buf["w"])
+                    B.moe_cache_resolve(c, l, buf["idx"], T, None)
+                    B.moe_expert_ffn(c, l, x, T, buf["idx"], None, buf["y_pairs"], buf["y_shared"],
+                                     B.MOE_PATH_DECODE)
+                    B.moe_combine(c, buf["y_pairs"], buf["w"], buf["y_shared"], T, buf["out"])
+                    xn = xa if (l % 2 == 0) else xb
+                    B.moe_chain_norm(c, buf["out"], T, xn)
+                    x = xn
+
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            cs = torch.cuda.Stream()
+            cs.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.graph(graph, stream=cs):
+                step()
+            torch.cuda.synchronize()
+            xs = [torch.from_numpy(moe_synth.gen_x(seed, 500000 + 100 * T + i, T, d)).cuda() for i in range(warm + reps)]
+            for i in range(warm):
+                xin.copy_(xs[i])
+                graph.replay()
+            torch.cuda.synchronize()
+            st0 = B.moe_get_stats(c)
+            ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(reps)]
+            for i in range(reps):
+                xin.copy_(xs[warm + i])
+                ev[i][0].record()
+                graph.replay()
+                ev[i][1].record()
+            torch.cuda.synchronize()
+            st1 = B.moe_get_stats(c)
+            ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+            distinct = (st1["lookups"] - st0["lookups"]) / (st1["resolve_calls"] - st0["resolve_calls"])
+            rows.append({"slots": slots, "spec": spec, "T": T, "tok_per_s": round(T / (ms * 1e-3), 1),
+                         "ms_per_step": round(ms, 3), "distinct_experts_per_layer": round(distinct, 2),
+                         "expert_mb_per_token": round((distinct + 1) * blob * L / T / 1e6, 1)})
+            del graph
+    log("[bench] verify sweep: " + ", ".join(f"T={r['T']}: {r['tok_per_s']:.0f} tok/s "
+                                             f"{r['expert_mb_per_token']} MB/tok" for r in rows))
+    return {"workload": "verify_sweep", "layers": L, "reps": reps, "rows": rows}
 
 
 def cpu_baseline(seed, d, f, E, k, T, alpha, x0, n_layers):

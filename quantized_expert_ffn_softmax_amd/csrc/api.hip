@@ -127,7 +127,9 @@ extern "C" moe_status moe_create(const moe_config *cfg, moe_ctx **out) {
   c->route_ks = 256 / ((k.n_experts + 15) / 16);
   if (c->route_ks < 1) c->route_ks = 1;
   while (c->route_ks > 1 && k.d_model / 16 < c->route_ks * 8) c->route_ks /= 2;
-  TRY(dalloc(&c->route_part, (size_t)c->route_ks * 16 * k.n_experts));
+  // the MFMA router (and its partials) serves up to 64 tokens
+  c->route_small_t = k.max_tokens < 64 ? k.max_tokens : 64;
+  TRY(dalloc(&c->route_part, (size_t)c->route_ks * c->route_small_t * k.n_experts));
 
   TRY(dalloc(&c->dmiss, 3 + 2 * (size_t)c->max_pairs + 2 * (size_t)k.n_experts));
   if (e == hipSuccess)

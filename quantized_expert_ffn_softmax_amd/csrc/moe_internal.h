@@ -107,8 +107,9 @@ struct moe_ctx {
   uint16_t *h16;         // prefill: [max_pairs + max_tokens][d_ff] fp16
   int32_t *tile_ws;      // prefill tile list
   int32_t *slot_ws;      // [max_pairs] slots when the caller passes none
-  float *route_part;     // [route_ks][16][n_experts] partial logits (decode-size router)
+  float *route_part;     // [route_ks][route_small_t][n_experts] partial logits (decode-size router)
   int32_t route_ks;      // column slices of the decode-size router
+  int32_t route_small_t; // largest T routed by the decode-size router (<= 64)
   int32_t max_pairs;
   int32_t max_work;
   int32_t n_chunks_max;

@@ -116,12 +116,13 @@ __global__ void __launch_bounds__(256) router_topk(const float *__restrict__ log
   topk_row(logits + (size_t)t * E, E, k, idx + (size_t)t * k, w + (size_t)t * k);
 }
 
-// --- decode-size batches (T <= 16): logits on fp32 MFMA.  Workgroup
-// (eg, ks) covers experts 16 eg .. 16 eg + 15 and the ks-th of KS slices of
-// the columns; each of its waves takes every kRouteWaves-th chunk of 16
-// columns of that slice.  v_mfma_f32_16x16x4_f32 with lane (m, g):
-// A = W[16 eg + m][col], B = x[token m][col], col = chunk + 4 g + i for the
-// i-th of the 4 MFMAs of a chunk; D: lane holds experts 4 g + i, token m.
+// --- decode-size batches (T <= 64): logits on fp32 MFMA.  Workgroup
+// (tg, eg, ks) covers tokens 16 tg .. 16 tg + 15, experts 16 eg .. 16 eg + 15
+// and the ks-th of KS slices of the columns; each of its waves takes every
+// kRouteWaves-th chunk of 16 columns of that slice.  v_mfma_f32_16x16x4_f32
+// with lane (m, g): A = W[16 eg + m][col], B = x[token 16 tg + m][col],
+// col = chunk + 4 g + i for the i-th of the 4 MFMAs of a chunk; D: lane holds
+// experts 4 g + i, token 16 tg + m.
 // Wave partials are added in wave order into part[ks][t][e]; a second,
 // single-workgroup kernel adds the KS slices in order, adds the bias and runs
 // the top-k (the kernel boundary is the cross-workgroup handoff: an in-kernel
@@ -135,18 +136,19 @@ __global__ void __launch_bounds__(64 * kRouteWaves) router_logits_mfma(const flo
   __shared__ float red[kRouteWaves][64][4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m = lane & 15, g = lane >> 4;
-  const int eg = blockIdx.x / KS, ks = blockIdx.x % KS;
-  const int e = 16 * eg + m;
+  const int n_eg = (E + 15) / 16;
+  const int tg = blockIdx.x / (n_eg * KS), eg = (blockIdx.x / KS) % n_eg, ks = blockIdx.x % KS;
+  const int e = 16 * eg + m, tok = 16 * tg + m;
   const int nchunk = d / 16;
   const int c0 = (int)((long)nchunk * ks / KS), c1 = (int)((long)nchunk * (ks + 1) / KS);
   f4v acc = {0.f, 0.f, 0.f, 0.f};
   const float *wrow = wr + (size_t)(e < E ? e : 0) * d;
-  const float *xrow = x + (size_t)(m < T ? m : 0) * d;
+  const float *xrow = x + (size_t)(tok < T ? tok : 0) * d;
   for (int ch = c0 + wave; ch < c1; ch += kRouteWaves) {
     const int col = ch * 16 + 4 * g;
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
     if (e < E) a = *reinterpret_cast<const float4 *>(wrow + col);
-    if (m < T) b = *reinterpret_cast<const float4 *>(xrow + col);
+    if (tok < T) b = *reinterpret_cast<const float4 *>(xrow + col);
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, acc, 0, 0, 0);
@@ -160,7 +162,7 @@ __global__ void __launch_bounds__(64 * kRouteWaves) router_logits_mfma(const flo
     for (int i = 0; i < 4; ++i) {
       float v = red[0][lane][i];
       for (int ww = 1; ww < kRouteWaves; ++ww) v += red[ww][lane][i];
-      const int ee = 16 * eg + 4 * g + i, t = m;
+      const int ee = 16 * eg + 4 * g + i, t = tok;
       if (ee < E && t < T) part[((size_t)ks * T + t) * E + ee] = v;
     }
   }
@@ -249,10 +251,11 @@ namespace moe {
 hipError_t launch_router(const moe_ctx *c, const float *x, int T, const float *wr, const float *bias, float *logits,
                          int32_t *idx, float *w, hipStream_t s) {
   const int E = c->cfg.n_experts, d = c->cfg.d_model, k = c->cfg.top_k;
-  if (T <= 16) {
+  if (T <= c->route_small_t) {
     const int KS = c->route_ks;
-    hipLaunchKernelGGL(router_logits_mfma, dim3(((E + 15) / 16) * KS), dim3(64 * kRouteWaves), 0, s, x, T, d, wr, E,
-                       KS, c->route_part);
+    const int n_tg = (T + 15) / 16;
+    hipLaunchKernelGGL(router_logits_mfma, dim3(n_tg * ((E + 15) / 16) * KS), dim3(64 * kRouteWaves), 0, s, x, T, d,
+                       wr, E, KS, c->route_part);
     hipLaunchKernelGGL(router_finish_small, dim3(T), dim3((E + 63) / 64 * 64), 0, s, c->route_part, T, E, KS, bias,
                        k, logits, idx, w);
     return hipGetLastError();

@@ -86,6 +86,14 @@ def test_real_layer_decode_T15_zipf():
     layer.close()
 
 
+def test_real_layer_decode_T28_zipf():
+    # 4 request slots x (1 + 6) verified tokens: the decode-size router's largest
+    # batches take two 16-token groups
+    layer = _layer(T=28, alpha=0.75, **REAL)
+    _check_layer(layer, B.MOE_PATH_DECODE, "fp16_weights", 1e-4)
+    layer.close()
+
+
 def test_real_layer_prefill_small():
     layer = _layer(T=200, alpha=0.75, **REAL)
     _check_layer(layer, B.MOE_PATH_PREFILL, "fp16_operands", TOL)
