@@ -170,21 +170,26 @@ __global__ void __launch_bounds__(64 * kRouteWaves) router_logits_mfma(const flo
 
 // One workgroup per token: logits = sum of the KS slices (in order) + bias,
 // then the top-k by rank, where an expert's rank is the number of experts
-// ordered before it by (logit desc, index asc).  Two passes: each wave ranks
-// its 64 experts among themselves; an expert of global rank < k has wave rank
-// < k, so only those candidates (k per wave) are ranked against each other,
-// and for a candidate in the global top-k that rank is its global rank (every
+// ordered before it by (logit desc, index asc).  The order is that of one
+// 64-bit key, (logit mapped to an order-preserving uint32) << 32 | ~index, so
+// each comparison is one v_cmp_gt_u64.  Two passes: each wave ranks its 64
+// experts among themselves; an expert of global rank < k has wave rank < k,
+// so only those candidates (k per wave) are ranked against each other, and
+// for a candidate in the global top-k that rank is its global rank (every
 // expert ordered before it is a candidate too).  Weights: softmax of the k
 // chosen logits.
-__device__ inline bool before(float u, int ou, float v, int ov) { return u > v || (u == v && ou < ov); }
+__device__ inline uint64_t order_key(float v, int e) {
+  const uint32_t b = v == 0.f ? 0u : __float_as_uint(v);  // -0 and +0 are equal logits
+  const uint32_t mono = (b & 0x80000000u) ? ~b : (b | 0x80000000u);  // larger float -> larger uint
+  return ((uint64_t)mono << 32) | (uint32_t)~(uint32_t)e;               // equal logits: lower index larger
+}
 
 __global__ void __launch_bounds__(1024) router_finish_small(const float *__restrict__ part, int T, int E, int KS,
                                                             const float *__restrict__ bias, int k,
                                                             float *__restrict__ logits, int32_t *__restrict__ idx,
                                                             float *__restrict__ w) {
-  __shared__ float lg[1024];
-  __shared__ float cv[16 * 32];
-  __shared__ int ci[16 * 32];
+  __shared__ uint64_t lk[1024];
+  __shared__ uint64_t ck[16 * 32];
   __shared__ float top[32];
   const int t = blockIdx.x, e = threadIdx.x, wave = e >> 6;
   float v = -INFINITY;
@@ -201,46 +206,31 @@ __global__ void __launch_bounds__(1024) router_finish_small(const float *__restr
     v += bias ? bias[e] : 0.f;
     logits[(size_t)t * E + e] = v;
   }
-  lg[e] = v;
+  const uint64_t key = e < E ? order_key(v, e) : 0ull;  // lanes past E order after everything
+  lk[e] = key;
+  const int nw = blockDim.x / 64;
+  for (int i = e; i < nw * k; i += blockDim.x) ck[i] = 0ull;  // empty candidate: orders before nothing
   __syncthreads();
   // pass 1: rank inside the wave
   int r1 = 0;
-  for (int o = wave * 64; o < wave * 64 + 64; ++o) r1 += before(lg[o], o, v, e);
-  const int nw = blockDim.x / 64;
-  for (int i = e; i < nw * k; i += blockDim.x) ci[i] = -1;
-  __syncthreads();
-  if (e < E && r1 < k) {
-    cv[wave * k + r1] = v;
-    ci[wave * k + r1] = e;
-  }
+#pragma unroll 16
+  for (int o = 0; o < 64; ++o) r1 += lk[wave * 64 + o] > key;
+  if (e < E && r1 < k) ck[wave * k + r1] = key;
   __syncthreads();
   // pass 2: rank among the candidates
+  int r = k;
   if (e < E && r1 < k) {
-    // candidates read 16 at a time so the LDS reads overlap
-    int r = 0;
-    for (int i0 = 0; i0 < nw * k; i0 += 16) {
-      int o[16];
-      float c[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        o[i] = i0 + i < nw * k ? ci[i0 + i] : -1;
-        c[i] = i0 + i < nw * k ? cv[i0 + i] : 0.f;
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) r += (o[i] >= 0) && before(c[i], o[i], v, e);
-    }
-    r1 = r;  // global rank when < k
+    r = 0;
+    for (int i = 0; i < nw * k; ++i) r += ck[i] > key;
     if (r < k) top[r] = v;
-  } else {
-    r1 = k;
   }
   __syncthreads();
-  if (e < E && r1 < k) {
+  if (r < k) {
     const float m = top[0];
     float sum = 0.f;
     for (int j = 0; j < k; ++j) sum += expf(top[j] - m);
-    idx[(size_t)t * k + r1] = e;
-    w[(size_t)t * k + r1] = expf(v - m) / sum;
+    idx[(size_t)t * k + r] = e;
+    w[(size_t)t * k + r] = expf(v - m) / sum;
   }
 }
 

@@ -126,3 +126,29 @@ def test_bucket_small_and_large():
         torch.cuda.synchronize()
         check_bucket(off.cpu().numpy(), perm.cpu().numpy(), idx, 512)
         ctx.close()
+
+
+@pytest.mark.parametrize("T", [8, 40, 100])
+def test_router_exact_ties(T):
+    # zero router weights: every logit is exactly its bias, and the bias holds
+    # repeated values (and a -0.0 beside +0.0), so the top-k is decided by the
+    # index rule alone; both router paths (T <= 64 and above) must pick the
+    # lowest indices among equal logits and weight them by the softmax
+    from quantized_expert_ffn_softmax_amd.runtime import MoeContext
+    E, k, d = 64, 8, 256
+    ctx = MoeContext(d, 128, E, k, 1, None, T)
+    x = torch.from_numpy(moe_synth.gen_x(1, 0, T, d)).cuda()
+    wr = torch.zeros((E, d), dtype=torch.float32, device="cuda")
+    bias_np = np.array([(e * 7) % 5 for e in range(E)], dtype=np.float32) * np.float32(0.25)
+    bias_np[[0, 5, 10]] = 0.0
+    bias_np[[3, 8]] = -0.0
+    bias = torch.from_numpy(bias_np).cuda()
+    buf = ctx.buffers(T)
+    B.moe_route(ctx.ctx, 0, x, T, wr, bias, buf["logits"], buf["idx"], buf["w"])
+    torch.cuda.synchronize()
+    logits = buf["logits"].cpu().numpy()
+    assert np.array_equal(logits, np.broadcast_to(bias_np, (T, E)))
+    want_idx, want_w = oracle.topk_from_logits(logits, k)
+    assert np.array_equal(buf["idx"].cpu().numpy(), want_idx)
+    assert np.abs(buf["w"].cpu().numpy() - want_w).max() <= 1e-6
+    ctx.close()
