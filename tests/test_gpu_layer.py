@@ -58,6 +58,14 @@ def test_tiny_decode(T):
     layer.close()
 
 
+def test_tiny_decode_past_the_small_bucketing():
+    # 140 tokens x 8 of 64 experts = 1,120 pairs: the multi-workgroup bucketing,
+    # whose entries carry no row lists (the decode kernels then read perm)
+    layer = _layer(T=140, **dict(TINY, n_experts=64, top_k=8))
+    _check_layer(layer, B.MOE_PATH_DECODE, "fp16_weights", 1e-4)
+    layer.close()
+
+
 @pytest.mark.parametrize("T", [1, 8, 65, 130])
 def test_tiny_prefill(T):
     layer = _layer(T=T, **TINY)
