@@ -6,8 +6,9 @@ verified together -- through the 48-layer stack, every layer routing each
 token to 10 of 512 experts plus the shared expert, with all 24,576 expert
 identities resident in HBM (54.8 GB of 3-bit blobs) and Zipf-skewed router
 bias (alpha 0.75).  Per layer: moe_route -> moe_cache_resolve ->
-moe_expert_ffn (decode path) -> moe_combine -> moe_chain_norm (which feeds
-the next layer).  Inputs are synthetic and seeded; weights are random.
+moe_expert_ffn (decode path) -> moe_combine_norm (moe_combine and the
+stacking normalisation moe_chain_norm in one kernel; it feeds the next
+layer).  Inputs are synthetic and seeded; weights are random.
 
 Also timed: the prefill chunk (12,288 tokens through one layer, prefill path),
 and the CPU oracle on a bounded sample of the decode workload.
@@ -129,9 +130,8 @@ def main():
             B.moe_expert_ffn(c, l, x, T, buf["idx"], None, buf["y_pairs"], buf["y_shared"], B.MOE_PATH_DECODE)
             if ev is not None:
                 ev[l][1].record()
-            B.moe_combine(c, buf["y_pairs"], buf["w"], buf["y_shared"], T, buf["out"])
             xn = xa if (l % 2 == 0) else xb
-            B.moe_chain_norm(c, buf["out"], T, xn)
+            B.moe_combine_norm(c, buf["y_pairs"], buf["w"], buf["y_shared"], T, buf["out"], xn)
             x = xn
 
     for s in range(W):
@@ -362,9 +362,8 @@ def bench_lru(seed, d, f, E, k, L, routers, biases, shared_pool, warmup, steps):
                 B.moe_cache_resolve(c, l, buf["idx"], T, buf["slot"])
             B.moe_expert_ffn(c, l, x, T, buf["idx"], buf["slot"], buf["y_pairs"], buf["y_shared"],
                              B.MOE_PATH_DECODE)
-            B.moe_combine(c, buf["y_pairs"], buf["w"], buf["y_shared"], T, buf["out"])
             xn = xa if (l % 2 == 0) else xb
-            B.moe_chain_norm(c, buf["out"], T, xn)
+            B.moe_combine_norm(c, buf["y_pairs"], buf["w"], buf["y_shared"], T, buf["out"], xn)
             x = xn
 
     xs = [torch.from_numpy(moe_synth.gen_x(seed, 300000 + s, T, d)).cuda() for s in range(warmup + steps)]
@@ -463,9 +462,8 @@ def verify_sweep(ctx, routers, biases, seed, d, f, L, reps=5, warm=2):
                     B.moe_cache_resolve(c, l, buf["idx"], T, None)
                     B.moe_expert_ffn(c, l, x, T, buf["idx"], None, buf["y_pairs"], buf["y_shared"],
                                      B.MOE_PATH_DECODE)
-                    B.moe_combine(c, buf["y_pairs"], buf["w"], buf["y_shared"], T, buf["out"])
                     xn = xa if (l % 2 == 0) else xb
-                    B.moe_chain_norm(c, buf["out"], T, xn)
+                    B.moe_combine_norm(c, buf["y_pairs"], buf["w"], buf["y_shared"], T, buf["out"], xn)
                     x = xn
 
             torch.cuda.synchronize()

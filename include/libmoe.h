@@ -194,6 +194,15 @@ moe_status moe_get_stats(moe_ctx *ctx, moe_resolve_info *cumulative);
  * fp32.  out [T][d_model], x_next [T][d_model] (may not alias).  Asynchronous. */
 moe_status moe_chain_norm(moe_ctx *ctx, const float *out, int32_t T, float *x_next, void *stream);
 
+/* moe_combine followed by moe_chain_norm in one kernel (one workgroup per
+ * token), for stacks that chain layers: out[t] as moe_combine writes it, and
+ * x_next[t] as moe_chain_norm would compute it from that out -- bit for bit the
+ * two calls' results, one dispatch instead of two.  Same shapes, alignment and
+ * asynchrony as those calls; out and x_next must not overlap. */
+moe_status moe_combine_norm(moe_ctx *ctx, const float *y_pairs, const float *w,
+                            const float *y_shared, int32_t T, float *out, float *x_next,
+                            void *stream);
+
 const char *moe_status_str(moe_status s);
 /* Detail of the last error on the calling thread ("" if none). */
 const char *moe_last_error(void);

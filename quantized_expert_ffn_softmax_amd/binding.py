@@ -70,6 +70,7 @@ _SIGS = {
     "moe_route": (_I, [_P, _I, _P, _I, _P, _P, _P, _P, _P, _P]),
     "moe_cache_resolve": (_I, [_P, _I, _P, _I, _P, ctypes.POINTER(moe_resolve_info), _P]),
     "moe_cache_resolve_async": (_I, [_P, _I, _P, _I, _P, _P]),
+    "moe_combine_norm": (_I, [_P, _P, _P, _P, _I, _P, _P, _P]),
     "moe_expert_ffn": (_I, [_P, _I, _P, _I, _P, _P, _P, _P, _I, _P]),
     "moe_combine": (_I, [_P, _P, _P, _P, _I, _P, _P]),
     "moe_bucket": (_I, [_P, _P, _I, _P, _P, _P]),
@@ -200,6 +201,11 @@ def moe_get_stats(ctx) -> dict:
     ri = moe_resolve_info()
     _check(load().moe_get_stats(ctx, ctypes.byref(ri)), "moe_get_stats")
     return ri.as_dict()
+
+
+def moe_combine_norm(ctx, y_pairs, w, y_shared, T, out, x_next, stream=None):
+    _check(load().moe_combine_norm(ctx, _ptr(y_pairs), _ptr(w), _ptr(y_shared), T, _ptr(out), _ptr(x_next),
+                                   _stream(stream)), "moe_combine_norm")
 
 
 def moe_chain_norm(ctx, out, T, x_next, stream=None):

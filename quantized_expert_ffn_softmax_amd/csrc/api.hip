@@ -372,3 +372,17 @@ extern "C" moe_status moe_chain_norm(moe_ctx *c, const float *out, int32_t T, fl
   if (e != hipSuccess) return moe_fail(MOE_ERR_HIP, std::string("moe_chain_norm: ") + hipGetErrorString(e));
   return MOE_OK;
 }
+
+extern "C" moe_status moe_combine_norm(moe_ctx *c, const float *y_pairs, const float *w, const float *y_shared,
+                                       int32_t T, float *out, float *x_next, void *stream) {
+  MOE_CHECK(c, MOE_ERR_INVALID, "moe_combine_norm: null ctx");
+  MOE_CHECK(T >= 1 && T <= c->cfg.max_tokens, MOE_ERR_INVALID, "moe_combine_norm: T must be 1..max_tokens");
+  MOE_CHECK(y_pairs && w && y_shared && out && x_next, MOE_ERR_INVALID, "moe_combine_norm: null pointer");
+  MOE_CHECK(aligned(y_pairs, 16) && aligned(y_shared, 16) && aligned(out, 16) && aligned(x_next, 16), MOE_ERR_ALIGN,
+            "moe_combine_norm: y_pairs, y_shared, out and x_next must be 16-byte aligned");
+  MOE_CHECK(out != x_next, MOE_ERR_INVALID, "moe_combine_norm: out and x_next must differ");
+  hipError_t e = moe::launch_combine_norm(y_pairs, w, y_shared, T, c->cfg.top_k, c->cfg.d_model, out, x_next,
+                                          as_stream(stream));
+  if (e != hipSuccess) return moe_fail(MOE_ERR_HIP, std::string("moe_combine_norm: ") + hipGetErrorString(e));
+  return MOE_OK;
+}

@@ -95,9 +95,86 @@ __global__ void __launch_bounds__(256) chain_norm_kernel(const float *__restrict
   }
 }
 
+// combine_kernel then chain_norm_kernel in one workgroup per token, with the
+// same arithmetic as the two: each thread combines the 8 float4 columns that
+// chain_norm_kernel gives it (ascending j by fma, the shared row added last,
+// as in combine_kernel), writes them to out, keeps them in registers and
+// normalises them with chain_norm_kernel's reductions -- so out and x_next
+// are bit for bit those of the two separate calls.
+__global__ void __launch_bounds__(256) combine_norm_kernel(const float *__restrict__ y_pairs,
+                                                           const float *__restrict__ w,
+                                                           const float *__restrict__ y_shared, int k, int d,
+                                                           float *__restrict__ out, float *__restrict__ x_next) {
+  __shared__ float part[4];
+  const int t = blockIdx.x, d4 = d / 4;
+  const float4 *yp = reinterpret_cast<const float4 *>(y_pairs + (size_t)t * k * d);
+  const float4 *ys = reinterpret_cast<const float4 *>(y_shared + (size_t)t * d);
+  float4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c >= d4) continue;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      float4 y[8];
+      float wj[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bool ok = j0 + j < k;
+        y[j] = ok ? yp[(size_t)(j0 + j) * d4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        wj[j] = ok ? w[(size_t)t * k + j0 + j] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        acc.x = fmaf(wj[j], y[j].x, acc.x);
+        acc.y = fmaf(wj[j], y[j].y, acc.y);
+        acc.z = fmaf(wj[j], y[j].z, acc.z);
+        acc.w = fmaf(wj[j], y[j].w, acc.w);
+      }
+    }
+    const float4 sh = ys[c];
+    acc.x += sh.x;
+    acc.y += sh.y;
+    acc.z += sh.z;
+    acc.w += sh.w;
+    reinterpret_cast<float4 *>(out + (size_t)t * d)[c] = acc;
+    v[i] = acc;
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+  const float mean = block_sum_256(s, part) / (float)d;
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (threadIdx.x + 256 * i < d4) {
+      v[i].x -= mean;
+      v[i].y -= mean;
+      v[i].z -= mean;
+      v[i].w -= mean;
+      ss = fmaf(v[i].x, v[i].x, fmaf(v[i].y, v[i].y, fmaf(v[i].z, v[i].z, fmaf(v[i].w, v[i].w, ss))));
+    }
+  }
+  const float inv = 1.0f / sqrtf(block_sum_256(ss, part) / (float)d + 1e-6f);
+  float4 *o = reinterpret_cast<float4 *>(x_next + (size_t)t * d);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    if (c < d4) o[c] = make_float4(v[i].x * inv, v[i].y * inv, v[i].z * inv, v[i].w * inv);
+  }
+}
+
 }  // namespace
 
 namespace moe {
+
+hipError_t launch_combine_norm(const float *y_pairs, const float *w, const float *y_shared, int T, int k, int d,
+                               float *out, float *x_next, hipStream_t s) {
+  hipLaunchKernelGGL(combine_norm_kernel, dim3(T), dim3(256), 0, s, y_pairs, w, y_shared, k, d, out, x_next);
+  return hipGetLastError();
+}
+
 
 hipError_t launch_combine(const float *y_pairs, const float *w, const float *y_shared, int T, int k, int d, float *out,
                           hipStream_t s) {

@@ -150,4 +150,6 @@ hipError_t launch_ffn_prefill(const moe_ctx *c, int layer, const float *x, int T
 hipError_t launch_combine(const float *y_pairs, const float *w, const float *y_shared, int T, int k, int d,
                           float *out, hipStream_t s);
 hipError_t launch_chain_norm(const float *out, int T, int d, float *x_next, hipStream_t s);
+hipError_t launch_combine_norm(const float *y_pairs, const float *w, const float *y_shared, int T, int k, int d,
+                               float *out, float *x_next, hipStream_t s);
 }  // namespace moe

@@ -160,3 +160,26 @@ def test_router_exact_ties(T):
     assert np.array_equal(buf["idx"].cpu().numpy(), want_idx)
     assert np.abs(buf["w"].cpu().numpy() - want_w).max() <= 1e-6
     ctx.close()
+
+
+@pytest.mark.parametrize("shape,T", [("tiny", 8), ("real", 1), ("real", 15), ("real", 64)])
+def test_combine_norm_equals_the_two_calls(shape, T):
+    dims = TINY if shape == "tiny" else REAL
+    from quantized_expert_ffn_softmax_amd.runtime import MoeContext
+    d, k = dims["d_model"], dims["top_k"]
+    ctx = MoeContext(d, dims["d_ff"], dims["n_experts"], k, 1, None, T)
+    g = torch.Generator().manual_seed(T)
+    yp = torch.randn((T * k, d), generator=g).cuda()
+    ys = torch.randn((T, d), generator=g).cuda()
+    w = torch.softmax(torch.randn((T, k), generator=g), dim=1).cuda()
+    out1, xn1 = torch.empty((T, d), device="cuda"), torch.empty((T, d), device="cuda")
+    out2, xn2 = torch.empty_like(out1), torch.empty_like(xn1)
+    B.moe_combine(ctx.ctx, yp, w, ys, T, out1)
+    B.moe_chain_norm(ctx.ctx, out1, T, xn1)
+    B.moe_combine_norm(ctx.ctx, yp, w, ys, T, out2, xn2)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2) and torch.equal(xn1, xn2)
+    ref = oracle.combine(yp.cpu().double().numpy(), w.cpu().double().numpy(), ys.cpu().double().numpy())
+    assert rel_err(out2.cpu().numpy(), ref) <= 1e-6
+    assert rel_err(xn2.cpu().numpy(), oracle.chain_norm(ref)) <= 1e-5
+    ctx.close()
