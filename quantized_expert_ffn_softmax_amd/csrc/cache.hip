@@ -49,6 +49,12 @@ __device__ uint64_t block_min_u64(uint64_t v, uint64_t *sh) {
   return r;
 }
 
+// counters are added without reading them back (no round trip before the
+// kernel can end); one thread of one workgroup adds, so the sums are exact
+__device__ inline void add_stat(int64_t *p, int64_t v) {
+  atomicAdd(reinterpret_cast<unsigned long long *>(p), static_cast<unsigned long long>(v));
+}
+
 // stats: [0] unique identities, [1] hits, [2] misses, [3] calls, [4] calls that
 // could not pin their working set, [5] the clock
 __global__ void __launch_bounds__(kThreads) resolve_kernel(const int32_t *__restrict__ idx, int n, int layer, int E,
@@ -64,7 +70,6 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(const int32_t *__rest
   __shared__ int nuniq_sh;
   __shared__ uint64_t shred[17];
   const int tid = threadIdx.x;
-  const uint32_t clock = (uint32_t)stats[5] + 1u;  // written back (by thread 0, last) only on success
   mark[tid] = 0;
   if (tid == 0) nuniq_sh = 0;
   __syncthreads();
@@ -86,12 +91,13 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(const int32_t *__rest
       dmiss[0] = nuniq_sh;
       dmiss[1] = 0;
       dmiss[2] = 0;
-      stats[0] += nuniq_sh;
-      stats[1] += nuniq_sh;
-      stats[3] += 1;
+      add_stat(stats + 0, nuniq_sh);
+      add_stat(stats + 1, nuniq_sh);
+      add_stat(stats + 3, 1);
     }
     return;
   }
+  const uint32_t clock = (uint32_t)stats[5] + 1u;  // written back (by thread 0, last) only on success
   // capped: unique identities, hits and the ascending list of misses
   const int is_u = (tid < E) && mark[tid];
   const int s_e = is_u ? slot_of[base + tid] : -1;
@@ -107,7 +113,7 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(const int32_t *__rest
       dmiss[0] = nuniq;
       dmiss[1] = 0;
       dmiss[2] = 1;
-      stats[4] += 1;
+      add_stat(stats + 4, 1);
     }
     return;
   }
@@ -138,7 +144,7 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(const int32_t *__rest
         dmiss[0] = nuniq;
         dmiss[1] = 0;
         dmiss[2] = 2;
-        stats[4] += 1;
+        add_stat(stats + 4, 1);
       }
       return;
     }
@@ -169,10 +175,10 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(const int32_t *__rest
     dmiss[0] = nuniq;
     dmiss[1] = nmiss;
     dmiss[2] = 0;
-    stats[0] += nuniq;
-    stats[1] += nuniq - nmiss;
-    stats[2] += nmiss;
-    stats[3] += 1;
+    add_stat(stats + 0, nuniq);
+    add_stat(stats + 1, nuniq - nmiss);
+    add_stat(stats + 2, nmiss);
+    add_stat(stats + 3, 1);
     stats[5] = clock;
   }
 }
