@@ -88,5 +88,7 @@ def test_null_context_calls(lib):
     assert lib.moe_get_stats(None, None) == B.MOE_ERR_INVALID
     assert lib.moe_cache_reset(None) == B.MOE_ERR_INVALID
     assert lib.moe_chain_norm(None, None, 1, None, None) == B.MOE_ERR_INVALID
+    assert lib.moe_cache_resolve_async(None, 0, None, 1, None, None) == B.MOE_ERR_INVALID
+    assert lib.moe_combine_norm(None, None, None, None, 1, None, None, None) == B.MOE_ERR_INVALID
     with pytest.raises(B.MoeError):
         B.moe_destroy(None)
