@@ -288,9 +288,12 @@ extern "C" moe_status moe_expert_ffn(moe_ctx *c, int32_t layer, const float *x, 
   MOE_CHECK(path == MOE_PATH_AUTO || path == MOE_PATH_DECODE || path == MOE_PATH_PREFILL, MOE_ERR_INVALID,
             "moe_expert_ffn: unknown path");
   const bool prefill_ok = c->cfg.d_model % 64 == 0 && c->cfg.d_ff % 64 == 0;
-  if (path == MOE_PATH_AUTO) path = (T <= 64 || !prefill_ok) ? MOE_PATH_DECODE : MOE_PATH_PREFILL;
+  const bool decode_ok = c->L.gate.nsb <= moe::kDecodeMaxNsb && c->L.down.nsb <= moe::kDecodeMaxNsb;
+  if (path == MOE_PATH_AUTO) path = ((T <= 64 && decode_ok) || !prefill_ok) ? MOE_PATH_DECODE : MOE_PATH_PREFILL;
   MOE_CHECK(path != MOE_PATH_PREFILL || prefill_ok, MOE_ERR_INVALID,
             "moe_expert_ffn: the prefill path needs d_model and d_ff to be multiples of 64");
+  MOE_CHECK(path != MOE_PATH_DECODE || decode_ok, MOE_ERR_INVALID,
+            "moe_expert_ffn: the decode path takes d_model and d_ff up to 2048 (13 superblocks of 160 columns)");
   hipStream_t s = as_stream(stream);
   hipError_t e = path == MOE_PATH_DECODE
                      ? moe::launch_ffn_decode(c, layer, x, T, idx, slot_of_pair, y_pairs, y_shared, s)

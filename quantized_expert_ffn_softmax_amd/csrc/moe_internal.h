@@ -70,8 +70,12 @@ inline int xrec_halves(int nsb) { return nsb * kSteps * 16; }
 
 // One unit of decode work: up to kEntryTokens tokens of one expert (or of the
 // shared expert) in one layer.  The decode kernels put a token's hi half in
-// MFMA column n and its lo half in column n + 8, hence 8.
-constexpr int kEntryTokens = 8;
+// MFMA column n and its lo half in column n + 4, and keep an entry's whole
+// activation record (4 columns) in LDS, hence 4.
+constexpr int kEntryTokens = 4;
+// Superblocks per row the decode kernels are built for: all of a unit's
+// word quads are requested at once, which bounds K (d_model, d_ff <= 2048).
+constexpr int kDecodeMaxNsb = 13;
 struct WorkEntry {
   int32_t expert;  // routed expert index, or -1 for the shared expert
   int32_t first;   // routed: index into perm of the first pair; shared: first token
