@@ -121,10 +121,18 @@ __global__ void __launch_bounds__(kBucketThreads) bucket_scan(int32_t *__restric
   const int e = threadIdx.x;
   int run = 0;
   if (e < E) {
-    for (int ch = 0; ch < nchunks; ++ch) {
-      const int v = chunk_cnt[(size_t)ch * E + e];
-      chunk_cnt[(size_t)ch * E + e] = run;
-      run += v;
+    // 32 chunk counts in flight per batch (one dependent read per chunk was
+    // bound by memory latency: 480 chunks took ~120 us)
+    constexpr int kBatch = 32;
+    for (int ch0 = 0; ch0 < nchunks; ch0 += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) v[i] = ch0 + i < nchunks ? chunk_cnt[(size_t)(ch0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        if (ch0 + i < nchunks) chunk_cnt[(size_t)(ch0 + i) * E + e] = run;
+        run += v[i];
+      }
     }
     cnt[e] = run;
   }

@@ -400,7 +400,7 @@ __device__ inline void unit_epilogue(const DecodeParams &P, const Unit &U, int w
 // two matrices in flight within the register budget of 3 waves per SIMD)
 template <int NSB, int NMAT>
 constexpr int words_depth() {
-  return NMAT == 2 ? (NSB < 9 ? NSB : 9) : NSB;
+  return NMAT == 2 ? (NSB < 4 ? NSB : 4) : NSB;
 }
 
 template <int NSB, int NMAT>
@@ -422,30 +422,58 @@ __device__ inline void load_first(std::integer_sequence<int, Ss...>, const WordS
 }
 
 template <int NSB, int NMAT, int S>
-__device__ inline void compute_superblock(uint4 (&W)[NSB][NMAT], const WordSrc<NSB, NMAT> &Src,
-                                          const uint8_t *(&srow)[NMAT], int g, int nblk, const uint32_t (&sel)[6],
-                                          const Consts &K, const uint8_t *xb, f4 &acc0, f4 &acc1) {
-  MatSb M[NMAT];
-#pragma unroll
-  for (int mat = 0; mat < NMAT; ++mat) M[mat] = mat_sb<S + 1 == NSB>(W[S][mat], srow[mat], 5 * S + g, nblk, sel);
+__device__ inline void refill(uint4 (&W)[NSB][NMAT], const WordSrc<NSB, NMAT> &Src) {
   constexpr int D = words_depth<NSB, NMAT>();
   if constexpr (S + D < NSB) {
     load_words<NSB, NMAT, S + D>(Src, W);
     asm volatile("" ::: "memory");  // keep the request here, a full D superblocks ahead of its use
   }
-  const uint8_t *xs = xb + S * moe::kSteps * 128;
-  sb_step<NMAT, 0>(M, K, xs, acc0, acc1);
-  sb_step<NMAT, 1>(M, K, xs, acc0, acc1);
-  sb_step<NMAT, 2>(M, K, xs, acc0, acc1);
-  sb_step<NMAT, 3>(M, K, xs, acc0, acc1);
-  sb_step<NMAT, 4>(M, K, xs, acc0, acc1);
 }
 
-template <int NSB, int NMAT, int... Ss>
-__device__ inline void compute_all(std::integer_sequence<int, Ss...>, uint4 (&W)[NSB][NMAT],
+// superblocks S and S + 1 together, their steps interleaved (twice the
+// independent dequantise-and-MFMA chains per wave); a last odd superblock
+// alone
+template <int NSB, int NMAT, int S>
+__device__ inline void compute_pair(uint4 (&W)[NSB][NMAT], const WordSrc<NSB, NMAT> &Src,
+                                    const uint8_t *(&srow)[NMAT], int g, int nblk, const uint32_t (&sel)[6],
+                                    const Consts &K, const uint8_t *xb, f4 &acc0, f4 &acc1, f4 &acc2, f4 &acc3) {
+  MatSb M[NMAT];
+#pragma unroll
+  for (int mat = 0; mat < NMAT; ++mat) M[mat] = mat_sb<S + 1 == NSB>(W[S][mat], srow[mat], 5 * S + g, nblk, sel);
+  refill<NSB, NMAT, S>(W, Src);
+  const uint8_t *xs = xb + S * moe::kSteps * 128;
+  if constexpr (S + 1 < NSB) {
+    MatSb M2[NMAT];
+#pragma unroll
+    for (int mat = 0; mat < NMAT; ++mat)
+      M2[mat] = mat_sb<S + 2 == NSB>(W[S + 1][mat], srow[mat], 5 * (S + 1) + g, nblk, sel);
+    refill<NSB, NMAT, S + 1>(W, Src);
+    const uint8_t *xs2 = xs + moe::kSteps * 128;
+    sb_step<NMAT, 0>(M, K, xs, acc0, acc1);
+    sb_step<NMAT, 0>(M2, K, xs2, acc2, acc3);
+    sb_step<NMAT, 1>(M, K, xs, acc0, acc1);
+    sb_step<NMAT, 1>(M2, K, xs2, acc2, acc3);
+    sb_step<NMAT, 2>(M, K, xs, acc0, acc1);
+    sb_step<NMAT, 2>(M2, K, xs2, acc2, acc3);
+    sb_step<NMAT, 3>(M, K, xs, acc0, acc1);
+    sb_step<NMAT, 3>(M2, K, xs2, acc2, acc3);
+    sb_step<NMAT, 4>(M, K, xs, acc0, acc1);
+    sb_step<NMAT, 4>(M2, K, xs2, acc2, acc3);
+  } else {
+    sb_step<NMAT, 0>(M, K, xs, acc0, acc1);
+    sb_step<NMAT, 1>(M, K, xs, acc0, acc1);
+    sb_step<NMAT, 2>(M, K, xs, acc0, acc1);
+    sb_step<NMAT, 3>(M, K, xs, acc0, acc1);
+    sb_step<NMAT, 4>(M, K, xs, acc0, acc1);
+  }
+}
+
+template <int NSB, int NMAT, int... Ps>
+__device__ inline void compute_all(std::integer_sequence<int, Ps...>, uint4 (&W)[NSB][NMAT],
                                    const WordSrc<NSB, NMAT> &Src, const uint8_t *(&srow)[NMAT], int g, int nblk,
-                                   const uint32_t (&sel)[6], const Consts &K, const uint8_t *xb, f4 &acc0, f4 &acc1) {
-  (compute_superblock<NSB, NMAT, Ss>(W, Src, srow, g, nblk, sel, K, xb, acc0, acc1), ...);
+                                   const uint32_t (&sel)[6], const Consts &K, const uint8_t *xb, f4 &acc0, f4 &acc1,
+                                   f4 &acc2, f4 &acc3) {
+  (compute_pair<NSB, NMAT, 2 * Ps>(W, Src, srow, g, nblk, sel, K, xb, acc0, acc1, acc2, acc3), ...);
 }
 
 template <int NSB, int NMAT>
@@ -506,8 +534,11 @@ __global__ void __launch_bounds__(64 * kWaves, NMAT == 2 ? 3 : 4) ffn_decode_ker
     const uint8_t *srow[NMAT];
 #pragma unroll
     for (int mat = 0; mat < NMAT; ++mat) srow[mat] = lsc + mat * 64 * 5 * NSB * 2 + (w * 16 + r16) * nblk * 2;
-    f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    compute_all<NSB, NMAT>(std::make_integer_sequence<int, NSB>{}, W, Src, srow, g, nblk, sel, K, xb, acc0, acc1);
+    f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f}, acc2 = acc0, acc3 = acc0;
+    compute_all<NSB, NMAT>(std::make_integer_sequence<int, (NSB + 1) / 2>{}, W, Src, srow, g, nblk, sel, K, xb, acc0,
+                           acc1, acc2, acc3);
+    acc0 += acc2;
+    acc1 += acc3;
     unit_epilogue<NMAT>(P, U, w, lane, acc0, acc1);
   }
 }
