@@ -66,6 +66,27 @@ def test_tiny_decode_past_the_small_bucketing():
     layer.close()
 
 
+@pytest.mark.parametrize("d_model,d_ff", [(64, 64), (1024, 512), (640, 2048)])
+def test_decode_other_widths(d_model, d_ff):
+    # the decode kernels are built per superblock count (160 columns each):
+    # 1/1, 7/4 and 4/13 superblocks for gate-up/down, with the last scale
+    # block of a row at the clamp and a wide down matrix
+    layer = _layer(T=9, d_model=d_model, d_ff=d_ff, n_experts=16, top_k=3)
+    _check_layer(layer, B.MOE_PATH_DECODE, "fp16_weights", 1e-4)
+    layer.close()
+
+
+def test_decode_width_limit():
+    # d_model = 2112 is 14 superblocks: the decode path refuses it, the
+    # automatic choice takes the prefill path (still checked at the bar)
+    layer = _layer(T=6, d_model=2112, d_ff=128, n_experts=16, top_k=2)
+    with pytest.raises(B.MoeError) as ei:
+        layer.forward_gpu(B.MOE_PATH_DECODE)
+    assert ei.value.status == B.MOE_ERR_INVALID
+    _check_layer(layer, B.MOE_PATH_AUTO, "fp16_operands", TOL)
+    layer.close()
+
+
 @pytest.mark.parametrize("T", [1, 8, 65, 130])
 def test_tiny_prefill(T):
     layer = _layer(T=T, **TINY)
