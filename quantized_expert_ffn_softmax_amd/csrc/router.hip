@@ -10,51 +10,119 @@ namespace {
 
 constexpr int kWave = 64;
 
-// --- logits, many tokens: LDS-tiled fp32 GEMM, 64x64 output tile, each thread 4x4.
-constexpr int kTm = 64, kTn = 64, kTk = 16;
+// --- logits, many tokens: fp32 MFMA GEMM (v_mfma_f32_16x16x4_f32).  A
+// workgroup computes 128 experts x 128 tokens; wave (we, wt) of its 2 x 2
+// waves takes experts 64 we .. and tokens 64 wt .. as 4 x 4 blocks of 16 x 16.
+// K runs in stages of 32 columns through LDS, double-buffered.  In LDS a row
+// of a stage is stored as [k % 4][k / 4] (36-float pitch), so the 8 values
+// lane (m, g) feeds to the 8 MFMA steps of a stage (k = 4 s + g, s = 0..7)
+// are 8 consecutive floats: two 16-byte reads per row block.
+// MFMA operands: A = W[expert 16 b + m][k], B = x[token 16 c + m][k]; D:
+// lane (m, g) holds experts 16 b + 4 g + i, token 16 c + m.
+constexpr int kGm = 128, kGk = 32, kGp = 36;  // tile (both sides), K stage, LDS row pitch in floats
+
+typedef float f4g __attribute__((ext_vector_type(4)));
+
+// one stage of 128 rows x 32 columns of src (row stride d): loaded into
+// registers (4 float4 per thread), then stored to LDS in [row][k%4][k/4]
+// order once the current stage's MFMAs have been issued
+constexpr int kGv = kGm * kGk / 4 / 256;
+
+__device__ inline void stage_load(const float *__restrict__ src, int rows, int r0, int d, int k0, int tid,
+                                  float4 (&v)[kGv]) {
+#pragma unroll
+  for (int i = 0; i < kGv; ++i) {
+    const int q = tid + 256 * i;  // float4 index: row q / 8, columns 4 (q % 8) ..
+    const int gr = r0 + (q >> 3);
+    v[i] = gr < rows ? *reinterpret_cast<const float4 *>(src + (size_t)gr * d + k0 + 4 * (q & 7))
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+__device__ inline void stage_store(const float4 (&v)[kGv], int tid, float *__restrict__ lds) {
+#pragma unroll
+  for (int i = 0; i < kGv; ++i) {
+    const int q = tid + 256 * i;
+    float *o = lds + (q >> 3) * kGp + (q & 7);
+    o[0] = v[i].x;
+    o[8] = v[i].y;
+    o[16] = v[i].z;
+    o[24] = v[i].w;
+  }
+}
 
 __global__ void __launch_bounds__(256) router_logits_gemm(const float *__restrict__ x, int T, int d,
                                                           const float *__restrict__ wr,
                                                           const float *__restrict__ bias, int E,
                                                           float *__restrict__ logits) {
-  __shared__ float xs[kTk][kTm + 4];
-  __shared__ float ws[kTk][kTn + 4];
-  const int tid = threadIdx.x;
-  const int m0 = blockIdx.y * kTm, n0 = blockIdx.x * kTn;
-  const int tm = (tid / 16) * 4, tn = (tid % 16) * 4;
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < d; k0 += kTk) {
-    // 64 rows x 16 cols of x and of W: 1024 floats each, 4 per thread
-    for (int i = tid; i < kTm * kTk / 4; i += 256) {
-      const int r = i / (kTk / 4), cc = (i % (kTk / 4)) * 4;
-      const int gm = m0 + r, gn = n0 + r;
-      float4 xv = gm < T ? *reinterpret_cast<const float4 *>(x + (size_t)gm * d + k0 + cc) : make_float4(0, 0, 0, 0);
-      float4 wv = gn < E ? *reinterpret_cast<const float4 *>(wr + (size_t)gn * d + k0 + cc) : make_float4(0, 0, 0, 0);
-      xs[cc + 0][r] = xv.x; xs[cc + 1][r] = xv.y; xs[cc + 2][r] = xv.z; xs[cc + 3][r] = xv.w;
-      ws[cc + 0][r] = wv.x; ws[cc + 1][r] = wv.y; ws[cc + 2][r] = wv.z; ws[cc + 3][r] = wv.w;
+  __shared__ __attribute__((aligned(16))) float lw[2][kGm * kGp];
+  __shared__ __attribute__((aligned(16))) float lx[2][kGm * kGp];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = lane & 15, g = lane >> 4;
+  const int we = wave >> 1, wt = wave & 1;
+  const int e0 = blockIdx.x * kGm, t0 = blockIdx.y * kGm;
+  f4g acc[4][4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[b][c] = (f4g){0.f, 0.f, 0.f, 0.f};
+  const int nst = d / kGk;
+  float4 vw[kGv], vx[kGv];
+  stage_load(wr, E, e0, d, 0, tid, vw);
+  stage_load(x, T, t0, d, 0, tid, vx);
+  stage_store(vw, tid, lw[0]);
+  stage_store(vx, tid, lx[0]);
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int cur = st & 1;
+    const bool more = st + 1 < nst;
+    if (more) {
+      stage_load(wr, E, e0, d, (st + 1) * kGk, tid, vw);
+      stage_load(x, T, t0, d, (st + 1) * kGk, tid, vx);
     }
-    __syncthreads();
+    float4 av[4][2], bv[4][2];
 #pragma unroll
-    for (int kk = 0; kk < kTk; ++kk) {
-      float a[4], b[4];
+    for (int b = 0; b < 4; ++b) {
+      const float *pa = lw[cur] + (64 * we + 16 * b + m) * kGp + 8 * g;
+      const float *pb = lx[cur] + (64 * wt + 16 * b + m) * kGp + 8 * g;
+      av[b][0] = *reinterpret_cast<const float4 *>(pa);
+      av[b][1] = *reinterpret_cast<const float4 *>(pa + 4);
+      bv[b][0] = *reinterpret_cast<const float4 *>(pb);
+      bv[b][1] = *reinterpret_cast<const float4 *>(pb + 4);
+    }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { a[i] = xs[kk][tm + i]; b[i] = ws[kk][tn + i]; }
+    for (int s8 = 0; s8 < 8; ++s8) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int b = 0; b < 4; ++b) {
+        const float4 &A = av[b][s8 >> 2];
+        const float a = (s8 & 3) == 0 ? A.x : (s8 & 3) == 1 ? A.y : (s8 & 3) == 2 ? A.z : A.w;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+        for (int c = 0; c < 4; ++c) {
+          const float4 &Bq = bv[c][s8 >> 2];
+          const float bb = (s8 & 3) == 0 ? Bq.x : (s8 & 3) == 1 ? Bq.y : (s8 & 3) == 2 ? Bq.z : Bq.w;
+          acc[b][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, acc[b][c], 0, 0, 0);
+        }
+      }
+    }
+    if (more) {
+      // the other buffer was last read in stage st - 1, before the barrier that ended it
+      stage_store(vw, tid, lw[cur ^ 1]);
+      stage_store(vx, tid, lx[cur ^ 1]);
     }
     __syncthreads();
   }
+  // D: lane (m, g) of block (b, c) holds experts e0 + 64 we + 16 b + 4 g + i, token t0 + 64 wt + 16 c + m
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int gm = m0 + tm + i;
-    if (gm >= T) continue;
+  for (int c = 0; c < 4; ++c) {
+    const int t = t0 + 64 * wt + 16 * c + m;
+    if (t >= T) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int gn = n0 + tn + j;
-      if (gn < E) logits[(size_t)gm * E + gn] = acc[i][j] + (bias ? bias[gn] : 0.f);
-    }
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = e0 + 64 * we + 16 * b + 4 * g + i;
+        if (e < E) logits[(size_t)t * E + e] = acc[b][c][i] + (bias ? bias[e] : 0.f);
+      }
   }
 }
 
@@ -250,7 +318,7 @@ hipError_t launch_router(const moe_ctx *c, const float *x, int T, const float *w
                        k, logits, idx, w);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(router_logits_gemm, dim3((E + kTn - 1) / kTn, (T + kTm - 1) / kTm), dim3(256), 0, s, x, T, d, wr,
+  hipLaunchKernelGGL(router_logits_gemm, dim3((E + kGm - 1) / kGm, (T + kGm - 1) / kGm), dim3(256), 0, s, x, T, d, wr,
                      bias, E, logits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
