@@ -171,11 +171,13 @@ hipError_t launch_bucket_ex(const moe_ctx *c, const int32_t *idx, int T, int32_t
                             int entry_m, const float *x, uint16_t *xrec, int xrec_h, hipStream_t s) {
   const int E = c->cfg.n_experts, n = T * c->cfg.top_k;
   if (n <= kSmallMax) {
-    // with x: 1 + enough workgroups to build its record, ~8 values per thread
+    // with x: 1 + enough workgroups to build its record, one value per
+    // thread (so all its loads are in flight at once: at 8 per thread the
+    // record took ~6 us of dependent loads)
     int blocks = 1;
     if (x) {
       const int vals = T * c->L.gate.nsb * moe::kSteps * 8;
-      blocks += (vals + 8 * kBucketThreads - 1) / (8 * kBucketThreads);
+      blocks += (vals + kBucketThreads - 1) / kBucketThreads;
     }
     hipLaunchKernelGGL(bucket_small, dim3(blocks), dim3(kBucketThreads), 0, s, idx, n, E, T, offsets, perm,
                        build ? 1 : 0, entry_m, c->work, c->n_work, x, c->cfg.d_model, c->L.gate.nsb, xrec, xrec_h);

@@ -16,14 +16,18 @@ __device__ inline int block_excl_scan_1024(int v, int *total, int *sh /* >= 17 i
   }
   if (lane == 63) sh[wave] = incl;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int w = 0; w < 16; ++w) {
-      const int t = sh[w];
-      sh[w] = run;
-      run += t;
+  if (wave == 0) {
+    // the 16 wave sums scanned by the first 16 lanes of wave 0 (shuffles,
+    // not a serial chain of LDS reads)
+    const int t = lane < 16 ? sh[lane] : 0;
+    int run = t;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const int o = __shfl_up(run, off, 64);
+      if (lane >= off) run += o;
     }
-    sh[16] = run;
+    if (lane < 16) sh[lane] = run - t;
+    if (lane == 15) sh[16] = run;
   }
   __syncthreads();
   const int res = sh[wave] + incl - v;
