@@ -10,23 +10,26 @@ namespace {
 
 constexpr int kWave = 64;
 
-// --- logits, many tokens: fp32 MFMA GEMM (v_mfma_f32_16x16x4_f32).  A
-// workgroup computes 128 experts x 128 tokens; wave (we, wt) of its 2 x 2
+// --- logits, many tokens: fp16 MFMA on split operands.  Each fp32 operand
+// v is carried as hi = fp16(v) and lo = fp16(v - hi) (v = hi + lo to ~2^-22
+// relative), and a 32-column K step of a 16 x 16 block takes three
+// v_mfma_f32_16x16x32_f16: W_hi x_hi + W_hi x_lo + W_lo x_hi (the dropped
+// W_lo x_lo is ~2^-22 of a product), every product exact in the fp32
+// accumulation.  fp16 MFMA runs 16x the fp32 MFMA rate on this part.
+// A workgroup computes 128 experts x 128 tokens; wave (we, wt) of its 2 x 2
 // waves takes experts 64 we .. and tokens 64 wt .. as 4 x 4 blocks of 16 x 16.
-// K runs in stages of 32 columns through LDS, double-buffered.  In LDS a row
-// of a stage is stored as [k % 4][k / 4] (36-float pitch), so the 8 values
-// lane (m, g) feeds to the 8 MFMA steps of a stage (k = 4 s + g, s = 0..7)
-// are 8 consecutive floats: two 16-byte reads per row block.
-// MFMA operands: A = W[expert 16 b + m][k], B = x[token 16 c + m][k]; D:
-// lane (m, g) holds experts 16 b + 4 g + i, token 16 c + m.
-constexpr int kGm = 128, kGk = 32, kGp = 36;  // tile (both sides), K stage, LDS row pitch in floats
+// K runs in stages of 32 columns through LDS (double-buffered; the next
+// stage is loaded into registers during the MFMAs).  An LDS row of a stage
+// holds 32 hi halves then 32 lo halves (144-byte pitch).
+// MFMA operands: A = W[expert 16 b + m][k], B = x[token 16 c + m][k], lane
+// (m, g) supplying k = 8 g .. 8 g + 7; D: lane (m, g) holds experts
+// 16 b + 4 g + i, token 16 c + m.
+constexpr int kGm = 128, kGk = 32, kGpb = 144;  // tile (both sides), K stage, LDS row pitch in bytes
+constexpr int kGv = kGm * kGk / 4 / 256;        // float4 loads per thread per matrix and stage
 
 typedef float f4g __attribute__((ext_vector_type(4)));
-
-// one stage of 128 rows x 32 columns of src (row stride d): loaded into
-// registers (4 float4 per thread), then stored to LDS in [row][k%4][k/4]
-// order once the current stage's MFMAs have been issued
-constexpr int kGv = kGm * kGk / 4 / 256;
+typedef _Float16 h8g __attribute__((ext_vector_type(8)));
+typedef _Float16 h4g __attribute__((ext_vector_type(4)));
 
 __device__ inline void stage_load(const float *__restrict__ src, int rows, int r0, int d, int k0, int tid,
                                   float4 (&v)[kGv]) {
@@ -39,15 +42,20 @@ __device__ inline void stage_load(const float *__restrict__ src, int rows, int r
   }
 }
 
-__device__ inline void stage_store(const float4 (&v)[kGv], int tid, float *__restrict__ lds) {
+__device__ inline void stage_store(const float4 (&v)[kGv], int tid, uint8_t *__restrict__ lds) {
 #pragma unroll
   for (int i = 0; i < kGv; ++i) {
     const int q = tid + 256 * i;
-    float *o = lds + (q >> 3) * kGp + (q & 7);
-    o[0] = v[i].x;
-    o[8] = v[i].y;
-    o[16] = v[i].z;
-    o[24] = v[i].w;
+    const float f[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    h4g hi, lo;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      hi[j] = (_Float16)f[j];
+      lo[j] = (_Float16)(f[j] - (float)hi[j]);
+    }
+    uint8_t *o = lds + (q >> 3) * kGpb + 8 * (q & 7);
+    *reinterpret_cast<h4g *>(o) = hi;
+    *reinterpret_cast<h4g *>(o + 64) = lo;
   }
 }
 
@@ -55,8 +63,8 @@ __global__ void __launch_bounds__(256) router_logits_gemm(const float *__restric
                                                           const float *__restrict__ wr,
                                                           const float *__restrict__ bias, int E,
                                                           float *__restrict__ logits) {
-  __shared__ __attribute__((aligned(16))) float lw[2][kGm * kGp];
-  __shared__ __attribute__((aligned(16))) float lx[2][kGm * kGp];
+  __shared__ __attribute__((aligned(16))) uint8_t lw[2][kGm * kGpb];
+  __shared__ __attribute__((aligned(16))) uint8_t lx[2][kGm * kGpb];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 15, g = lane >> 4;
   const int we = wave >> 1, wt = wave & 1;
@@ -80,30 +88,24 @@ __global__ void __launch_bounds__(256) router_logits_gemm(const float *__restric
       stage_load(wr, E, e0, d, (st + 1) * kGk, tid, vw);
       stage_load(x, T, t0, d, (st + 1) * kGk, tid, vx);
     }
-    float4 av[4][2], bv[4][2];
+    h8g ah[4], al[4], bh[4], bl[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const float *pa = lw[cur] + (64 * we + 16 * b + m) * kGp + 8 * g;
-      const float *pb = lx[cur] + (64 * wt + 16 * b + m) * kGp + 8 * g;
-      av[b][0] = *reinterpret_cast<const float4 *>(pa);
-      av[b][1] = *reinterpret_cast<const float4 *>(pa + 4);
-      bv[b][0] = *reinterpret_cast<const float4 *>(pb);
-      bv[b][1] = *reinterpret_cast<const float4 *>(pb + 4);
+      const uint8_t *pa = lw[cur] + (64 * we + 16 * b + m) * kGpb + 16 * g;
+      const uint8_t *pb = lx[cur] + (64 * wt + 16 * b + m) * kGpb + 16 * g;
+      ah[b] = *reinterpret_cast<const h8g *>(pa);
+      al[b] = *reinterpret_cast<const h8g *>(pa + 64);
+      bh[b] = *reinterpret_cast<const h8g *>(pb);
+      bl[b] = *reinterpret_cast<const h8g *>(pb + 64);
     }
 #pragma unroll
-    for (int s8 = 0; s8 < 8; ++s8) {
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const float4 &A = av[b][s8 >> 2];
-        const float a = (s8 & 3) == 0 ? A.x : (s8 & 3) == 1 ? A.y : (s8 & 3) == 2 ? A.z : A.w;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const float4 &Bq = bv[c][s8 >> 2];
-          const float bb = (s8 & 3) == 0 ? Bq.x : (s8 & 3) == 1 ? Bq.y : (s8 & 3) == 2 ? Bq.z : Bq.w;
-          acc[b][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, acc[b][c], 0, 0, 0);
-        }
+      for (int c = 0; c < 4; ++c) {
+        acc[b][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[b], bh[c], acc[b][c], 0, 0, 0);
+        acc[b][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[b], bl[c], acc[b][c], 0, 0, 0);
+        acc[b][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[b], bh[c], acc[b][c], 0, 0, 0);
       }
-    }
     if (more) {
       // the other buffer was last read in stage st - 1, before the barrier that ended it
       stage_store(vw, tid, lw[cur ^ 1]);
