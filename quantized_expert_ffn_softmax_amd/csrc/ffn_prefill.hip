@@ -9,7 +9,7 @@
 // Operands are fp16, as the reading for this path fixes: x, the dequantised
 // weights fp16((q - 4) * s) and h = silu(g) * u are each rounded to fp16
 // once; products and sums are fp32 (v_mfma_f32_16x16x32_f16).
-// Work: tiles of (up to 128 tokens of one expert) x (64 weight rows); K runs
+// Work: tiles of (up to 128 tokens of one expert) x (128 weight rows); K runs
 // in steps of 80 slots, dequantised into LDS.
 #include <algorithm>
 
@@ -23,8 +23,12 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
-// Tiles: 128 tokens of one expert x 64 weight rows (gate/up: 32 rows of each
-// matrix, so one tile yields h for 32 rows; down: 64 rows).  K runs in steps
+// Tiles: 128 tokens of one expert x 128 weight rows (gate/up: 64 rows of each
+// matrix, so one tile yields h for 64 rows; down: 128 rows, the last tile of a
+// d_model that is an odd multiple of 64 half used).  Every token's activations
+// are read once per row tile, so the row tile sets how often they are read:
+// 128 rows read them 12 (gate/up) and 16 (down) times per chunk instead of 24
+// and 32 with 64-row tiles.  K runs in steps
 // of 80 slots -- half a 160-column superblock, 8 packed words -- in "pair
 // order": inside each superblock, slot 2p + e holds column c_p + 5 e with
 // c_p = 10 (p / 5) + p % 5, i.e. the two codes that share the two halves of a
@@ -32,17 +36,16 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 // that order (zero at slots past the last column), so one v_and_or_b32 +
 // v_pk_add + v_pk_mul dequantises two adjacent K slots in place, and any K
 // order is the same contraction.
-// Per step every thread copies 80 bytes of activations and dequantises two
+// Per step every thread copies 80 bytes of activations and dequantises four
 // words of one weight row into LDS; the next step's global loads are in flight
 // while the MFMAs of this one run.  The LDS tile is single-buffered (two
-// barriers per step): at 35 KB a CU holds four workgroups instead of the two
-// that a double buffer allows, and the extra waves hide more of each step's
-// latency (3.8 -> 3.3 ms per 12,288-token chunk).
+// barriers per step): at 46 KB a CU holds three workgroups.
 // MFMA: v_mfma_f32_16x16x32_f16 twice and v_mfma_f32_16x16x16_f16 once per
-// 16 x 16 output tile per step; D[token][row].
+// 16 x 16 output tile per step; each wave owns 64 tokens x 64 rows (4 x 4
+// tiles); D[token][row].
 // ---------------------------------------------------------------------------
 constexpr int kPM = 128;       // tokens per tile (work entries hold <= kPM tokens)
-constexpr int kPN = 64;        // weight rows per tile
+constexpr int kPN = 128;       // weight rows per tile
 constexpr int kPK = 80;        // K slots per step
 constexpr int kPld = kPK + 8;  // LDS pitch in halves: rows 176 B apart, 8 consecutive rows on 8 bank groups
 
@@ -104,24 +107,26 @@ __host__ __device__ inline int slot_col(int s) {
 __device__ inline f4 mfma32(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 __device__ inline f4 mfma16(h4 a, h4 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0); }
 
-// Weight part of one thread: B row brow = tid / 4, words 2u, 2u+1 (u = tid %
-// 4) of each 8-word step, so the 4 lanes of a row read its 32 bytes together.
+// Weight part of one thread: B row brow, words 4u .. 4u+3 of each 8-word step
+// (u is the same for a whole wave, so the pair selectors below are uniform).
 struct WSrc {
   const uint8_t *codes;   // the row's words
   const uint8_t *scales;  // the row's scales
   int nblk;
 };
 
-// raw loads of step s for this thread: 2 words and the 2 scale blocks they touch
+// raw loads of step s for this thread: 4 words (40 columns starting at
+// 80 hh + 40 u of the superblock, always inside 2 scale blocks) and those 2
+// scale blocks
 struct WRaw {
-  uint2 w;
+  uint4 w;
   uint32_t s0, s1;
 };
 
 __device__ inline void load_w(const WSrc &W, int s, int u, WRaw &r) {
   const int S = s >> 1, hh = s & 1;
-  r.w = *reinterpret_cast<const uint2 *>(W.codes + (size_t)(S * 16 + 8 * hh + 2 * u) * 4);
-  const int b0 = 5 * S + (80 * hh + 20 * u) / 32;
+  r.w = *reinterpret_cast<const uint4 *>(W.codes + (size_t)(S * 16 + 8 * hh + 4 * u) * 4);
+  const int b0 = 5 * S + (80 * hh + 40 * u) / 32;
   r.s0 = *reinterpret_cast<const uint16_t *>(W.scales + (size_t)min(b0, W.nblk - 1) * 2);
   r.s1 = *reinterpret_cast<const uint16_t *>(W.scales + (size_t)min(b0 + 1, W.nblk - 1) * 2);
 }
@@ -136,14 +141,14 @@ struct PConsts {
 // superblock-relative column of the thread's first code, column c0 + lc uses
 // the second block when lc >= 32 (c0 / 32 + 1) - c0.
 struct PairSel {
-  uint32_t sel[10];
+  uint32_t sel[20];
 };
 
 __device__ inline void make_sel(int hh, int u, PairSel &P) {
-  const int c0 = 80 * hh + 20 * u;
+  const int c0 = 80 * hh + 40 * u;
   const int thr = (c0 / 32 + 1) * 32 - c0;
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int j = 0; j < 5; ++j) {
       const int lc = 10 * a + j;
@@ -153,16 +158,16 @@ __device__ inline void make_sel(int hh, int u, PairSel &P) {
     }
 }
 
-// Dequantise the thread's 10 code pairs into 20 consecutive K slots (40 B).
+// Dequantise the thread's 20 code pairs into 40 consecutive K slots (80 B).
 // Per pair: one v_and_or_b32 (fp16 1024 + f q), one v_pk_add (- (1024 + 4 f),
 // exact), one v_pk_mul by 1/f (exact), one v_perm_b32 (the pair's scales),
 // one v_pk_mul by them (one rounding: fp16((q - 4) s), the oracle's fp16
 // reading).
 __device__ inline void deq_w(const WRaw &r, const PairSel &P, const PConsts &K, _Float16 *dst) {
-  h2 out[10];
+  h2 out[20];
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    const uint32_t word = a ? r.w.y : r.w.x;
+  for (int a = 0; a < 4; ++a) {
+    const uint32_t word = a == 0 ? r.w.x : a == 1 ? r.w.y : a == 2 ? r.w.z : r.w.w;
 #pragma unroll
     for (int j = 0; j < 5; ++j) {
       const int jj = j % 3;
@@ -177,8 +182,9 @@ __device__ inline void deq_w(const WRaw &r, const PairSel &P, const PConsts &K, 
   }
 #pragma unroll
   for (int i = 0; i < 5; ++i) {
-    const uint2 pk = make_uint2(__builtin_bit_cast(uint32_t, out[2 * i]), __builtin_bit_cast(uint32_t, out[2 * i + 1]));
-    *reinterpret_cast<uint2 *>(dst + 4 * i) = pk;
+    const uint4 pk = make_uint4(__builtin_bit_cast(uint32_t, out[4 * i]), __builtin_bit_cast(uint32_t, out[4 * i + 1]),
+                                __builtin_bit_cast(uint32_t, out[4 * i + 2]), __builtin_bit_cast(uint32_t, out[4 * i + 3]));
+    *reinterpret_cast<uint4 *>(dst + 8 * i) = pk;
   }
 }
 
@@ -189,8 +195,8 @@ template <int B, int NBUF>
 __device__ inline void prefill_step(int s, int nsteps, bool xact, uint4 &xv0, uint4 &xv1, uint4 &xv2, uint4 &xv3,
                                     uint4 &xv4, _Float16 *xdst, WRaw &wr, const PairSel &sel, const PConsts &K,
                                     _Float16 *wdst, const WSrc &W, int u, const _Float16 *xsrc, int xh,
-                                    const _Float16 (*wsb)[kPld], const _Float16 (*xsb)[kPld], int bro0, int bro1,
-                                    int r16, int g, int wm, int mt_active, f4 (&acc)[4][2]) {
+                                    const _Float16 (*wsb)[kPld], const _Float16 (*xsb)[kPld], const int (&bro)[4],
+                                    int r16, int g, int wm, int mt_active, f4 (&acc)[4][4]) {
   if constexpr (NBUF == 1) __syncthreads();  // every wave has read the previous step
   if (xact) {
     uint4 *dst = reinterpret_cast<uint4 *>(xdst);
@@ -213,11 +219,11 @@ __device__ inline void prefill_step(int s, int nsteps, bool xact, uint4 &xv0, ui
     load_w(W, s + 1, u, wr);
   }
   __syncthreads();
-  h8 b32[2][2];
-  h4 b16[2];
+  h8 b32[4][2];
+  h4 b16[4];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const _Float16 *wrow = wsb[(nb ? bro1 : bro0) + r16];
+  for (int nb = 0; nb < 4; ++nb) {
+    const _Float16 *wrow = wsb[bro[nb] + r16];
     b32[nb][0] = *reinterpret_cast<const h8 *>(wrow + 8 * g);
     b32[nb][1] = *reinterpret_cast<const h8 *>(wrow + 32 + 8 * g);
     b16[nb] = *reinterpret_cast<const h4 *>(wrow + 64 + 4 * g);
@@ -230,7 +236,7 @@ __device__ inline void prefill_step(int s, int nsteps, bool xact, uint4 &xv0, ui
       const h8 a1 = *reinterpret_cast<const h8 *>(xrow + 32 + 8 * g);
       const h4 a2 = *reinterpret_cast<const h4 *>(xrow + 64 + 4 * g);
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+      for (int nb = 0; nb < 4; ++nb) {
         acc[mt][nb] = mfma32(a0, b32[nb][0], acc[mt][nb]);
         acc[mt][nb] = mfma32(a1, b32[nb][1], acc[mt][nb]);
         acc[mt][nb] = mfma16(a2, b16[nb], acc[mt][nb]);
@@ -241,13 +247,13 @@ __device__ inline void prefill_step(int s, int nsteps, bool xact, uint4 &xv0, ui
 
 constexpr int kNBuf = 1;  // LDS buffers of the K loop (2: double-buffered, one barrier per step)
 template <int NMAT>
-__global__ void __launch_bounds__(256, kNBuf == 1 ? 4 : 2) prefill_kernel(PrefillParams P) {
+__global__ void __launch_bounds__(256, kNBuf == 1 ? 3 : 2) prefill_kernel(PrefillParams P) {
   __shared__ __attribute__((aligned(16))) _Float16 xs[kNBuf][kPM][kPld];
   __shared__ __attribute__((aligned(16))) _Float16 ws[kNBuf][kPN][kPld];
   __shared__ int row_sh[kPM], tok_sh[kPM];
   const int rows_out = NMAT == 2 ? P.d_ff : P.d_model;
   const int tile_rows = NMAT == 2 ? kPN / 2 : kPN;  // output rows per tile
-  const int ntile = rows_out / tile_rows;
+  const int ntile = (rows_out + tile_rows - 1) / tile_rows;
   const int item = blockIdx.x;
   if (item >= min(P.n_work[0], P.max_work) * ntile) return;
   const moe::WorkEntry we = P.work[item / ntile];
@@ -271,12 +277,13 @@ __global__ void __launch_bounds__(256, kNBuf == 1 ? 4 : 2) prefill_kernel(Prefil
   const bool xact = xr < m && row_sh[xr] >= 0;
   const _Float16 *xsrc = nullptr;
   if (xact) xsrc = NMAT == 2 ? P.x16 + (size_t)tok_sh[xr] * kp : P.h16 + (size_t)row_sh[xr] * kp;
-  // weight role: B row brow, word pair u
-  const int brow = tid >> 2, u = tid & 3;
+  // weight role: B row brow, word quad u (one u per wave; readfirstlane makes
+  // that visible, so the pair selectors live in scalar registers)
+  const int brow = lane + 64 * (wave >> 1), u = __builtin_amdgcn_readfirstlane(wave & 1);
   WSrc W;
   {
     const moe::MatLayout &M = NMAT == 2 ? (brow < kPN / 2 ? P.gate : P.up) : P.down;
-    const int wrow = NMAT == 2 ? nt * (kPN / 2) + (brow & (kPN / 2 - 1)) : nt * kPN + brow;
+    const int wrow = NMAT == 2 ? nt * (kPN / 2) + (brow & (kPN / 2 - 1)) : min(nt * kPN + brow, rows_out - 1);
     W.codes = blob + M.code_off + (size_t)wrow * M.wpr * 4;
     W.scales = blob + M.scale_off + (size_t)wrow * M.nblk * 2;
     W.nblk = M.nblk;
@@ -294,13 +301,17 @@ __global__ void __launch_bounds__(256, kNBuf == 1 ? 4 : 2) prefill_kernel(Prefil
   WRaw wr;
   const int wm = wave & 1, wn = wave >> 1;
   // output tiles of this wave: M tiles mt (16 tokens each), N tiles nb
-  f4 acc[4][2];
+  f4 acc[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = (f4){0.f, 0.f, 0.f, 0.f};
-  // B rows of N tile nb: gate/up -> 16 wn (+32 for up); down -> 32 wn + 16 nb
-  const int bro0 = NMAT == 2 ? 16 * wn : 32 * wn, bro1 = NMAT == 2 ? kPN / 2 + 16 * wn : 32 * wn + 16;
+    for (int b = 0; b < 4; ++b) acc[a][b] = (f4){0.f, 0.f, 0.f, 0.f};
+  // B rows of N tile nb: gate/up -> gate rows 32 wn + 16 nb (nb < 2), up rows
+  // 64 + 32 wn + 16 (nb - 2); down -> 64 wn + 16 nb
+  int bro[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+    bro[nb] = NMAT == 2 ? (nb < 2 ? 32 * wn + 16 * nb : kPN / 2 + 32 * wn + 16 * (nb - 2)) : 64 * wn + 16 * nb;
   const int r16 = lane & 15, g = lane >> 4;
   const int mt_active = min(4, max(0, (m - 64 * wm + 15) / 16));  // M tiles holding tokens
   if (xact) {
@@ -316,10 +327,9 @@ __global__ void __launch_bounds__(256, kNBuf == 1 ? 4 : 2) prefill_kernel(Prefil
   for (int s = 0; s < nsteps; s += 2) {
     constexpr int b1 = kNBuf - 1;
     prefill_step<0, kNBuf>(s, nsteps, xact, xv0, xv1, xv2, xv3, xv4, xs[0][xr] + 40 * xh, wr, sel0, K,
-                           ws[0][brow] + 20 * u, W, u, xsrc, xh, ws[0], xs[0], bro0, bro1, r16, g, wm, mt_active, acc);
+                           ws[0][brow] + 40 * u, W, u, xsrc, xh, ws[0], xs[0], bro, r16, g, wm, mt_active, acc);
     prefill_step<b1, kNBuf>(s + 1, nsteps, xact, xv0, xv1, xv2, xv3, xv4, xs[b1][xr] + 40 * xh, wr, sel1, K,
-                            ws[b1][brow] + 20 * u, W, u, xsrc, xh, ws[b1], xs[b1], bro0, bro1, r16, g, wm, mt_active,
-                            acc);
+                            ws[b1][brow] + 40 * u, W, u, xsrc, xh, ws[b1], xs[b1], bro, r16, g, wm, mt_active, acc);
   }
   // D: lane holds tokens 4 g + i of the M tile for column r16 of the N tile
 #pragma unroll
@@ -331,15 +341,21 @@ __global__ void __launch_bounds__(256, kNBuf == 1 ? 4 : 2) prefill_kernel(Prefil
       const int hrow = row_sh[mm];
       if (hrow < 0) continue;
       if constexpr (NMAT == 2) {
-        const int col = nt * (kPN / 2) + 16 * wn + r16;
-        const float gv = acc[mt][0][i], uv = acc[mt][1][i];
-        // h is rounded to fp16 here, so the division is kept exact
-        const float h = gv / (1.0f + __expf(-gv)) * uv;
-        P.h16[(size_t)hrow * P.kp_ff + pair_slot(col)] = (_Float16)h;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const int col = nt * (kPN / 2) + 32 * wn + 16 * nb + r16;
+          const float gv = acc[mt][nb][i], uv = acc[mt][nb + 2][i];
+          // h is rounded to fp16 here, so the division is kept exact
+          const float h = gv / (1.0f + __expf(-gv)) * uv;
+          P.h16[(size_t)hrow * P.kp_ff + pair_slot(col)] = (_Float16)h;
+        }
       } else {
         float *y = we.expert >= 0 ? P.y_pairs + (size_t)hrow * P.d_model : P.y_shared + (size_t)tok_sh[mm] * P.d_model;
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) y[nt * kPN + 32 * wn + 16 * nb + r16] = acc[mt][nb][i];
+        for (int nb = 0; nb < 4; ++nb) {
+          const int col = nt * kPN + 64 * wn + 16 * nb + r16;
+          if (col < P.d_model) y[col] = acc[mt][nb][i];
+        }
       }
     }
 }
@@ -365,7 +381,7 @@ hipError_t launch_bucket_ex(const moe_ctx *c, const int32_t *idx, int T, int32_t
 hipError_t launch_ffn_prefill(const moe_ctx *c, int layer, const float *x, int T, const int32_t *idx,
                               const int32_t *slot_of_pair, float *y_pairs, float *y_shared, hipStream_t s) {
   const moe_config &k = c->cfg;
-  if (k.d_ff % kPN || k.d_model % kPN) return hipErrorInvalidValue;
+  if (k.d_ff % (kPN / 2) || k.d_model % (kPN / 2)) return hipErrorInvalidValue;
   hipError_t e = launch_bucket_ex(c, idx, T, c->offsets_ws, c->perm_ws, true, kPM, nullptr, nullptr, 0, s);
   if (e != hipSuccess) return e;
   const int kpm = c->L.gate.nsb * moe::kSbCols, kpf = c->L.down.nsb * moe::kSbCols;
@@ -404,7 +420,7 @@ hipError_t launch_ffn_prefill(const moe_ctx *c, int layer, const float *x, int T
   const int pairs = T * k.top_k;
   const int ents = pairs / kPM + (pairs < k.n_experts ? pairs : k.n_experts) + (T + kPM - 1) / kPM;
   hipLaunchKernelGGL(prefill_kernel<2>, dim3(ents * (k.d_ff / (kPN / 2))), dim3(256), 0, s, P);
-  hipLaunchKernelGGL(prefill_kernel<1>, dim3(ents * (k.d_model / kPN)), dim3(256), 0, s, P);
+  hipLaunchKernelGGL(prefill_kernel<1>, dim3(ents * ((k.d_model + kPN - 1) / kPN)), dim3(256), 0, s, P);
   return hipGetLastError();
 }
 
