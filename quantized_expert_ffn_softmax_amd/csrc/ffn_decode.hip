@@ -151,6 +151,7 @@ __device__ inline bool entry_token(const DecodeParams &P, const moe::WorkEntry &
 
 constexpr int kWaves = 4;
 constexpr int kXcds = 8;      // accelerator dies of MI355X, each with its own L2
+constexpr int kSplitMaxTokens = 5;  // gate/up splits K over the waves up to this batch
 constexpr int kCols = moe::kEntryTokens;                 // entry columns held in LDS
 constexpr int kSbBytes = moe::kSteps * 2 * kCols * 16;   // one superblock of an entry's activations: 2,560 B
 
@@ -218,9 +219,9 @@ __device__ inline Mats<NMAT> mats_of(const DecodeParams &P) {
   return Mt;
 }
 
-__device__ inline void unit_setup(const DecodeParams &P, int u, int tpu, int col, Unit &U) {
+__device__ inline void unit_setup(const DecodeParams &P, int u, int tpu, int tiles, int col, Unit &U) {
   const moe::WorkEntry we = P.work[u / tpu];
-  U.tile0 = (u % tpu) * kWaves;
+  U.tile0 = (u % tpu) * tiles;
   U.routed = we.expert >= 0;
   const uint8_t *blob = entry_ok(P, we) ? entry_blob(P, we) : nullptr;
   U.m = blob ? we.m : 0;
@@ -269,7 +270,7 @@ struct CopyCounts {
 // 8 halves of that record step for entry column col
 template <int NSB, int NMAT>
 __device__ inline void copy_unit_lds(const Mats<NMAT> &Mt, const Unit &U, int tid, uint32_t row_off, uint32_t zero_off,
-                                     uint8_t *lact, uint8_t *lsc) {
+                                     int unit_rows, int sc_mat_bytes, uint8_t *lact, uint8_t *lsc) {
   const uint8_t *rec = reinterpret_cast<const uint8_t *>(Mt.rec);
   const int col = tid & 3, half = (tid >> 2) & 1, w = tid >> 6;
   (void)col;
@@ -286,12 +287,12 @@ __device__ inline void copy_unit_lds(const Mats<NMAT> &Mt, const Unit &U, int ti
   const uint32_t s0 = lds_addr(lsc) + 1024u * w;
 #pragma unroll
   for (int mat = 0; mat < NMAT; ++mat) {
-    const int nbytes = 64 * Mt.m[mat].nblk * 2;  // the unit's 64 rows, contiguous
+    const int nbytes = unit_rows * Mt.m[mat].nblk * 2;  // the unit's rows, contiguous
     const uint8_t *src = U.blob + Mt.m[mat].scale_off + (uint32_t)U.tile0 * 16 * Mt.m[mat].nblk * 2;
 #pragma unroll
     for (int i = 0; i < CopyCounts<NSB, NMAT>::sc; ++i) {
       const int byte = 16 * tid + 4096 * i;
-      if (byte < nbytes) lds_copy16(src + byte, s0 + (uint32_t)(mat * 64 * 5 * NSB * 2) + 4096u * i);
+      if (byte < nbytes) lds_copy16(src + byte, s0 + (uint32_t)(mat * sc_mat_bytes) + 4096u * i);
     }
   }
 }
@@ -332,14 +333,14 @@ struct MatSb {
 
 // scales (s_b, s_b+1) of this lane's row from the LDS copy, b = 5 S + g
 // clamped to the row (only the last superblock can reach past it)
-template <bool LAST>
+template <bool CLAMP>
 __device__ inline MatSb mat_sb(const uint4 &wq, const uint8_t *srow, int b, int nblk, const uint32_t (&sel)[6]) {
   MatSb M;
   M.w[0] = wq.x;
   M.w[1] = wq.y;
   M.w[2] = wq.z;
   M.w[3] = wq.w;
-  const int b0 = LAST ? min(b, nblk - 1) : b, b1 = LAST ? min(b + 1, nblk - 1) : b + 1;
+  const int b0 = CLAMP ? min(b, nblk - 1) : b, b1 = CLAMP ? min(b + 1, nblk - 1) : b + 1;
   const uint32_t lo = *reinterpret_cast<const uint16_t *>(srow + 2 * b0);
   const uint32_t hi = *reinterpret_cast<const uint16_t *>(srow + 2 * b1);
   M.P = lo | (hi << 16);
@@ -400,19 +401,26 @@ __device__ inline void unit_epilogue(const DecodeParams &P, const Unit &U, int w
 // two matrices in flight within the register budget of 3 waves per SIMD)
 template <int NSB, int NMAT>
 constexpr int words_depth() {
-  return NMAT == 2 ? (NSB < 4 ? NSB : 4) : NSB;
+  // a half range (K split, <= 7 superblocks) keeps 3: its kernel carries the split's extra registers
+  return NMAT == 2 ? (NSB <= 7 ? (NSB < 3 ? NSB : 3) : 4) : NSB;
 }
 
+// A wave walks NSB superblocks of its range (the whole row, or one half of it
+// when K is split): superblock S of the range is superblock sb0 + S of the
+// row; only the first `nvalid` exist (the last one of a second half may not).
 template <int NSB, int NMAT>
 struct WordSrc {
   const uint8_t *blob;
-  uint32_t off[NMAT];  // this lane's quad of superblock 0 in each matrix
+  uint32_t off[NMAT];  // this lane's quad of the range's first superblock in each matrix
+  int nvalid;
 };
 
 template <int NSB, int NMAT, int S>
 __device__ inline void load_words(const WordSrc<NSB, NMAT> &Src, uint4 (&W)[NSB][NMAT]) {
+  // only a range's last superblock can lie past the row (a shorter second half)
+  const uint32_t so = S + 1 < NSB ? (uint32_t)S * 64 : (uint32_t)min(S, Src.nvalid - 1) * 64;
 #pragma unroll
-  for (int mat = 0; mat < NMAT; ++mat) W[S][mat] = *reinterpret_cast<const uint4 *>(Src.blob + (Src.off[mat] + S * 64));
+  for (int mat = 0; mat < NMAT; ++mat) W[S][mat] = *reinterpret_cast<const uint4 *>(Src.blob + (Src.off[mat] + so));
 }
 
 template <int NSB, int NMAT, int... Ss>
@@ -437,16 +445,20 @@ template <int NSB, int NMAT, int S>
 __device__ inline void compute_pair(uint4 (&W)[NSB][NMAT], const WordSrc<NSB, NMAT> &Src,
                                     const uint8_t *(&srow)[NMAT], int g, int nblk, const uint32_t (&sel)[6],
                                     const Consts &K, const uint8_t *xb, f4 &acc0, f4 &acc1, f4 &acc2, f4 &acc3) {
+  // g carries the range's first scale block: block 5 S + g of the range
+  if constexpr (S + 1 >= NSB) {
+    if (S >= Src.nvalid) return;  // a second half one superblock shorter (uniform)
+  }
   MatSb M[NMAT];
 #pragma unroll
-  for (int mat = 0; mat < NMAT; ++mat) M[mat] = mat_sb<S + 1 == NSB>(W[S][mat], srow[mat], 5 * S + g, nblk, sel);
+  for (int mat = 0; mat < NMAT; ++mat) M[mat] = mat_sb<S + 2 >= NSB>(W[S][mat], srow[mat], 5 * S + g, nblk, sel);
   refill<NSB, NMAT, S>(W, Src);
   const uint8_t *xs = xb + S * moe::kSteps * 128;
   if constexpr (S + 1 < NSB) {
     MatSb M2[NMAT];
 #pragma unroll
     for (int mat = 0; mat < NMAT; ++mat)
-      M2[mat] = mat_sb<S + 2 == NSB>(W[S + 1][mat], srow[mat], 5 * (S + 1) + g, nblk, sel);
+      M2[mat] = mat_sb<S + 3 >= NSB>(W[S + 1][mat], srow[mat], 5 * (S + 1) + g, nblk, sel);
     refill<NSB, NMAT, S + 1>(W, Src);
     const uint8_t *xs2 = xs + moe::kSteps * 128;
     sb_step<NMAT, 0>(M, K, xs, acc0, acc1);
@@ -476,17 +488,30 @@ __device__ inline void compute_all(std::integer_sequence<int, Ps...>, uint4 (&W)
   (compute_pair<NSB, NMAT, 2 * Ps>(W, Src, srow, g, nblk, sel, K, xb, acc0, acc1, acc2, acc3), ...);
 }
 
-template <int NSB, int NMAT>
+// KS = 2 (gate/up of small batches): K split in two halves over the waves of a
+// workgroup -- waves 2h + l take tile l of the unit's 2 tiles and superblocks
+// [h H, min((h + 1) H, NSB)) with H = ceil(NSB / 2) -- and the halves' sums
+// added through LDS before the epilogue.  Twice the waves in flight and half
+// the chain per wave, for batches whose units leave CUs idle.
+template <int NSB, int NMAT, int KS>
 __global__ void __launch_bounds__(64 * kWaves, NMAT == 2 ? 3 : 4) ffn_decode_kernel(DecodeParams P) {
+  static_assert(KS == 1 || (NMAT == 2 && ((NSB + 1) / 2) % 2 == 1), "K split: gate/up, an odd half length");
+  constexpr int NS = KS == 2 ? (NSB + 1) / 2 : NSB;  // superblocks of a wave's range
+  constexpr int kTiles = kWaves / KS;                 // 16-row tiles of a unit
   constexpr int kActBytes = NSB * kSbBytes;
-  constexpr int kScBytes = NMAT * 64 * 5 * NSB * 2;
+  constexpr int kScMat = 16 * kTiles * 5 * NSB * 2;  // one matrix's scales of the unit's rows (nblk <= 5 NSB)
+  constexpr int kScBytes = NMAT * kScMat;
   __shared__ __attribute__((aligned(1024))) uint8_t lact[kActBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t lsc[(kScBytes + 4095) / 4096 * 4096];
+  __shared__ f4 red[KS == 2 ? kTiles * 64 * 2 : 1];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
+  const int ltile = KS == 2 ? (w & 1) : w;                                 // tile of the unit
+  const int half = KS == 2 ? __builtin_amdgcn_readfirstlane(w >> 1) : 0;  // range (uniform per wave)
+  const int sb0 = half * NS;
   const Mats<NMAT> Mt = mats_of<NMAT>(P);
   const int ntile = Mt.m[0].rows / 16;
-  const int tpu = (ntile + kWaves - 1) / kWaves;
+  const int tpu = (ntile + kTiles - 1) / kTiles;
   const int nblk = Mt.m[0].nblk;
   const int n_units = min(P.n_work[0], P.max_work) * tpu;
   // Workgroup b runs on XCD b % 8 (round-robin dispatch).  Each XCD takes a
@@ -508,38 +533,52 @@ __global__ void __launch_bounds__(64 * kWaves, NMAT == 2 ? 3 : 4) ffn_decode_ker
   const uint32_t zero_off = (uint32_t)(Mt.zero - Mt.rec) * 2u;
   // B operand of lane (j, g) at step t of superblock S: slot ((20 S + 5 g +
   // t) * 2 + (j & 7) / 4) * 4 + j % 4, i.e. byte (20 S + t) * 128 + 640 g +
-  // 16 (j & 7)
-  const uint8_t *xb = lact + 640 * g + 16 * (r16 & 7);
+  // 16 (j & 7); the wave's range starts at superblock sb0
+  const uint8_t *xb = lact + 640 * g + 16 * (r16 & 7) + sb0 * moe::kSteps * 128;
   bool first = true;
   for (int u = xcd * per + blockIdx.x / kXcds; u < u_end; u += u_step) {
     if (!first) __syncthreads();  // every wave is done with the previous unit's LDS data
     first = false;
     Unit U;
-    unit_setup(P, u, tpu, tid & 3, U);
+    unit_setup(P, u, tpu, kTiles, tid & 3, U);
     const uint32_t row_off = (uint32_t)(NMAT == 2 ? U.tok : U.rrow) * (uint32_t)Mt.rec_h * 2u;
-    copy_unit_lds<NSB, NMAT>(Mt, U, tid, row_off, zero_off, lact, lsc);
+    copy_unit_lds<NSB, NMAT>(Mt, U, tid, row_off, zero_off, 16 * kTiles, kScMat, lact, lsc);
     // the word quads of this wave's rows, as many superblocks as fit
-    const int row = min((U.tile0 + w) * 16 + r16, Mt.m[0].rows - 1);
-    WordSrc<NSB, NMAT> Src;
+    const int row = min((U.tile0 + ltile) * 16 + r16, Mt.m[0].rows - 1);
+    WordSrc<NS, NMAT> Src;
     Src.blob = U.blob;
+    Src.nvalid = min(NS, NSB - sb0);
 #pragma unroll
-    for (int mat = 0; mat < NMAT; ++mat) Src.off[mat] = Mt.m[mat].code_off + (uint32_t)row * Mt.m[mat].wpr * 4 + g * 16;
-    constexpr int D = words_depth<NSB, NMAT>();
-    uint4 W[NSB][NMAT];
-    load_first<NSB, NMAT>(std::make_integer_sequence<int, D>{}, Src, W);
+    for (int mat = 0; mat < NMAT; ++mat)
+      Src.off[mat] = Mt.m[mat].code_off + (uint32_t)row * Mt.m[mat].wpr * 4 + g * 16 + sb0 * 64;
+    constexpr int D = words_depth<NS, NMAT>();
+    uint4 W[NS][NMAT];
+    load_first<NS, NMAT>(std::make_integer_sequence<int, D>{}, Src, W);
     // the copies were issued before the word loads: waiting until only the
     // word loads may be outstanding lands them; then publish
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(D * NMAT) : "memory");
     __syncthreads();
     const uint8_t *srow[NMAT];
 #pragma unroll
-    for (int mat = 0; mat < NMAT; ++mat) srow[mat] = lsc + mat * 64 * 5 * NSB * 2 + (w * 16 + r16) * nblk * 2;
+    for (int mat = 0; mat < NMAT; ++mat)
+      srow[mat] = lsc + mat * kScMat + (ltile * 16 + r16) * nblk * 2;
     f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f}, acc2 = acc0, acc3 = acc0;
-    compute_all<NSB, NMAT>(std::make_integer_sequence<int, (NSB + 1) / 2>{}, W, Src, srow, g, nblk, sel, K, xb, acc0,
-                           acc1, acc2, acc3);
+    compute_all<NS, NMAT>(std::make_integer_sequence<int, (NS + 1) / 2>{}, W, Src, srow, 5 * sb0 + g, nblk, sel, K,
+                          xb, acc0, acc1, acc2, acc3);
     acc0 += acc2;
     acc1 += acc3;
-    unit_epilogue<NMAT>(P, U, w, lane, acc0, acc1);
+    if constexpr (KS == 2) {
+      // second half -> LDS; the first half adds it (fixed order: first + second)
+      if (half == 1) {
+        red[(ltile * 64 + lane) * 2 + 0] = acc0;
+        red[(ltile * 64 + lane) * 2 + 1] = acc1;
+      }
+      __syncthreads();
+      if (half == 1) continue;
+      acc0 += red[(ltile * 64 + lane) * 2 + 0];
+      acc1 += red[(ltile * 64 + lane) * 2 + 1];
+    }
+    unit_epilogue<NMAT>(P, U, ltile, lane, acc0, acc1);
   }
 }
 
@@ -559,7 +598,7 @@ inline int max_entries(int T, int k, int E, int entry_m) {
 
 // one unit (entry x 4 tiles) per workgroup while that fits in the workgroups
 // the CUs hold at once; beyond, workgroups loop over units
-template <int NSB, int NMAT>
+template <int NSB, int NMAT, int KS = 1>
 hipError_t launch_decode_nsb(const DecodeParams &P, int units, hipStream_t s) {
   static int per_cu = 0, n_cu = 0;
   if (!per_cu) {
@@ -567,14 +606,14 @@ hipError_t launch_decode_nsb(const DecodeParams &P, int units, hipStream_t s) {
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e == hipSuccess)
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, ffn_decode_kernel<NSB, NMAT>, 64 * kWaves, 0);
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, ffn_decode_kernel<NSB, NMAT, KS>, 64 * kWaves, 0);
     if (e != hipSuccess) return e;
     n_cu = cus > 0 ? cus : 1;
     per_cu = occ > 0 ? occ : 1;
   }
   const int cap = per_cu * n_cu;
   const int grid = (std::min(units, cap) + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL((ffn_decode_kernel<NSB, NMAT>), dim3(grid), dim3(64 * kWaves), 0, s, P);
+  hipLaunchKernelGGL((ffn_decode_kernel<NSB, NMAT, KS>), dim3(grid), dim3(64 * kWaves), 0, s, P);
   return hipGetLastError();
 }
 
@@ -647,7 +686,15 @@ hipError_t launch_ffn_decode(const moe_ctx *c, int layer, const float *x, int T,
   P.d_ff = k.d_ff;
   const int ents = max_entries(T, k.top_k, k.n_experts, moe::kEntryTokens);
   const int u1 = ents * ((k.d_ff / 16 + kWaves - 1) / kWaves), u2 = ents * ((k.d_model / 16 + kWaves - 1) / kWaves);
-  e = launch_decode_mat<2>(c->L.gate.nsb, P, u1, s);
+  // Small batches (a single request's 1 + 4 verified tokens, ~30 entries)
+  // leave most CUs idle in gate/up: split its K over the waves instead.
+  // Built for the 13-superblock rows of d_model = 1,921..2,080.
+  if (T <= kSplitMaxTokens && c->L.gate.nsb == 13) {
+    const int u1s = ents * ((k.d_ff / 16 + kWaves / 2 - 1) / (kWaves / 2));
+    e = launch_decode_nsb<13, 2, 2>(P, u1s, s);
+  } else {
+    e = launch_decode_mat<2>(c->L.gate.nsb, P, u1, s);
+  }
   if (e != hipSuccess) return e;
   e = launch_decode_mat<1>(c->L.down.nsb, P, u2, s);
   if (e != hipSuccess) return e;
