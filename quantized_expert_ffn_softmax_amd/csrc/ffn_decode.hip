@@ -269,8 +269,8 @@ struct CopyCounts {
 // activation slot p = (superblock * 20 + step) * 8 + half * 4 + col holds the
 // 8 halves of that record step for entry column col
 template <int NSB, int NMAT>
-__device__ inline void copy_unit_lds(const Mats<NMAT> &Mt, const Unit &U, int tid, uint32_t row_off, uint32_t zero_off,
-                                     int unit_rows, int sc_mat_bytes, uint8_t *lact, uint8_t *lsc) {
+__device__ inline void copy_unit_lds(const Mats<NMAT> &Mt, const Unit &U, int tid, uint32_t row_off, int unit_rows,
+                                     int sc_mat_bytes, uint8_t *lact, uint8_t *lsc) {
   const uint8_t *rec = reinterpret_cast<const uint8_t *>(Mt.rec);
   const int col = tid & 3, half = (tid >> 2) & 1, w = tid >> 6;
   (void)col;
@@ -279,10 +279,10 @@ __device__ inline void copy_unit_lds(const Mats<NMAT> &Mt, const Unit &U, int ti
   for (int i = 0; i < CopyCounts<NSB, NMAT>::act; ++i) {
     const int p = tid + 64 * kWaves * i;
     const int ms = p >> 3;
-    if (p < NSB * moe::kSteps * 2 * kCols) {
-      const uint32_t off = U.has_tok ? row_off + (ms * 16 + half * 8) * 2 : zero_off + ((ms % moe::kSteps) * 16 + half * 8) * 2;
-      lds_copy16(rec + off, a0 + 4096u * i);
-    }
+    // columns past the entry's tokens are not copied: an MFMA output column
+    // depends only on its own B column and the epilogue writes only the
+    // entry's tokens, so those slots may hold anything
+    if (U.has_tok && p < NSB * moe::kSteps * 2 * kCols) lds_copy16(rec + row_off + (ms * 16 + half * 8) * 2, a0 + 4096u * i);
   }
   const uint32_t s0 = lds_addr(lsc) + 1024u * w;
 #pragma unroll
@@ -530,7 +530,6 @@ __global__ void __launch_bounds__(64 * kWaves, NMAT == 2 ? 3 : 4) ffn_decode_ker
                    s3 = cls_sel(pair_cls(3, q));
     sel[p - 1] = g == 0 ? s0 : g == 1 ? s1 : g == 2 ? s2 : s3;
   }
-  const uint32_t zero_off = (uint32_t)(Mt.zero - Mt.rec) * 2u;
   // B operand of lane (j, g) at step t of superblock S: slot ((20 S + 5 g +
   // t) * 2 + (j & 7) / 4) * 4 + j % 4, i.e. byte (20 S + t) * 128 + 640 g +
   // 16 (j & 7); the wave's range starts at superblock sb0
@@ -542,7 +541,7 @@ __global__ void __launch_bounds__(64 * kWaves, NMAT == 2 ? 3 : 4) ffn_decode_ker
     Unit U;
     unit_setup(P, u, tpu, kTiles, tid & 3, U);
     const uint32_t row_off = (uint32_t)(NMAT == 2 ? U.tok : U.rrow) * (uint32_t)Mt.rec_h * 2u;
-    copy_unit_lds<NSB, NMAT>(Mt, U, tid, row_off, zero_off, 16 * kTiles, kScMat, lact, lsc);
+    copy_unit_lds<NSB, NMAT>(Mt, U, tid, row_off, 16 * kTiles, kScMat, lact, lsc);
     // the word quads of this wave's rows, as many superblocks as fit
     const int row = min((U.tile0 + ltile) * 16 + r16, Mt.m[0].rows - 1);
     WordSrc<NS, NMAT> Src;
