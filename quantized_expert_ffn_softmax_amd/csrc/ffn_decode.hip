@@ -258,12 +258,20 @@ __device__ inline uint32_t lds_addr(const void *p) {
 
 __device__ inline h8 lds_h8(const uint8_t *p) { return *reinterpret_cast<const h8 *>(p); }
 
+// LDS row pitch of a unit's scale rows: the row's bytes, rounded up to an odd
+// number of 16-byte granules when they are a multiple of 16 (2 nblk = 128 at
+// d_model 2048 would put the 16 rows a wave reads on the same banks); other
+// widths keep the plain row (48 bytes at d_ff 768: already an odd count)
+__host__ __device__ constexpr int sc_pitch(int nblk) {
+  return (2 * nblk) % 16 == 0 ? ((2 * nblk / 16) | 1) * 16 : 2 * nblk;
+}
+
 // number of 16-byte-per-lane copies one thread issues for the unit's LDS data
 template <int NSB, int NMAT>
 struct CopyCounts {
   static constexpr int act = (NSB * moe::kSteps * 2 * kCols + 64 * kWaves - 1) / (64 * kWaves);
-  // scales: 64 rows x nblk x 2 B per matrix, nblk <= 5 NSB
-  static constexpr int sc = (64 * 5 * NSB * 2 + 16 * 64 * kWaves - 1) / (16 * 64 * kWaves);
+  // scales: <= 64 rows x sc_pitch(nblk) per matrix, nblk <= 5 NSB
+  static constexpr int sc = (64 * sc_pitch(5 * NSB + 8) + 16 * 64 * kWaves - 1) / (16 * 64 * kWaves);
 };
 
 // activation slot p = (superblock * 20 + step) * 8 + half * 4 + col holds the
@@ -284,15 +292,23 @@ __device__ inline void copy_unit_lds(const Mats<NMAT> &Mt, const Unit &U, int ti
     // entry's tokens, so those slots may hold anything
     if (U.has_tok && p < NSB * moe::kSteps * 2 * kCols) lds_copy16(rec + row_off + (ms * 16 + half * 8) * 2, a0 + 4096u * i);
   }
+  // scales: LDS row pitch sc_pitch(nblk) (see there); granule k of a matrix's
+  // region holds 16 bytes of row k / (pitch / 16) -- the copy picks each
+  // lane's source, so padding a row costs only the extra granule
   const uint32_t s0 = lds_addr(lsc) + 1024u * w;
+  const int rb = Mt.m[0].nblk * 2, pitch = sc_pitch(Mt.m[0].nblk), gpr = pitch / 16;
 #pragma unroll
   for (int mat = 0; mat < NMAT; ++mat) {
-    const int nbytes = unit_rows * Mt.m[mat].nblk * 2;  // the unit's rows, contiguous
-    const uint8_t *src = U.blob + Mt.m[mat].scale_off + (uint32_t)U.tile0 * 16 * Mt.m[mat].nblk * 2;
+    const uint8_t *src = U.blob + Mt.m[mat].scale_off + (uint32_t)U.tile0 * 16 * rb;
 #pragma unroll
     for (int i = 0; i < CopyCounts<NSB, NMAT>::sc; ++i) {
-      const int byte = 16 * tid + 4096 * i;
-      if (byte < nbytes) lds_copy16(src + byte, s0 + (uint32_t)(mat * sc_mat_bytes) + 4096u * i);
+      const int k = tid + 64 * kWaves * i;
+      if (pitch == rb) {  // rows copied as they lie (any row size)
+        if (16 * k < unit_rows * rb) lds_copy16(src + 16 * k, s0 + (uint32_t)(mat * sc_mat_bytes) + 4096u * i);
+      } else if (k < unit_rows * gpr) {
+        const int row = k / gpr, c = min(k - row * gpr, rb / 16 - 1);  // the pad granule repeats the last
+        lds_copy16(src + row * rb + 16 * c, s0 + (uint32_t)(mat * sc_mat_bytes) + 4096u * i);
+      }
     }
   }
 }
@@ -499,7 +515,7 @@ __global__ void __launch_bounds__(64 * kWaves, NMAT == 2 ? 3 : 4) ffn_decode_ker
   constexpr int NS = KS == 2 ? (NSB + 1) / 2 : NSB;  // superblocks of a wave's range
   constexpr int kTiles = kWaves / KS;                 // 16-row tiles of a unit
   constexpr int kActBytes = NSB * kSbBytes;
-  constexpr int kScMat = 16 * kTiles * 5 * NSB * 2;  // one matrix's scales of the unit's rows (nblk <= 5 NSB)
+  constexpr int kScMat = 16 * kTiles * sc_pitch(5 * NSB + 8);  // one matrix's scales of the unit's rows (nblk <= 5 NSB)
   constexpr int kScBytes = NMAT * kScMat;
   __shared__ __attribute__((aligned(1024))) uint8_t lact[kActBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t lsc[(kScBytes + 4095) / 4096 * 4096];
@@ -560,7 +576,7 @@ __global__ void __launch_bounds__(64 * kWaves, NMAT == 2 ? 3 : 4) ffn_decode_ker
     const uint8_t *srow[NMAT];
 #pragma unroll
     for (int mat = 0; mat < NMAT; ++mat)
-      srow[mat] = lsc + mat * kScMat + (ltile * 16 + r16) * nblk * 2;
+      srow[mat] = lsc + mat * kScMat + (ltile * 16 + r16) * sc_pitch(nblk);
     f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f}, acc2 = acc0, acc3 = acc0;
     compute_all<NS, NMAT>(std::make_integer_sequence<int, (NS + 1) / 2>{}, W, Src, srow, 5 * sb0 + g, nblk, sel, K,
                           xb, acc0, acc1, acc2, acc3);
