@@ -47,52 +47,93 @@ __device__ void build_work(const int *cnt_sh, const int *off_sh, int E, int T, i
   }
 }
 
-// n = T*k <= 1024 pairs: one workgroup does everything.
+// n = T*k <= 1024 pairs, E <= 1024: workgroup 0 does the bucketing with
+// blockDim.x >= max(n, E) threads (thread i holds pair i and expert i).
+//   1. each pair takes a slot in its expert by an LDS atomic (arrival order)
+//   2. one scan over the experts of (entries << 16 | pairs) gives the offsets
+//      and the first work entry of every expert (both totals <= 1024)
+//   3. pair ids go to their expert's segment in slot order, and each pair's
+//      place is its rank among the ids of its segment: perm is the stable
+//      order (ascending expert, then ascending pair id), at a cost of the
+//      segment's length instead of the number of pairs.
+// The other workgroups of the launch build the record of x (decode path).
 __global__ void __launch_bounds__(kBucketThreads) bucket_small(const int32_t *__restrict__ idx, int n, int E, int T,
                                                        int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
                                                        int build, int entry_m, moe::WorkEntry *work,
                                                        int32_t *n_work, const float *__restrict__ x, int d, int nsb,
                                                        uint16_t *__restrict__ xrec, int xrec_h) {
-  __shared__ int ex[kSmallMax];
   __shared__ int cnt[1024];
-  __shared__ int off[1025];
-  __shared__ int sh[17];
-  const int tid = threadIdx.x;
+  __shared__ int off[1024];
+  __shared__ int ids[kSmallMax];
+  __shared__ int wsum[kBucketThreads / 64];
+  const int tid = threadIdx.x, nt = blockDim.x;
   if (blockIdx.x > 0) {
-    // decode path: the other workgroups of this launch build the activation
-    // record of x (independent of the bucketing done by workgroup 0)
-    moe::build_xrec_range(x, T, d, nsb, xrec, xrec_h, (blockIdx.x - 1) * kBucketThreads + tid,
-                          (gridDim.x - 1) * kBucketThreads);
+    moe::build_xrec_range(x, T, d, nsb, xrec, xrec_h, (blockIdx.x - 1) * nt + tid, (gridDim.x - 1) * nt);
     return;
   }
-  cnt[tid] = 0;
-  __syncthreads();
+  const int lane = tid & 63, wave = tid >> 6, nwaves = nt >> 6;
+  int ex = -1;
   if (tid < n) {
-    const int e = idx[tid];
-    ex[tid] = (e >= 0 && e < E) ? e : -1;  // out-of-range ids are ignored
-    if (ex[tid] >= 0) atomicAdd(&cnt[e], 1);
+    const int v = idx[tid];
+    ex = (v >= 0 && v < E) ? v : -1;  // out-of-range ids are ignored
   }
+  if (tid < E) cnt[tid] = 0;
   __syncthreads();
-  int total;
-  const int excl = moe::block_excl_scan_1024(tid < E ? cnt[tid] : 0, &total, sh);
-  if (tid < E) off[tid] = excl;
-  if (tid == 0) off[E] = total;
+  const int slot = ex >= 0 ? atomicAdd(&cnt[ex], 1) : 0;
   __syncthreads();
-  if (tid <= E) offsets[tid] = off[tid];
-  if (tid < n && ex[tid] >= 0) {
-    const int e = ex[tid];
-    // stable rank among the pairs of expert e; 16 LDS reads in flight at once
-    int r = 0;
-    for (int q0 = 0; q0 < tid; q0 += 16) {
-      int v[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = ex[min(q0 + i, kSmallMax - 1)];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) r += (q0 + i < tid) && v[i] == e;
+  const int c = tid < E ? cnt[tid] : 0;
+  const int ne = build ? (c + entry_m - 1) / entry_m : 0;
+  const int packed = (ne << 16) | c;
+  const int incl = moe::wave_incl_scan(packed);
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+  for (int w = 0; w < nwaves; ++w) {
+    const int v = wsum[w];
+    before += w < wave ? v : 0;
+    total += v;
+  }
+  const int excl = before + incl - packed;
+  const int oe = excl & 0xffff, total_pairs = total & 0xffff;
+  if (tid < E) {
+    off[tid] = oe;
+    offsets[tid] = oe;
+  }
+  if (tid == 0) offsets[E] = total_pairs;
+  if (build) {
+    const int eb = excl >> 16, total_ents = total >> 16;
+    for (int i = 0; i < ne; ++i) {
+      moe::WorkEntry w;
+      w.expert = tid;
+      w.first = oe + i * entry_m;
+      w.m = min(entry_m, c - i * entry_m);
+      w.pad = 0;
+      work[eb + i] = w;
     }
-    perm[off[e] + r] = tid;
+    // then the shared expert's T tokens
+    const int ns = (T + entry_m - 1) / entry_m;
+    for (int i = tid; i < ns; i += nt) {
+      moe::WorkEntry w;
+      w.expert = -1;
+      w.first = i * entry_m;
+      w.m = min(entry_m, T - i * entry_m);
+      w.pad = 0;
+      work[total_ents + i] = w;
+    }
+    if (tid == 0) {
+      n_work[0] = total_ents + ns;
+      n_work[1] = total_ents;
+    }
   }
-  if (build) build_work(cnt, off, E, T, entry_m, work, n_work, sh);
+  __syncthreads();
+  if (ex >= 0) ids[off[ex] + slot] = tid;
+  __syncthreads();
+  if (ex >= 0) {
+    const int base = off[ex], len = cnt[ex];
+    int r = 0;
+    for (int j = 0; j < len; ++j) r += ids[base + j] < tid;
+    perm[base + r] = tid;
+  }
 }
 
 // Multi-block path, phase 1: per-chunk histograms chunk_cnt[chunk][E].
@@ -171,15 +212,16 @@ hipError_t launch_bucket_ex(const moe_ctx *c, const int32_t *idx, int T, int32_t
                             int entry_m, const float *x, uint16_t *xrec, int xrec_h, hipStream_t s) {
   const int E = c->cfg.n_experts, n = T * c->cfg.top_k;
   if (n <= kSmallMax) {
-    // with x: 1 + enough workgroups to build its record, one value per
-    // thread (so all its loads are in flight at once: at 8 per thread the
-    // record took ~6 us of dependent loads)
+    // one thread per pair and per expert; with x, 1 + enough workgroups to
+    // build its record, one value per thread (so all its loads are in flight
+    // at once: at 8 per thread the record took ~6 us of dependent loads)
+    const int nt = ((n > E ? n : E) + 63) / 64 * 64;
     int blocks = 1;
     if (x) {
       const int vals = T * c->L.gate.nsb * moe::kSteps * 8;
-      blocks += (vals + kBucketThreads - 1) / kBucketThreads;
+      blocks += (vals + nt - 1) / nt;
     }
-    hipLaunchKernelGGL(bucket_small, dim3(blocks), dim3(kBucketThreads), 0, s, idx, n, E, T, offsets, perm,
+    hipLaunchKernelGGL(bucket_small, dim3(blocks), dim3(nt), 0, s, idx, n, E, T, offsets, perm,
                        build ? 1 : 0, entry_m, c->work, c->n_work, x, c->cfg.d_model, c->L.gate.nsb, xrec, xrec_h);
     return hipGetLastError();
   }

@@ -111,35 +111,58 @@ __global__ void __launch_bounds__(256) combine_norm_kernel(const float *__restri
   const float4 *ys = reinterpret_cast<const float4 *>(y_shared + (size_t)t * d);
   float4 v[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int c = threadIdx.x + 256 * i;
-    v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (c >= d4) continue;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j0 = 0; j0 < k; j0 += 8) {
-      float4 y[8];
-      float wj[8];
+  for (int i = 0; i < 8; ++i) v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  // two columns at a time, all their pair rows (16 at a time) requested
+  // before the first fma: one memory round trip per 16 experts
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const bool ok = j0 + j < k;
-        y[j] = ok ? yp[(size_t)(j0 + j) * d4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
-        wj[j] = ok ? w[(size_t)t * k + j0 + j] : 0.f;
+  for (int i0 = 0; i0 < 8; i0 += 2) {
+    if (threadIdx.x + 256 * i0 >= d4) continue;
+    float4 acc[2], sh[2];
+    acc[0] = acc[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+    auto chunk = [&](int j0) {
+      float4 y[2][16];
+      float wj[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int jj = min(j0 + j, k - 1);  // rows past k are loaded clamped and not used
+        wj[j] = w[(size_t)t * k + jj];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) y[h][j] = yp[(size_t)jj * d4 + min((int)threadIdx.x + 256 * (i0 + h), d4 - 1)];
+      }
+      if (j0 == 0) {
+        // the shared rows, requested behind the pair rows (columns clamped,
+        // unused past d4)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) sh[h] = ys[min((int)threadIdx.x + 256 * (i0 + h), d4 - 1)];
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        acc.x = fmaf(wj[j], y[j].x, acc.x);
-        acc.y = fmaf(wj[j], y[j].y, acc.y);
-        acc.z = fmaf(wj[j], y[j].z, acc.z);
-        acc.w = fmaf(wj[j], y[j].w, acc.w);
+      for (int j = 0; j < 16; ++j) {
+        if (j0 + j >= k) continue;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          acc[h].x = fmaf(wj[j], y[h][j].x, acc[h].x);
+          acc[h].y = fmaf(wj[j], y[h][j].y, acc[h].y);
+          acc[h].z = fmaf(wj[j], y[h][j].z, acc[h].z);
+          acc[h].w = fmaf(wj[j], y[h][j].w, acc[h].w);
+        }
       }
+    };
+    if (k <= 16) {
+      chunk(0);  // straight-line: no loop header for the compiler to wait at
+    } else {
+      for (int j0 = 0; j0 < k; j0 += 16) chunk(j0);
     }
-    const float4 sh = ys[c];
-    acc.x += sh.x;
-    acc.y += sh.y;
-    acc.z += sh.z;
-    acc.w += sh.w;
-    reinterpret_cast<float4 *>(out + (size_t)t * d)[c] = acc;
-    v[i] = acc;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = threadIdx.x + 256 * (i0 + h);
+      if (c >= d4) continue;
+      acc[h].x += sh[h].x;
+      acc[h].y += sh[h].y;
+      acc[h].z += sh[h].z;
+      acc[h].w += sh[h].w;
+      reinterpret_cast<float4 *>(out + (size_t)t * d)[c] = acc[h];
+      v[i0 + h] = acc[h];
+    }
   }
   float s = 0.f;
 #pragma unroll

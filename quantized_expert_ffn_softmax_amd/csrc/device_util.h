@@ -36,4 +36,18 @@ __device__ inline int block_excl_scan_1024(int v, int *total, int *sh /* >= 17 i
   return res;
 }
 
+// Inclusive scan of one int per lane over a wave64, in DPP moves (no LDS
+// round trips): shifts by 1, 2, 4 and 8 inside each 16-lane row, then the
+// row totals carried across rows by the row_bcast:15 and row_bcast:31
+// broadcasts.  Lanes a move does not reach keep the 0 passed as `old`.
+__device__ inline int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1 and 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
 }  // namespace moe

@@ -258,9 +258,10 @@ __global__ void __launch_bounds__(1024) router_finish_small(const float *__restr
                                                             const float *__restrict__ bias, int k,
                                                             float *__restrict__ logits, int32_t *__restrict__ idx,
                                                             float *__restrict__ w) {
-  __shared__ uint64_t lk[1024];
+  __shared__ __attribute__((aligned(16))) uint64_t lk[1024];
   __shared__ uint64_t ck[16 * 32];
-  __shared__ float top[32];
+  __shared__ float top_v[32];
+  __shared__ int top_e[32];
   const int t = blockIdx.x, e = threadIdx.x, wave = e >> 6;
   float v = -INFINITY;
   if (e < E) {
@@ -278,29 +279,41 @@ __global__ void __launch_bounds__(1024) router_finish_small(const float *__restr
   }
   const uint64_t key = e < E ? order_key(v, e) : 0ull;  // lanes past E order after everything
   lk[e] = key;
-  const int nw = blockDim.x / 64;
-  for (int i = e; i < nw * k; i += blockDim.x) ck[i] = 0ull;  // empty candidate: orders before nothing
+  const int nc = (blockDim.x / 64) * k;  // candidate slots, k per wave
+  for (int i = e; i < nc; i += blockDim.x) ck[i] = 0ull;  // empty candidate: orders before nothing
   __syncthreads();
-  // pass 1: rank inside the wave
+  // pass 1: rank inside the wave, two keys per LDS read
   int r1 = 0;
-#pragma unroll 16
-  for (int o = 0; o < 64; ++o) r1 += lk[wave * 64 + o] > key;
+  const ulonglong2 *wk = reinterpret_cast<const ulonglong2 *>(lk + wave * 64);
+#pragma unroll 8
+  for (int o = 0; o < 32; ++o) {
+    const ulonglong2 q = wk[o];
+    r1 += (q.x > key) + (q.y > key);
+  }
   if (e < E && r1 < k) ck[wave * k + r1] = key;
   __syncthreads();
-  // pass 2: rank among the candidates
-  int r = k;
-  if (e < E && r1 < k) {
-    r = 0;
-    for (int i = 0; i < nw * k; ++i) r += ck[i] > key;
-    if (r < k) top[r] = v;
+  // pass 2: the candidates, one per thread of the first waves, ranked among
+  // themselves; the k best give their expert and logit
+  if (e < nc) {
+    const uint64_t ce = ck[e];
+    if (ce != 0ull) {
+      int r = 0;
+      for (int i = 0; i < nc; ++i) r += ck[i] > ce;
+      if (r < k) {
+        const uint32_t mono = (uint32_t)(ce >> 32);
+        top_v[r] = __uint_as_float((mono & 0x80000000u) ? (mono & 0x7fffffffu) : ~mono);
+        top_e[r] = (int)~(uint32_t)ce;
+      }
+    }
   }
   __syncthreads();
-  if (r < k) {
-    const float m = top[0];
+  // softmax of the k chosen logits
+  if (e < k) {
+    const float m = top_v[0];
     float sum = 0.f;
-    for (int j = 0; j < k; ++j) sum += expf(top[j] - m);
-    idx[(size_t)t * k + r] = e;
-    w[(size_t)t * k + r] = expf(v - m) / sum;
+    for (int j = 0; j < k; ++j) sum += expf(top_v[j] - m);
+    idx[(size_t)t * k + e] = top_e[e];
+    w[(size_t)t * k + e] = expf(top_v[e] - m) / sum;
   }
 }
 
