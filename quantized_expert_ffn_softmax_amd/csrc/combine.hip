@@ -4,6 +4,7 @@
 // The shared expert is added ungated after the routed terms ("另加 1 个共享
 // 专家" -- one shared expert on top of the 10 routed ones: "一张 RTX 4090
 // 跑千亿模型，Strata 实测 155 tok/s", section 如何做到：三层存储).
+#include "device_util.h"
 #include "moe_internal.h"
 
 namespace {
@@ -48,8 +49,7 @@ __global__ void __launch_bounds__(64) combine_kernel(const float *__restrict__ y
 // x_next[t] = c / sqrt(mean(c^2) + 1e-6) with c = out[t] - mean(out[t]); one
 // workgroup per token, two passes over the row (it stays in L2).
 __device__ inline float block_sum_256(float v, float *part) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  v = moe::wave_sum(v);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
   __syncthreads();
   const float tot = part[0] + part[1] + part[2] + part[3];

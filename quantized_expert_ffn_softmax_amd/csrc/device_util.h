@@ -50,4 +50,21 @@ __device__ inline int wave_incl_scan(int v) {
   return v;
 }
 
+template <int CTRL, int ROWS>
+__device__ inline float dpp_move(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWS, 0xf, false));
+}
+
+// Sum of one float per lane over a wave64, in the same DPP moves as
+// wave_incl_scan (a fixed tree order); the total is returned to every lane.
+__device__ inline float wave_sum(float v) {
+  v += dpp_move<0x111, 0xf>(v);  // row_shr:1
+  v += dpp_move<0x112, 0xf>(v);  // row_shr:2
+  v += dpp_move<0x114, 0xf>(v);  // row_shr:4
+  v += dpp_move<0x118, 0xf>(v);  // row_shr:8
+  v += dpp_move<0x142, 0xa>(v);  // row_bcast:15
+  v += dpp_move<0x143, 0xc>(v);  // row_bcast:31
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
 }  // namespace moe

@@ -214,15 +214,31 @@ __global__ void __launch_bounds__(64 * kRouteWaves) router_logits_mfma(const flo
   f4v acc = {0.f, 0.f, 0.f, 0.f};
   const float *wrow = wr + (size_t)(e < E ? e : 0) * d;
   const float *xrow = x + (size_t)(tok < T ? tok : 0) * d;
-  for (int ch = c0 + wave; ch < c1; ch += kRouteWaves) {
-    const int col = ch * 16 + 4 * g;
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-    if (e < E) a = *reinterpret_cast<const float4 *>(wrow + col);
-    if (tok < T) b = *reinterpret_cast<const float4 *>(xrow + col);
+  // two chunks per step, both requested before the first MFMA (a wave
+  // usually has exactly two: one memory round trip instead of two)
+  for (int ch = c0 + wave; ch < c1; ch += 2 * kRouteWaves) {
+    const int ch2 = ch + kRouteWaves;
+    const bool has2 = ch2 < c1;  // wave-uniform
+    const int col = ch * 16 + 4 * g, col2 = (has2 ? ch2 : ch) * 16 + 4 * g;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a, a2 = a, b2 = a;
+    if (e < E) {
+      a = *reinterpret_cast<const float4 *>(wrow + col);
+      a2 = *reinterpret_cast<const float4 *>(wrow + col2);
+    }
+    if (tok < T) {
+      b = *reinterpret_cast<const float4 *>(xrow + col);
+      b2 = *reinterpret_cast<const float4 *>(xrow + col2);
+    }
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, acc, 0, 0, 0);
+    if (has2) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a2.x, b2.x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a2.y, b2.y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a2.z, b2.z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a2.w, b2.w, acc, 0, 0, 0);
+    }
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) red[wave][lane][i] = acc[i];
@@ -265,16 +281,19 @@ __global__ void __launch_bounds__(1024) router_finish_small(const float *__restr
   const int t = blockIdx.x, e = threadIdx.x, wave = e >> 6;
   float v = -INFINITY;
   if (e < E) {
-    // the KS partial sums, requested 8 at a time and added in slice order
+    // the bias and the KS partial sums, requested together (8 slices at a
+    // time, slices past KS clamped and not added), added in slice order
+    const float bv = bias ? bias[e] : 0.f;
     v = 0.f;
     for (int q0 = 0; q0 < KS; q0 += 8) {
       float p[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = q0 + i < KS ? part[((size_t)(q0 + i) * T + t) * E + e] : 0.f;
+      for (int i = 0; i < 8; ++i) p[i] = part[((size_t)min(q0 + i, KS - 1) * T + t) * E + e];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v += p[i];
+      for (int i = 0; i < 8; ++i)
+        if (q0 + i < KS) v += p[i];
     }
-    v += bias ? bias[e] : 0.f;
+    v += bv;
     logits[(size_t)t * E + e] = v;
   }
   const uint64_t key = e < E ? order_key(v, e) : 0ull;  // lanes past E order after everything
