@@ -157,6 +157,35 @@ def test_bucket_small_and_large():
         ctx.close()
 
 
+@pytest.mark.parametrize("case", ["skewed", "n1024", "e1024", "one_expert", "e1k1"])
+def test_bucket_small_path_edges(case):
+    # the single-workgroup bucketing (<= 1024 pairs): long segments, the
+    # pair and expert limits, every pair on one expert, the smallest shape
+    from quantized_expert_ffn_softmax_amd.runtime import MoeContext
+    E, k, T = {"skewed": (512, 10, 100), "n1024": (512, 8, 128), "e1024": (1024, 10, 60),
+               "one_expert": (512, 4, 200), "e1k1": (1, 1, 37)}[case]
+    assert T * k <= 1024
+    rng = np.random.default_rng(7)
+    if case == "skewed":
+        # every token on experts 0..k-1 in shuffled order: segments of length T
+        idx = np.stack([rng.permutation(k) for _ in range(T)])
+    elif case == "one_expert":
+        idx = np.full((T, k), 333)  # repeated ids inside a token too
+    elif case == "e1k1":
+        idx = np.zeros((T, k))
+    else:
+        idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)])
+    idx = idx.astype(np.int32)
+    say(f"  bucketing {case}: E={E} k={k} T={T}")
+    ctx = MoeContext(256, 128, E, k, 1, None, T)
+    off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    B.moe_bucket(ctx.ctx, torch.from_numpy(idx).cuda(), T, off, perm)
+    torch.cuda.synchronize()
+    check_bucket(off.cpu().numpy(), perm.cpu().numpy(), idx, E)
+    ctx.close()
+
+
 @pytest.mark.parametrize("T", [8, 40, 100])
 def test_router_exact_ties(T):
     # zero router weights: every logit is exactly its bias, and the bias holds
