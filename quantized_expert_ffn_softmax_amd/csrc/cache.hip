@@ -70,23 +70,22 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(const int32_t *__rest
   __shared__ int nuniq_sh;
   __shared__ uint64_t shred[17];
   const int tid = threadIdx.x;
+  const int base = layer * E;
   mark[tid] = 0;
   if (tid == 0) nuniq_sh = 0;
   __syncthreads();
   for (int p = tid; p < n; p += kThreads) {
     const int e = idx[p];
     if (e >= 0 && e < E) mark[e] = 1;  // same value from every writer
+    // resident: the slot is the identity, known from the id alone
+    if (resident && slot_of_pair) slot_of_pair[p] = (e >= 0 && e < E) ? base + e : -1;
   }
   __syncthreads();
-  const int base = layer * E;
   if (resident) {
-    if (tid < E && mark[tid]) atomicAdd(&nuniq_sh, 1);
+    // unique count: one ballot per wave, one LDS add per wave
+    const uint64_t b = __ballot(tid < E && mark[tid]);
+    if ((tid & 63) == 0 && b) atomicAdd(&nuniq_sh, __popcll(b));
     __syncthreads();
-    if (slot_of_pair)
-      for (int p = tid; p < n; p += kThreads) {
-        const int e = idx[p];
-        slot_of_pair[p] = (e >= 0 && e < E) ? base + e : -1;
-      }
     if (tid == 0) {
       dmiss[0] = nuniq_sh;
       dmiss[1] = 0;

@@ -275,7 +275,7 @@ __global__ void __launch_bounds__(1024) router_finish_small(const float *__restr
                                                             float *__restrict__ logits, int32_t *__restrict__ idx,
                                                             float *__restrict__ w) {
   __shared__ __attribute__((aligned(16))) uint64_t lk[1024];
-  __shared__ uint64_t ck[16 * 32];
+  __shared__ __attribute__((aligned(16))) uint64_t ck[16 * 32];
   __shared__ float top_v[32];
   __shared__ int top_e[32];
   const int t = blockIdx.x, e = threadIdx.x, wave = e >> 6;
@@ -317,7 +317,12 @@ __global__ void __launch_bounds__(1024) router_finish_small(const float *__restr
     const uint64_t ce = ck[e];
     if (ce != 0ull) {
       int r = 0;
-      for (int i = 0; i < nc; ++i) r += ck[i] > ce;
+      const ulonglong2 *c2 = reinterpret_cast<const ulonglong2 *>(ck);
+      for (int i = 0; i < nc / 2; ++i) {  // two candidates per LDS read
+        const ulonglong2 q = c2[i];
+        r += (q.x > ce) + (q.y > ce);
+      }
+      if (nc & 1) r += ck[nc - 1] > ce;
       if (r < k) {
         const uint32_t mono = (uint32_t)(ce >> 32);
         top_v[r] = __uint_as_float((mono & 0x80000000u) ? (mono & 0x7fffffffu) : ~mono);
