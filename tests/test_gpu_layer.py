@@ -123,6 +123,14 @@ def test_real_layer_decode_T28_zipf():
     layer.close()
 
 
+def test_real_layer_decode_T40_zipf():
+    # past the K-split range (up to 32 tokens): the unsplit gate/up kernel at
+    # the real width, and the router's third 16-token group
+    layer = _layer(T=40, alpha=0.75, **REAL)
+    _check_layer(layer, B.MOE_PATH_DECODE, "fp16_weights", 1e-4)
+    layer.close()
+
+
 def test_real_layer_prefill_small():
     layer = _layer(T=200, alpha=0.75, **REAL)
     _check_layer(layer, B.MOE_PATH_PREFILL, "fp16_operands", TOL)
