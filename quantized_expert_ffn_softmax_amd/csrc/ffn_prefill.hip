@@ -103,6 +103,13 @@ __host__ __device__ inline int slot_col(int s) {
   const int S = s / moe::kSbCols, r = s - S * moe::kSbCols, p = r >> 1;
   return S * moe::kSbCols + 10 * (p / 5) + p % 5 + 5 * (r & 1);
 }
+// 1 / f of K slot s: the weights of a pair whose codes sit at slot j = p % 5
+// of their word reach the MFMA multiplied by f = 1, 8 or 64 (j mod 3), so the
+// activations in that slot are stored divided by f (exact powers of two)
+__host__ __device__ inline float slot_inv_f(int s) {
+  const int j = ((s % moe::kSbCols) >> 1) % 5 % 3;
+  return j == 0 ? 1.0f : (j == 1 ? 0.125f : 0.015625f);
+}
 
 __device__ inline f4 mfma32(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 __device__ inline f4 mfma16(h4 a, h4 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0); }
@@ -160,9 +167,9 @@ __device__ inline void make_sel(int hh, int u, PairSel &P) {
 
 // Dequantise the thread's 20 code pairs into 40 consecutive K slots (80 B).
 // Per pair: one v_and_or_b32 (fp16 1024 + f q), one v_pk_add (- (1024 + 4 f),
-// exact), one v_pk_mul by 1/f (exact), one v_perm_b32 (the pair's scales),
-// one v_pk_mul by them (one rounding: fp16((q - 4) s), the oracle's fp16
-// reading).
+// exact: f (q - 4)), one v_perm_b32 (the pair's scales), one v_pk_mul by them
+// (one rounding: f fp16((q - 4) s), f a power of two); the activations of the
+// slot carry 1 / f.
 __device__ inline void deq_w(const WRaw &r, const PairSel &P, const PConsts &K, _Float16 *dst) {
   h2 out[20];
 #pragma unroll
@@ -175,9 +182,8 @@ __device__ inline void deq_w(const WRaw &r, const PairSel &P, const PConsts &K, 
       const float f = jj == 0 ? 1.0f : (jj == 1 ? 8.0f : 64.0f);
       const h2 v = __builtin_bit_cast(h2, (src & K.mask[jj]) | K.magic);
       const h2 o = {(_Float16)(1024.0f + 4.0f * f), (_Float16)(1024.0f + 4.0f * f)};
-      const h2 inv = {(_Float16)(1.0f / f), (_Float16)(1.0f / f)};
       const h2 sc = __builtin_bit_cast(h2, __builtin_amdgcn_perm(r.s1, r.s0, P.sel[5 * a + j]));
-      out[5 * a + j] = ((v - o) * inv) * sc;
+      out[5 * a + j] = (v - o) * sc;
     }
   }
 #pragma unroll
@@ -331,7 +337,18 @@ __global__ void __launch_bounds__(256, kNBuf == 1 ? 3 : 2) prefill_kernel(Prefil
     prefill_step<b1, kNBuf>(s + 1, nsteps, xact, xv0, xv1, xv2, xv3, xv4, xs[b1][xr] + 40 * xh, wr, sel1, K,
                             ws[b1][brow] + 40 * u, W, u, xsrc, xh, ws[b1], xs[b1], bro, r16, g, wm, mt_active, acc);
   }
-  // D: lane holds tokens 4 g + i of the M tile for column r16 of the N tile
+  // D: lane holds tokens 4 g + i of the M tile for column r16 of the N tile.
+  // gate/up: the lane's two h columns, their K slots in the down record and
+  // the 1 / f they are stored with
+  int hsl[2] = {0, 0};
+  float hinv[2] = {1.0f, 1.0f};
+  if constexpr (NMAT == 2) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      hsl[nb] = pair_slot(nt * (kPN / 2) + 32 * wn + 16 * nb + r16);
+      hinv[nb] = slot_inv_f(hsl[nb]);
+    }
+  }
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -343,11 +360,11 @@ __global__ void __launch_bounds__(256, kNBuf == 1 ? 3 : 2) prefill_kernel(Prefil
       if constexpr (NMAT == 2) {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
-          const int col = nt * (kPN / 2) + 32 * wn + 16 * nb + r16;
           const float gv = acc[mt][nb][i], uv = acc[mt][nb + 2][i];
-          // h is rounded to fp16 here, so the division is kept exact
+          // h is rounded to fp16 here, so the division is kept exact; stored
+          // divided by the f of its K slot in the down weights
           const float h = gv / (1.0f + __expf(-gv)) * uv;
-          P.h16[(size_t)hrow * P.kp_ff + pair_slot(col)] = (_Float16)h;
+          P.h16[(size_t)hrow * P.kp_ff + hsl[nb]] = (_Float16)(h * hinv[nb]);
         }
       } else {
         float *y = we.expert >= 0 ? P.y_pairs + (size_t)hrow * P.d_model : P.y_shared + (size_t)tok_sh[mm] * P.d_model;
@@ -360,14 +377,15 @@ __global__ void __launch_bounds__(256, kNBuf == 1 ? 3 : 2) prefill_kernel(Prefil
     }
 }
 
-// x [T][d] fp32 -> fp16 in pair order, rows of kp slots (zero past column d)
+// x [T][d] fp32 -> fp16 in pair order, rows of kp slots (zero past column d),
+// each value divided by the f of its slot
 __global__ void __launch_bounds__(256) to_fp16_pairs_kernel(const float *__restrict__ x, int T, int d, int kp,
                                                             _Float16 *__restrict__ y) {
   const size_t n = (size_t)T * kp;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
     const int t = (int)(i / kp), sl = (int)(i - (size_t)t * kp);
     const int c = slot_col(sl);
-    y[i] = c < d ? (_Float16)x[(size_t)t * d + c] : (_Float16)0.f;
+    y[i] = c < d ? (_Float16)(x[(size_t)t * d + c] * slot_inv_f(sl)) : (_Float16)0.f;
   }
 }
 
