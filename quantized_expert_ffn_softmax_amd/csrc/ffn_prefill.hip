@@ -143,34 +143,25 @@ struct PConsts {
   uint32_t magic;    // fp16 1024 in both halves
 };
 
-// Byte selectors for v_perm_b32(s1, s0, sel): which of the thread's two scale
-// blocks each half of code pair (a, j) uses.  With c0 = 80 hh + 20 u the
-// superblock-relative column of the thread's first code, column c0 + lc uses
-// the second block when lc >= 32 (c0 / 32 + 1) - c0.
-struct PairSel {
-  uint32_t sel[20];
-};
-
-__device__ inline void make_sel(int hh, int u, PairSel &P) {
-  const int c0 = 80 * hh + 40 * u;
-  const int thr = (c0 / 32 + 1) * 32 - c0;
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int j = 0; j < 5; ++j) {
-      const int lc = 10 * a + j;
-      const uint32_t lo = lc >= thr ? 0x0504u : 0x0100u;      // bytes of s1 (src0) or s0 (src1)
-      const uint32_t hi = lc + 5 >= thr ? 0x0504u : 0x0100u;
-      P.sel[5 * a + j] = lo | (hi << 16);
-    }
+// Which of the thread's two scale blocks each half of code pair (a, j) uses:
+// with c0 = 80 hh + 40 u the superblock-relative column of the thread's
+// first code, column c0 + lc uses the second block when lc >= thr(hh, u) =
+// 32 (c0 / 32 + 1) - c0 (32, 24, 16, 8).  hh (step parity) and u (the wave's
+// word quad) are compile-time below, so each pair's scales come from one
+// packed register through op_sel, with no per-pair byte permute.
+__host__ __device__ constexpr int scale_thr(int hh, int u) {
+  return ((80 * hh + 40 * u) / 32 + 1) * 32 - (80 * hh + 40 * u);
 }
 
 // Dequantise the thread's 20 code pairs into 40 consecutive K slots (80 B).
 // Per pair: one v_and_or_b32 (fp16 1024 + f q), one v_pk_add (- (1024 + 4 f),
-// exact: f (q - 4)), one v_perm_b32 (the pair's scales), one v_pk_mul by them
-// (one rounding: f fp16((q - 4) s), f a power of two); the activations of the
-// slot carry 1 / f.
-__device__ inline void deq_w(const WRaw &r, const PairSel &P, const PConsts &K, _Float16 *dst) {
+// exact: f (q - 4)), one v_pk_mul by the pair's scales, taken from the packed
+// (s0, s1) by op_sel (one rounding: f fp16((q - 4) s), f a power of two); the
+// activations of the slot carry 1 / f.
+template <int HH, int U>
+__device__ inline void deq_w(const WRaw &r, const PConsts &K, _Float16 *dst) {
+  constexpr int thr = scale_thr(HH, U);
+  const h2 S = __builtin_bit_cast(h2, (r.s0 & 0xffffu) | (r.s1 << 16));
   h2 out[20];
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
@@ -182,7 +173,8 @@ __device__ inline void deq_w(const WRaw &r, const PairSel &P, const PConsts &K, 
       const float f = jj == 0 ? 1.0f : (jj == 1 ? 8.0f : 64.0f);
       const h2 v = __builtin_bit_cast(h2, (src & K.mask[jj]) | K.magic);
       const h2 o = {(_Float16)(1024.0f + 4.0f * f), (_Float16)(1024.0f + 4.0f * f)};
-      const h2 sc = __builtin_bit_cast(h2, __builtin_amdgcn_perm(r.s1, r.s0, P.sel[5 * a + j]));
+      const int lc = 10 * a + j;
+      const h2 sc = {lc >= thr ? S[1] : S[0], lc + 5 >= thr ? S[1] : S[0]};
       out[5 * a + j] = (v - o) * sc;
     }
   }
@@ -197,9 +189,9 @@ __device__ inline void deq_w(const WRaw &r, const PairSel &P, const PConsts &K, 
 // One K step: (with one buffer: wait until every wave has read the previous
 // step) store the prefetched activations and dequantised weights into buffer
 // B, request step s + 1, barrier, then the wave's MFMAs on buffer B.
-template <int B, int NBUF>
+template <int B, int NBUF, int HH>
 __device__ inline void prefill_step(int s, int nsteps, bool xact, uint4 &xv0, uint4 &xv1, uint4 &xv2, uint4 &xv3,
-                                    uint4 &xv4, _Float16 *xdst, WRaw &wr, const PairSel &sel, const PConsts &K,
+                                    uint4 &xv4, _Float16 *xdst, WRaw &wr, const PConsts &K,
                                     _Float16 *wdst, const WSrc &W, int u, const _Float16 *xsrc, int xh,
                                     const _Float16 (*wsb)[kPld], const _Float16 (*xsb)[kPld], const int (&bro)[4],
                                     int r16, int g, int wm, int mt_active, f4 (&acc)[4][4]) {
@@ -212,7 +204,10 @@ __device__ inline void prefill_step(int s, int nsteps, bool xact, uint4 &xv0, ui
     dst[3] = xv3;
     dst[4] = xv4;
   }
-  deq_w(wr, sel, K, wdst);
+  if (u == 0)  // u is wave-uniform
+    deq_w<HH, 0>(wr, K, wdst);
+  else
+    deq_w<HH, 1>(wr, K, wdst);
   if (s + 1 < nsteps) {
     if (xact) {
       const uint4 *src = reinterpret_cast<const uint4 *>(xsrc + (s + 1) * kPK + 40 * xh);
@@ -294,9 +289,6 @@ __global__ void __launch_bounds__(256, kNBuf == 1 ? 3 : 2) prefill_kernel(Prefil
     W.scales = blob + M.scale_off + (size_t)wrow * M.nblk * 2;
     W.nblk = M.nblk;
   }
-  PairSel sel0, sel1;  // even and odd steps
-  make_sel(0, u, sel0);
-  make_sel(1, u, sel1);
   PConsts K;
   K.mask[0] = 0x00070007u;
   K.mask[1] = 0x00380038u;
@@ -329,13 +321,13 @@ __global__ void __launch_bounds__(256, kNBuf == 1 ? 3 : 2) prefill_kernel(Prefil
     xv4 = src[4];
   }
   load_w(W, 0, u, wr);
-  // steps come in (even, odd) pairs: buffer and scale selectors are static
+  // steps come in (even, odd) pairs: buffer and scale classes are static
   for (int s = 0; s < nsteps; s += 2) {
     constexpr int b1 = kNBuf - 1;
-    prefill_step<0, kNBuf>(s, nsteps, xact, xv0, xv1, xv2, xv3, xv4, xs[0][xr] + 40 * xh, wr, sel0, K,
-                           ws[0][brow] + 40 * u, W, u, xsrc, xh, ws[0], xs[0], bro, r16, g, wm, mt_active, acc);
-    prefill_step<b1, kNBuf>(s + 1, nsteps, xact, xv0, xv1, xv2, xv3, xv4, xs[b1][xr] + 40 * xh, wr, sel1, K,
-                            ws[b1][brow] + 40 * u, W, u, xsrc, xh, ws[b1], xs[b1], bro, r16, g, wm, mt_active, acc);
+    prefill_step<0, kNBuf, 0>(s, nsteps, xact, xv0, xv1, xv2, xv3, xv4, xs[0][xr] + 40 * xh, wr, K,
+                              ws[0][brow] + 40 * u, W, u, xsrc, xh, ws[0], xs[0], bro, r16, g, wm, mt_active, acc);
+    prefill_step<b1, kNBuf, 1>(s + 1, nsteps, xact, xv0, xv1, xv2, xv3, xv4, xs[b1][xr] + 40 * xh, wr, K,
+                               ws[b1][brow] + 40 * u, W, u, xsrc, xh, ws[b1], xs[b1], bro, r16, g, wm, mt_active, acc);
   }
   // D: lane holds tokens 4 g + i of the M tile for column r16 of the N tile.
   // gate/up: the lane's two h columns, their K slots in the down record and
