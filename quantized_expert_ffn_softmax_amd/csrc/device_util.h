@@ -40,6 +40,8 @@ __device__ inline int block_excl_scan_1024(int v, int *total, int *sh /* >= 17 i
 // round trips): shifts by 1, 2, 4 and 8 inside each 16-lane row, then the
 // row totals carried across rows by the row_bcast:15 and row_bcast:31
 // broadcasts.  Lanes a move does not reach keep the 0 passed as `old`.
+// Every lane of the wave must be active (a DPP move reads inactive lanes'
+// stale registers): call it outside divergent branches.
 __device__ inline int wave_incl_scan(int v) {
   v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
   v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
@@ -57,6 +59,7 @@ __device__ inline float dpp_move(float x) {
 
 // Sum of one float per lane over a wave64, in the same DPP moves as
 // wave_incl_scan (a fixed tree order); the total is returned to every lane.
+// Every lane of the wave must be active, as for wave_incl_scan.
 __device__ inline float wave_sum(float v) {
   v += dpp_move<0x111, 0xf>(v);  // row_shr:1
   v += dpp_move<0x112, 0xf>(v);  // row_shr:2
