@@ -33,9 +33,16 @@ project's design notes):
   and is added after the k routed terms, taken in ascending j;
 * cache: LRU with the tie rules documented on ``LRUCache``;
 * precision: 'exact' is float64 on the exactly dequantised weights; the two
-  reduced modes model where the GPU paths round operands to fp16
-  ('fp16_weights': W rounded; 'fp16_operands': x, W and h rounded), with all
-  arithmetic after the rounding still in float64.
+  reduced modes model where the GPU paths round operands to fp16, with all
+  arithmetic after the rounding still in float64:
+  'fp16_weights' rounds every dequantised weight (q - 4) * s once to fp16
+  (round to nearest, ties to even) -- the decode path;
+  'fp16_wh' also rounds h = silu(g) * u once to fp16, straight from its
+  float64 value -- the prefill path, which keeps x at fp32 accuracy.
+  Both are pinned on the CPU against hand-worked values (the fp16 rounding
+  written out from its definition, sums in exact rationals), against the
+  exact mode where every operand is representable, and against a tie case of
+  the rounding in each direction.
 """
 from __future__ import annotations
 
@@ -292,25 +299,30 @@ def silu(z: np.ndarray) -> np.ndarray:
     return z / (1.0 + np.exp(-z))
 
 
+PRECISIONS = ("exact", "fp16_weights", "fp16_wh")
+
+
 def _f16(a: np.ndarray) -> np.ndarray:
-    return np.asarray(a).astype(np.float16).astype(np.float64)
+    """Round float64 values once to fp16 (nearest, ties to even) and back."""
+    return np.asarray(a, dtype=np.float64).astype(np.float16).astype(np.float64)
 
 
 def expert_ffn(x_rows: np.ndarray, weights, precision: str = "exact") -> np.ndarray:
     """y[t] = W_d (silu(W_g x_t) * W_u x_t) for every row of x_rows.
 
     ``weights`` are the float64 matrices from ``expert_weights`` (already
-    fp16-rounded for the reduced modes).  'fp16_operands' also rounds x and h.
+    fp16-rounded for the reduced modes).  'fp16_wh' also rounds h once to
+    fp16 from its float64 value; x is never rounded.
     """
+    if precision not in PRECISIONS:
+        raise ValueError(f"unknown precision {precision!r}")
     wg, wu, wd = weights
     x = np.asarray(x_rows, dtype=np.float64)
-    if precision == "fp16_operands":
-        x = _f16(np.asarray(x_rows, dtype=np.float32))
     g = x @ wg.T
     u = x @ wu.T
     h = silu(g) * u
-    if precision == "fp16_operands":
-        h = _f16(h.astype(np.float32))
+    if precision == "fp16_wh":
+        h = _f16(h)
     return h @ wd.T
 
 
