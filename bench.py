@@ -10,8 +10,11 @@ moe_expert_ffn (decode path) -> moe_combine_norm (moe_combine and the
 stacking normalisation moe_chain_norm in one kernel; it feeds the next
 layer).  Inputs are synthetic and seeded; weights are random.
 
-Also timed: the prefill chunk (12,288 tokens through one layer, prefill path),
-and the CPU oracle on a bounded sample of the decode workload.
+Also timed: measured HBM-read and fp16-MFMA peaks of the device, the prefill
+chunk (12,288 tokens through one layer, prefill path), a single layer at
+5 tokens, the speculative-verify sweep, the 1-token stack through the
+8,445-slot LRU cache, and the CPU oracle on bounded samples of the decode and
+prefill workloads.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -72,6 +75,9 @@ def main():
     ap.add_argument("--no-layer", action="store_true", help="skip the single-layer T=5 decode measurement")
     ap.add_argument("--no-lru", action="store_true", help="skip the T=1 stack through the 8,445-slot LRU cache")
     ap.add_argument("--no-sweep", action="store_true", help="skip the speculative-verify batch sweep")
+    ap.add_argument("--no-stack", action="store_true",
+                    help="skip the 48-layer decode stack (the headline figure is then null; for profiling other legs)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured HBM-read and MFMA-loop peaks")
     ap.add_argument("--lru-steps", type=int, default=256)
     ap.add_argument("--lru-warmup", type=int, default=64)
     args = ap.parse_args()
@@ -80,7 +86,6 @@ def main():
               "the multi-GPU layout is described in DESIGN.md", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import moe_synth
@@ -99,26 +104,123 @@ def main():
     prefill_T = moe_synth.WORKLOADS["prefill_chunk"]["n_tokens"]
 
     t0 = time.time()
-    log(f"[bench] allocating {L * E} + {L} blobs x {stride} B in HBM")
+    # the stack and the sweep need all 48 layers; the other legs use layer 0
+    L_gen = L if not (args.no_stack and args.no_sweep) else 1
+    log(f"[bench] allocating {L * E} + {L} blobs x {stride} B in HBM (generating {L_gen} layer(s))")
     slot_pool = torch.empty((L * E, stride), dtype=torch.uint8, device="cuda")
     shared_pool = torch.empty((L, stride), dtype=torch.uint8, device="cuda")
-    for l0 in range(0, L, 8):
-        fill_pool(slot_pool[l0 * E:(l0 + 8) * E], list(range(l0 * E, (l0 + 8) * E)), seed, d, f, E, chunk=512)
-        log(f"[bench] generated layers {l0}..{l0 + 7} ({time.time() - t0:.0f}s)")
+    for l0 in range(0, L_gen, 8):
+        l1 = min(l0 + 8, L_gen)
+        fill_pool(slot_pool[l0 * E:l1 * E], list(range(l0 * E, l1 * E)), seed, d, f, E, chunk=512)
+        log(f"[bench] generated layers {l0}..{l1 - 1} ({time.time() - t0:.0f}s)")
     fill_pool(shared_pool, [(l, E) for l in range(L)], seed, d, f, E)
     routers = torch.stack([torch.from_numpy(moe_synth.gen_router(seed, l, E, d)) for l in range(L)]).cuda()
     biases = torch.stack([torch.from_numpy(moe_synth.gen_bias(seed, l, E, alpha)) for l in range(L)]).cuda()
     max_tokens = max(T, prefill_T)
     ctx = MoeContext(d, f, E, k, L, None, max_tokens, slot_pool=slot_pool, shared_pool=shared_pool)
-    W, K = args.warmup, args.steps
+    torch.cuda.synchronize()
+    log(f"[bench] setup {time.time() - t0:.0f}s")
+
+    peaks = None if args.no_peaks else measure_peaks(slot_pool)
+    result = {
+        "metric": "MoE decode tok/s (48 layers) + prefill tok/s; % of HBM BW / MFMA peak",
+        "value": None,
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": None,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "batched_decode_stack", "layers": L, "experts_per_layer": E, "top_k": k,
+                   "shared_experts": 1, "tokens_per_step": T, "d_model": d, "d_ff": f,
+                   "resident_identities": L * E, "zipf_alpha": alpha, "expert_blob_bytes": stride,
+                   "seed": seed},
+    }
+    if peaks is not None:
+        result["measured_peaks"] = peaks
+    if not args.no_stack:
+        result.update(bench_stack(ctx, routers, biases, seed, d, f, L, T, args.warmup, args.steps,
+                                  not args.no_graph, peaks))
+    if not args.no_prefill:
+        result["prefill"] = bench_prefill(ctx, routers[0], biases[0], seed, d, f, k, prefill_T, args.prefill_reps,
+                                          peaks)
+    if not args.no_sweep:
+        result["verify_sweep"] = verify_sweep(ctx, routers, biases, seed, d, f, L)
+    if not args.no_layer:
+        result["decode_layer"] = bench_decode_layer(ctx, routers[0], seed, d, f, E, k)
+    ctx.close()
+    del ctx, slot_pool
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if not args.no_lru:
+        result["decode_lru"] = bench_lru(seed, d, f, E, k, L, routers, biases, shared_pool, args.lru_warmup,
+                                         args.lru_steps)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(seed, d, f, E, k, T, alpha, args.cpu_sample_layers, args.warmup,
+                                              prefill_T)
+    print(json.dumps(result), flush=True)
+
+
+def _median_ms(pairs):
+    import numpy as np
+    return float(np.median([a.elapsed_time(b) for a, b in pairs]))
+
+
+def measure_peaks(buf, read_bytes=4 << 30, reps=5):
+    """Achievable peaks on this device: a streaming read of `read_bytes` of the
+    (already filled) expert pool, and a loop of independent fp16 MFMAs
+    (v_mfma_f32_16x16x32_f16, the instruction of the FFN kernels).  Median of
+    `reps` timed launches after one warm-up each."""
+    import torch
+
+    from quantized_expert_ffn_softmax_amd import binding as B
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    flat = buf.view(-1)
+    nbytes = min(read_bytes, flat.numel()) // 16 * 16
+    sink = torch.empty(1 << 20, dtype=torch.int32, device="cuda")
+    blocks = n_cu * 8
+    ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(reps + 1)]
+    for a, b in ev:
+        a.record()
+        B.moe_peak_hbm_read(flat, nbytes, sink, blocks)
+        b.record()
+    torch.cuda.synchronize()
+    hbm_ms = _median_ms(ev[1:])
+    iters, mblocks = 4096, n_cu * 2
+    flops = mblocks * 4 * iters * 8 * 16384.0
+    for a, b in ev:
+        a.record()
+        B.moe_peak_mfma_f16(iters, mblocks, sink)
+        b.record()
+    torch.cuda.synchronize()
+    mfma_ms = _median_ms(ev[1:])
+    out = {"hbm_read_gbs": round(nbytes / (hbm_ms * 1e-3) / 1e9, 1), "hbm_read_bytes": nbytes,
+           "hbm_frac_of_spec": round(nbytes / (hbm_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "mfma_f16_tflops": round(flops / (mfma_ms * 1e-3) / 1e12, 1),
+           "mfma_frac_of_spec": round(flops / (mfma_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+           "how": f"moe_peak_hbm_read over {nbytes >> 20} MiB ({blocks} workgroups); moe_peak_mfma_f16 "
+                  f"{mblocks} x 4 waves x {iters} x 8 v_mfma_f32_16x16x32_f16; median of {reps} launches"}
+    log(f"[bench] measured peaks: HBM read {out['hbm_read_gbs']} GB/s, fp16 MFMA {out['mfma_f16_tflops']} TFLOP/s")
+    return out
+
+
+def bench_stack(ctx, routers, biases, seed, d, f, L, T, W, K, use_graph, peaks):
+    """The headline: the 48-layer batched-decode stack, eager with HIP events
+    around every moe_expert_ffn call, then captured in a HIP graph."""
+    import numpy as np
+    import torch
+
+    import moe_synth
+    from quantized_expert_ffn_softmax_amd import binding as B
+    c = ctx.ctx
     xs = [torch.from_numpy(moe_synth.gen_x(seed, s, T, d)).cuda() for s in range(W + K)]
     buf = ctx.buffers(T)
     xa = torch.empty((T, d), dtype=torch.float32, device="cuda")
     xb = torch.empty_like(xa)
-    torch.cuda.synchronize()
-    log(f"[bench] setup {time.time() - t0:.0f}s")
-
-    c = ctx.ctx
 
     def step(x0, ev=None):
         x = x0
@@ -165,7 +267,7 @@ def main():
     # the same step captured once in a HIP graph (the deployable form of a
     # fixed-shape decode step), replayed on fresh inputs copied in beforehand
     graph_ms = None
-    if not args.no_graph:
+    if use_graph:
         xin = torch.empty((T, d), dtype=torch.float32, device="cuda")
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
@@ -193,89 +295,67 @@ def main():
         del graph
         log(f"[bench] decode stack (graph): {graph_ms:.3f} ms/step, {T / (graph_ms * 1e-3):.0f} tok/s")
     ms_per_step = graph_ms if graph_ms is not None else eager_ms
-    value = T / (ms_per_step * 1e-3)
+    roof = {"bound": "hbm", "kernel": "moe_expert_ffn (decode path)",
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "bytes_per_launch": round(bytes_per_call), "avg_launch_us": round(ffn_avg_ms * 1e3, 2),
+            "distinct_experts_per_layer": round(uniq / calls, 2),
+            "measured_in": "eager timed region (HIP events around each moe_expert_ffn call)",
+            "stack_bytes_per_step": round(ffn_bytes_total / K),
+            "stack_frac": round(ffn_bytes_total / K / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    if peaks is not None:
+        roof["measured_peak"] = peaks["hbm_read_gbs"]
+        roof["frac_of_measured"] = round(achieved / peaks["hbm_read_gbs"], 4)
+    return {"value": round(T / (ms_per_step * 1e-3), 1), "ms_per_step": round(ms_per_step, 4), "roofline": roof,
+            "eager_ms_per_step": round(eager_ms, 4), "step_mode": "hip_graph" if graph_ms is not None else "eager"}
 
-    sweep = None if args.no_sweep else verify_sweep(ctx, routers, biases, seed, d, f, L)
 
-    result = {
-        "metric": "MoE decode tok/s (48 layers) + prefill tok/s; % of HBM BW / MFMA peak",
-        "value": round(value, 1),
-        "unit": "tok/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": W,
-        "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f16",
-        "data": "synthetic",
-        "config": {"workload": "batched_decode_stack", "layers": L, "experts_per_layer": E, "top_k": k,
-                   "shared_experts": 1, "tokens_per_step": T, "d_model": d, "d_ff": f,
-                   "resident_identities": L * E, "zipf_alpha": alpha, "expert_blob_bytes": stride,
-                   "seed": seed},
-        "roofline": {"bound": "hbm", "kernel": "moe_expert_ffn (decode path)",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
-                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                     "bytes_per_launch": round(bytes_per_call), "avg_launch_us": round(ffn_avg_ms * 1e3, 2),
-                     "distinct_experts_per_layer": round(uniq / calls, 2),
-                     "measured_in": "eager timed region (HIP events around each moe_expert_ffn call)",
-                     "stack_bytes_per_step": round(ffn_bytes_total / K),
-                     "stack_frac": round(ffn_bytes_total / K / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
-        "eager_ms_per_step": round(eager_ms, 4),
-        "step_mode": "hip_graph" if graph_ms is not None else "eager",
-    }
+def bench_prefill(ctx, router, bias, seed, d, f, k, T, reps, peaks):
+    """The prefill chunk: T tokens through one real layer (route, resolve,
+    expert FFN on the prefill path, combine); medians over `reps` after one
+    warm-up."""
+    import numpy as np
+    import torch
 
-    if not args.no_prefill:
-        xp = torch.from_numpy(moe_synth.gen_x(seed, 100000, prefill_T, d)).cuda()
-        pbuf = ctx.buffers(prefill_T)
-        pev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.prefill_reps + 1)]
-        for r in range(args.prefill_reps + 1):
-            e = pev[r]
-            e[0].record()
-            B.moe_route(c, 0, xp, prefill_T, routers[0], biases[0], None, pbuf["idx"], pbuf["w"])
-            B.moe_cache_resolve(c, 0, pbuf["idx"], prefill_T, None)
-            e[1].record()
-            B.moe_expert_ffn(c, 0, xp, prefill_T, pbuf["idx"], None, pbuf["y_pairs"], pbuf["y_shared"],
-                             B.MOE_PATH_PREFILL)
-            e[2].record()
-            B.moe_combine(c, pbuf["y_pairs"], pbuf["w"], pbuf["y_shared"], prefill_T, pbuf["out"])
-            e[3].record()
-        torch.cuda.synchronize()
-        layer_ms = float(np.median([pev[r][0].elapsed_time(pev[r][3]) for r in range(1, args.prefill_reps + 1)]))
-        ffn_p_ms = float(np.median([pev[r][1].elapsed_time(pev[r][2]) for r in range(1, args.prefill_reps + 1)]))
-        flops = 6.0 * d * f * (prefill_T * k + prefill_T)
-        tflops = flops / (ffn_p_ms * 1e-3) / 1e12
-        result["prefill"] = {"workload": "prefill_chunk", "tokens": prefill_T, "tok_per_s": round(prefill_T / (layer_ms * 1e-3), 1),
-                             "layer_ms": round(layer_ms, 4), "ffn_ms": round(ffn_p_ms, 4),
-                             "roofline": {"bound": "mfma", "kernel": "moe_expert_ffn (prefill path)",
-                                          "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
-                                          "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
-                                          "flops_per_launch": flops}}
-        log(f"[bench] prefill chunk: layer {layer_ms:.2f} ms ({prefill_T / (layer_ms * 1e-3):.0f} tok/s), "
-            f"FFN {ffn_p_ms:.2f} ms = {tflops:.1f} TFLOP/s")
-
-    if sweep is not None:
-        result["verify_sweep"] = sweep
-    if not args.no_layer:
-        result["decode_layer"] = bench_decode_layer(ctx, routers[0], seed, d, f, E, k)
-    cpu_x = xs[W].cpu().numpy()
-    ctx.close()
-    del ctx, slot_pool, buf, xs
+    import moe_synth
+    from quantized_expert_ffn_softmax_amd import binding as B
+    c = ctx.ctx
+    xp = torch.from_numpy(moe_synth.gen_x(seed, 100000, T, d)).cuda()
+    pbuf = ctx.buffers(T)
+    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps + 1)]
+    for r in range(reps + 1):
+        e = pev[r]
+        e[0].record()
+        B.moe_route(c, 0, xp, T, router, bias, None, pbuf["idx"], pbuf["w"])
+        B.moe_cache_resolve(c, 0, pbuf["idx"], T, None)
+        e[1].record()
+        B.moe_expert_ffn(c, 0, xp, T, pbuf["idx"], None, pbuf["y_pairs"], pbuf["y_shared"], B.MOE_PATH_PREFILL)
+        e[2].record()
+        B.moe_combine(c, pbuf["y_pairs"], pbuf["w"], pbuf["y_shared"], T, pbuf["out"])
+        e[3].record()
     torch.cuda.synchronize()
-    torch.cuda.empty_cache()
-    if not args.no_lru:
-        result["decode_lru"] = bench_lru(seed, d, f, E, k, L, routers, biases, shared_pool, args.lru_warmup,
-                                         args.lru_steps)
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(seed, d, f, E, k, T, alpha, cpu_x, args.cpu_sample_layers)
-    print(json.dumps(result), flush=True)
+    layer_ms = float(np.median([pev[r][0].elapsed_time(pev[r][3]) for r in range(1, reps + 1)]))
+    ffn_p_ms = float(np.median([pev[r][1].elapsed_time(pev[r][2]) for r in range(1, reps + 1)]))
+    flops = 6.0 * d * f * (T * k + T)
+    tflops = flops / (ffn_p_ms * 1e-3) / 1e12
+    roof = {"bound": "mfma", "kernel": "moe_expert_ffn (prefill path)",
+            "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+            "flops_per_launch": flops}
+    if peaks is not None:
+        roof["measured_peak"] = peaks["mfma_f16_tflops"]
+        roof["frac_of_measured"] = round(tflops / peaks["mfma_f16_tflops"], 4)
+    log(f"[bench] prefill chunk: layer {layer_ms:.2f} ms ({T / (layer_ms * 1e-3):.0f} tok/s), "
+        f"FFN {ffn_p_ms:.2f} ms = {tflops:.1f} TFLOP/s")
+    return {"workload": "prefill_chunk", "tokens": T, "tok_per_s": round(T / (layer_ms * 1e-3), 1),
+            "layer_ms": round(layer_ms, 4), "ffn_ms": round(ffn_p_ms, 4), "roofline": roof}
 
 
 def bench_decode_layer(ctx, router, seed, d, f, E, k, reps=200):
     """One real layer at T = 5 (one request: 1 + 4 draft tokens), no router
-    bias, a fresh x per repetition: route -> resolve -> expert FFN -> combine."""
+    bias, a fresh x per repetition and 1 GiB written between repetitions:
+    route -> resolve -> expert FFN -> combine."""
     import numpy as np
     import torch
 
@@ -287,11 +367,15 @@ def bench_decode_layer(ctx, router, seed, d, f, E, k, reps=200):
     xs = [torch.from_numpy(moe_synth.gen_x(seed, 200000 + r, T, d)).cuda() for r in range(reps + 10)]
     buf = ctx.buffers(T)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps + 10)]
+    # one real layer's ~107 MB of expert bytes fit in the 256 MB last-level
+    # cache: 1 GiB is written between repetitions (outside the timed events)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     st0 = None
     for r in range(reps + 10):
         if r == 10:
             torch.cuda.synchronize()
             st0 = B.moe_get_stats(c)
+        flush.fill_(r & 0xff)
         e = ev[r]
         e[0].record()
         B.moe_route(c, 0, xs[r], T, router, None, None, buf["idx"], buf["w"])
@@ -498,19 +582,24 @@ def verify_sweep(ctx, routers, biases, seed, d, f, L, reps=5, warm=2):
     return {"workload": "verify_sweep", "layers": L, "reps": reps, "rows": rows}
 
 
-def cpu_baseline(seed, d, f, E, k, T, alpha, x0, n_layers):
-    """The oracle, as it stands, on the first layers of one decode step."""
+def cpu_baseline(seed, d, f, E, k, T, alpha, n_layers, step, prefill_T, prefill_experts=24):
+    """The oracle, as it stands, on bounded samples of two workloads:
+    the first `n_layers` layers of one decode step of the stack (scaled to the
+    48 layers), and the prefill chunk with its router on every token and the
+    expert FFNs of a seeded sample of the experts that receive tokens (scaled
+    by the number of such experts)."""
     import numpy as np
 
     import moe_synth
     import oracle
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
-        cores = 1
+        blas_threads = None
+    cores = len(os.sched_getaffinity(0))
     L = moe_synth.WORKLOADS["batched_decode_stack"]["n_layers"]
-    x = x0
+    x = moe_synth.gen_x(seed, step, T, d)
     spent = 0.0
     for l in range(n_layers):
         wr = moe_synth.gen_router(seed, l, E, d)
@@ -522,11 +611,43 @@ def cpu_baseline(seed, d, f, E, k, T, alpha, x0, n_layers):
         r = oracle.moe_layer(x, wr, bias, k, lambda e: blobs[e], shared, d, f, precision="exact")
         spent += time.time() - t
         x = oracle.chain_norm(r["out64"])
-        log(f"[bench] cpu oracle layer {l}: {spent:.1f}s so far")
+        log(f"[bench] cpu oracle decode layer {l}: {spent:.1f}s so far")
     per_layer = spent / n_layers
-    return {"value": round(T / (per_layer * L), 3), "unit": "tok/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n_layers} of {L} layers of one {T}-token decode step (float64 numpy oracle, exact "
-                      f"precision), scaled to the 48-layer stack; {per_layer:.2f} s per layer"}
+    out = {"value": round(T / (per_layer * L), 3), "unit": "tok/s", "cores": cores, "blas_threads": blas_threads,
+           "kind": "oracle",
+           "sample": f"{n_layers} of {L} layers of one {T}-token decode step (float64 numpy oracle, exact "
+                     f"precision), scaled to the 48-layer stack; {per_layer:.2f} s per layer"}
+    # prefill chunk: route every token, then the FFNs of a sample of experts
+    xp = moe_synth.gen_x(seed, 100000, prefill_T, d)
+    wr = moe_synth.gen_router(seed, 0, E, d)
+    bias = moe_synth.gen_bias(seed, 0, E, alpha)
+    t = time.time()
+    _, idx, w = oracle.route(xp, wr, bias, k)
+    t_route = time.time() - t
+    flat = idx.reshape(-1)
+    used = np.unique(flat)
+    rng = np.random.default_rng(seed)
+    pick = rng.choice(used, size=min(prefill_experts, used.size), replace=False)
+    t_ffn, rows = 0.0, 0
+    for e in pick:
+        blob = moe_synth.gen_blob(seed, 0, int(e), d, f)
+        pairs = np.nonzero(flat == e)[0]
+        t = time.time()
+        oracle.expert_ffn(xp[pairs // k], oracle.expert_weights(blob, d, f), "exact")
+        t_ffn += time.time() - t
+        rows += pairs.size
+    shared = moe_synth.gen_blob(seed, 0, E, d, f)
+    t = time.time()
+    oracle.expert_ffn(xp, oracle.expert_weights(shared, d, f), "exact")
+    t_shared = time.time() - t
+    est = t_route + t_ffn * used.size / pick.size + t_shared
+    out["prefill"] = {"value": round(prefill_T / est, 2), "unit": "tok/s", "cores": cores, "kind": "oracle",
+                      "sample": f"prefill chunk of {prefill_T} tokens: router and top-k on every token "
+                                f"({t_route:.1f} s), shared expert on every token ({t_shared:.1f} s), expert FFNs "
+                                f"of {pick.size} of the {used.size} experts with tokens (seeded pick, {rows} pairs, "
+                                f"{t_ffn:.1f} s) scaled by {used.size}/{pick.size}; estimated {est:.1f} s per chunk"}
+    log(f"[bench] cpu oracle: decode {out['value']} tok/s, prefill {out['prefill']['value']} tok/s on {cores} cores")
+    return out
 
 
 if __name__ == "__main__":

@@ -204,6 +204,27 @@ moe_status moe_combine_norm(moe_ctx *ctx, const float *y_pairs, const float *w,
                             const float *y_shared, int32_t T, float *out, float *x_next,
                             void *stream);
 
+/* --- measurement support ------------------------------------------------
+ * Probes of what the device actually sustains, so that the layer's roofline
+ * fractions can be quoted against measured peaks beside the data-sheet ones
+ * (the pages print no figure for this hardware).  Both only enqueue one
+ * kernel on `stream`; the caller times it (e.g. with events around the call).
+ *
+ * moe_peak_hbm_read: n_blocks workgroups of 256 threads load every byte of
+ * buf[0, bytes) once with 16-byte loads (8 in flight per thread) and write
+ * nothing unless the data XOR to one fixed 32-bit value; sink
+ * [n_blocks] uint32 is scratch for that case.  buf and bytes must be
+ * multiples of 16 (MOE_ERR_ALIGN otherwise).  Use bytes well above the
+ * 256 MiB last-level cache so that the figure is HBM's.
+ *
+ * moe_peak_mfma_f16: n_blocks workgroups of 4 waves; every wave runs `iters`
+ * rounds of 8 independent v_mfma_f32_16x16x32_f16 on register operands, so
+ * one launch is n_blocks * 4 * iters * 8 * 16384 flops; sink [n_blocks]
+ * float is scratch (written only under a condition no run meets).
+ * Invalid arguments return MOE_ERR_INVALID and enqueue nothing. */
+moe_status moe_peak_hbm_read(const void *buf, uint64_t bytes, uint32_t *sink, int32_t n_blocks, void *stream);
+moe_status moe_peak_mfma_f16(int32_t iters, int32_t n_blocks, float *sink, void *stream);
+
 const char *moe_status_str(moe_status s);
 /* Detail of the last error on the calling thread ("" if none). */
 const char *moe_last_error(void);

@@ -32,17 +32,14 @@ project's design notes):
 * expert: y = W_d (silu(W_g x) * W_u x); the shared expert is ungated (weight 1)
   and is added after the k routed terms, taken in ascending j;
 * cache: LRU with the tie rules documented on ``LRUCache``;
-* precision: 'exact' is float64 on the exactly dequantised weights; the two
-  reduced modes model where the GPU paths round operands to fp16, with all
-  arithmetic after the rounding still in float64:
-  'fp16_weights' rounds every dequantised weight (q - 4) * s once to fp16
-  (round to nearest, ties to even) -- the decode path;
-  'fp16_wh' also rounds h = silu(g) * u once to fp16, straight from its
-  float64 value -- the prefill path, which keeps x at fp32 accuracy.
-  Both are pinned on the CPU against hand-worked values (the fp16 rounding
-  written out from its definition, sums in exact rationals), against the
-  exact mode where every operand is representable, and against a tie case of
-  the rounding in each direction.
+* precision: 'exact' is float64 on the exactly dequantised weights;
+  'fp16_weights' models where both GPU paths round: every dequantised weight
+  (q - 4) * s is rounded once to fp16 (round to nearest, ties to even), the
+  activations x and h are kept at fp32 accuracy, and all arithmetic after the
+  rounding is float64.  It is pinned on the CPU against hand-worked values
+  (the fp16 rounding written out from its definition, sums in exact
+  rationals), against the exact mode where every weight is representable, and
+  against a tie case of the rounding in each direction.
 """
 from __future__ import annotations
 
@@ -299,20 +296,14 @@ def silu(z: np.ndarray) -> np.ndarray:
     return z / (1.0 + np.exp(-z))
 
 
-PRECISIONS = ("exact", "fp16_weights", "fp16_wh")
-
-
-def _f16(a: np.ndarray) -> np.ndarray:
-    """Round float64 values once to fp16 (nearest, ties to even) and back."""
-    return np.asarray(a, dtype=np.float64).astype(np.float16).astype(np.float64)
+PRECISIONS = ("exact", "fp16_weights")
 
 
 def expert_ffn(x_rows: np.ndarray, weights, precision: str = "exact") -> np.ndarray:
     """y[t] = W_d (silu(W_g x_t) * W_u x_t) for every row of x_rows.
 
     ``weights`` are the float64 matrices from ``expert_weights`` (already
-    fp16-rounded for the reduced modes).  'fp16_wh' also rounds h once to
-    fp16 from its float64 value; x is never rounded.
+    fp16-rounded for 'fp16_weights'); x and h are never rounded.
     """
     if precision not in PRECISIONS:
         raise ValueError(f"unknown precision {precision!r}")
@@ -321,8 +312,6 @@ def expert_ffn(x_rows: np.ndarray, weights, precision: str = "exact") -> np.ndar
     g = x @ wg.T
     u = x @ wu.T
     h = silu(g) * u
-    if precision == "fp16_wh":
-        h = _f16(h)
     return h @ wd.T
 
 

@@ -78,6 +78,8 @@ _SIGS = {
     "moe_cache_reset": (_I, [_P]),
     "moe_get_stats": (_I, [_P, ctypes.POINTER(moe_resolve_info)]),
     "moe_chain_norm": (_I, [_P, _P, _I, _P, _P]),
+    "moe_peak_hbm_read": (_I, [_P, ctypes.c_uint64, _P, _I, _P]),
+    "moe_peak_mfma_f16": (_I, [_I, _I, _P, _P]),
     "moe_status_str": (ctypes.c_char_p, [_I]),
     "moe_last_error": (ctypes.c_char_p, []),
 }
@@ -224,3 +226,11 @@ def make_config(d_model, d_ff, n_experts, top_k, n_layers, n_slots, max_tokens, 
                 host_store=None) -> moe_config:
     return moe_config(d_model, d_ff, n_experts, top_k, n_layers, n_slots, max_tokens, _ptr(host_store),
                       _ptr(slot_pool), _ptr(shared_pool))
+
+
+def moe_peak_hbm_read(buf, nbytes, sink, n_blocks, stream=None):
+    _check(load().moe_peak_hbm_read(_ptr(buf), nbytes, _ptr(sink), n_blocks, _stream(stream)), "moe_peak_hbm_read")
+
+
+def moe_peak_mfma_f16(iters, n_blocks, sink, stream=None):
+    _check(load().moe_peak_mfma_f16(iters, n_blocks, _ptr(sink), _stream(stream)), "moe_peak_mfma_f16")

@@ -50,7 +50,7 @@ static hipError_t dalloc(T **p, size_t n) {
 static void free_ctx(moe_ctx *c) {
   if (!c) return;
   void *dev[] = {c->slot_of, c->id_of, c->stamp, c->dstats, c->logits_ws, c->offsets_ws, c->perm_ws,
-                 c->chunk_ws, c->work, c->n_work, c->xrec, c->hrec, c->x16, c->h16, c->tile_ws,
+                 c->chunk_ws, c->work, c->n_work, c->xrec, c->hrec, c->h16,
                  c->slot_ws, c->dmiss, c->route_part};
   for (void *p : dev)
     if (p) (void)hipFree(p);
@@ -91,11 +91,15 @@ extern "C" moe_status moe_create(const moe_config *cfg, moe_ctx **out) {
   c->resident = resident;
   c->host_dev = nullptr;
   hipError_t e = hipGetDevice(&c->device);
+  c->n_cu = 0;
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&c->n_cu, hipDeviceAttributeMultiprocessorCount, c->device);
+  if (c->n_cu < 1) c->n_cu = 1;
   c->max_pairs = k.max_tokens * k.top_k;
   c->max_work = c->max_pairs / moe::kEntryTokens + (c->max_pairs < k.n_experts ? c->max_pairs : k.n_experts) +
                 k.max_tokens / moe::kEntryTokens + 4;
   c->n_chunks_max = (c->max_pairs + 255) / 256;
   const int gsb = c->L.gate.nsb, dsb = c->L.down.nsb;
+  if (e == hipSuccess) e = moe::decode_occupancy(c);
   const int64_t hrows = (int64_t)c->max_pairs + k.max_tokens;
 #define TRY(x)                                                          \
   do {                                                                  \
@@ -116,11 +120,9 @@ extern "C" moe_status moe_create(const moe_config *cfg, moe_ctx **out) {
   const size_t hrec_n = (size_t)(hrows + 1) * moe::xrec_halves(dsb);
   TRY(dalloc(&c->xrec, xrec_n));
   TRY(dalloc(&c->hrec, hrec_n));
-  // prefill operands in pair order, rows padded to whole superblocks
-  TRY(dalloc(&c->x16, (size_t)k.max_tokens * gsb * moe::kSbCols));
-  TRY(dalloc(&c->h16, (size_t)hrows * dsb * moe::kSbCols));
-  c->max_tiles = (int)((hrows + 127) / 128 + k.n_experts + 2);
-  TRY(dalloc(&c->tile_ws, (size_t)c->max_tiles * 4 + 4));
+  // prefill h record: hi and lo halves, rows of whole superblocks (the x
+  // record shares xrec)
+  TRY(dalloc(&c->h16, (size_t)hrows * dsb * moe::kSbCols * 2));
   TRY(dalloc(&c->slot_ws, c->max_pairs));
   // decode-size router: about 256 workgroups in all, at least one 16-column
   // chunk per wave (8 waves per workgroup)
@@ -156,7 +158,7 @@ extern "C" moe_status moe_create(const moe_config *cfg, moe_ctx **out) {
   // record positions past a matrix's columns are never written: they stay zero
   TRY(hipMemset(c->xrec, 0, xrec_n * sizeof(uint16_t)));
   TRY(hipMemset(c->hrec, 0, hrec_n * sizeof(uint16_t)));
-  TRY(hipMemset(c->h16, 0, (size_t)hrows * dsb * moe::kSbCols * sizeof(uint16_t)));  // pad slots stay zero
+  TRY(hipMemset(c->h16, 0, (size_t)hrows * dsb * moe::kSbCols * 2 * sizeof(uint16_t)));  // pad slots stay zero
   TRY(hipDeviceSynchronize());
 #undef TRY
   if (e != hipSuccess) {

@@ -20,6 +20,7 @@
 #include <utility>
 
 #include "moe_internal.h"
+#include "dequant.h"
 #include "record.h"
 
 namespace {
@@ -60,37 +61,8 @@ __device__ inline const uint8_t *entry_blob(const DecodeParams &P, const moe::Wo
   return P.slot_pool + (size_t)slot * P.stride;
 }
 
-// Two weights of one packed word, times f (see record.h): the two 3-bit codes
-// of slot j sit at bits 3j' and 16 + 3j' of `src` (src = word for j < 3,
-// word >> 9 for j >= 3, j' = j mod 3); one v_and_or_b32 drops them into the
-// mantissas of fp16 1024 + f q; one v_pk_add takes 1024 + 4 f off (exact:
-// f (q - 4)); one v_pk_mul applies the block scales (one rounding, and the
-// product is f times fp16((q - 4) s) because f is a power of two).
-struct Consts {
-  uint32_t mask[3];  // 0x00070007 << 3 j', kept in VGPRs so v_and_or_b32 can be used
-  uint32_t magic;    // 0x64006400: fp16 1024 in both halves
-};
-
-__device__ inline Consts make_consts() {
-  Consts k;
-  k.mask[0] = 0x00070007u;
-  k.mask[1] = 0x00380038u;
-  k.mask[2] = 0x01c001c0u;
-  k.magic = 0x64006400u;
-  // opaque to the optimiser: stay in registers instead of becoming literals
-  asm volatile("" : "+v"(k.mask[0]), "+v"(k.mask[1]), "+v"(k.mask[2]), "+s"(k.magic));
-  return k;
-}
-
-template <int j>
-__device__ inline h2 deq_pair(uint32_t src, const Consts &K, h2 sc) {
-  constexpr int jj = j % 3;
-  const uint32_t u = (src & K.mask[jj]) | K.magic;
-  const h2 v = __builtin_bit_cast(h2, u);
-  constexpr float off = 1024.0f + 4.0f * (jj == 0 ? 1.0f : (jj == 1 ? 8.0f : 64.0f));
-  const h2 o = {(_Float16)off, (_Float16)off};
-  return (v - o) * sc;
-}
+using moe::Consts;
+using moe::make_consts;
 
 __device__ inline f4 mfma(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 
@@ -139,14 +111,8 @@ __device__ inline bool entry_token(const DecodeParams &P, const moe::WorkEntry &
 // is 5 MFMA steps: at step t the lane group supplies pairs 4t .. 4t+3 of its
 // quad, i.e. pairs 20g + 4t .. of the superblock, whose activations are
 // record step 5g + t.  B columns n < 4 hold token n's hi halves, n + 4 its lo
-// halves; columns 8..15 repeat 0..7 (their outputs are not used).
-//
-// The scale pair a code pair needs depends on where its two columns fall:
-// a quad starts at column 8g of scale block b = 5S + g, so a pair's columns
-// lie in blocks (b, b), (b, b+1) or (b+1, b+1), and which depends on g.  Per
-// superblock a lane holds P = (s_b, s_b+1) and six byte-permuted copies of
-// it, one per pattern of classes over the four lane groups that occurs
-// (pairs whose class is the same for every g read P through op_sel).
+// halves; columns 8..15 repeat 0..7 (their outputs are not used).  The
+// dequantisation and its per-pair scale classes are in dequant.h.
 // ---------------------------------------------------------------------------
 
 constexpr int kWaves = 4;
@@ -154,37 +120,6 @@ constexpr int kXcds = 8;      // accelerator dies of MI355X, each with its own L
 constexpr int kSplitMaxTokens = 32;  // gate/up splits K over the waves up to this batch
 constexpr int kCols = moe::kEntryTokens;                 // entry columns held in LDS
 constexpr int kSbBytes = moe::kSteps * 2 * kCols * 16;   // one superblock of an entry's activations: 2,560 B
-
-// class of local pair q of quad g: 0 = both columns in block b, 1 = low in b
-// and high in b + 1, 2 = both in b + 1 (b = the quad's first block)
-constexpr int pair_cls(int g, int q) {
-  const int lo = 40 * g + pair_col(q);
-  return (lo / 32 - g) + ((lo + 5) / 32 - g);
-}
-// pattern id of pair q: 0 = class 0 for every g, 7 = class 2 for every g,
-// 1..6 = the mixed patterns.  In q order they are q 0-2: 0000, 3-4: 0001,
-// 5: 0002, 6-9: 0012, 10-13: 0122, 14: 0222, 15-16: 1222, 17-19: 2222.
-constexpr int pat_of(int q) {
-  return q < 3 ? 0 : q < 5 ? 1 : q < 6 ? 2 : q < 10 ? 3 : q < 14 ? 4 : q < 15 ? 5 : q < 17 ? 6 : 7;
-}
-constexpr int pat_rep(int p) {  // a pair with pattern p
-  return p == 0 ? 0 : p == 1 ? 3 : p == 2 ? 5 : p == 3 ? 6 : p == 4 ? 10 : p == 5 ? 14 : p == 6 ? 15 : 17;
-}
-constexpr bool pat_table_ok() {
-  for (int q = 0; q < 20; ++q)
-    for (int g = 0; g < 4; ++g) {
-      if (pair_cls(g, q) != pair_cls(g, pat_rep(pat_of(q)))) return false;
-      if (pat_of(q) == 0 && pair_cls(g, q) != 0) return false;
-      if (pat_of(q) == 7 && pair_cls(g, q) != 2) return false;
-    }
-  return true;
-}
-static_assert(pat_table_ok(), "pattern table matches the scale classes");
-// v_perm_b32 selector giving (s_lo, s_hi) of a class from P = s_b | s_b+1 << 16
-constexpr uint32_t cls_sel(int c) {
-  const uint32_t lo = c == 2 ? 2u : 0u, hi = c == 0 ? 0u : 2u;
-  return lo | (lo + 1) << 8 | hi << 16 | (hi + 1) << 24;
-}
 
 struct Unit {
   const uint8_t *blob;  // the expert's blob (a readable stand-in when the entry is unusable)
@@ -313,33 +248,7 @@ __device__ inline void copy_unit_lds(const Mats<NMAT> &Mt, const Unit &U, int ti
   }
 }
 
-template <int q>
-__device__ inline h2 pair_scale(uint32_t P, const uint32_t (&Pm)[6]) {
-  constexpr int pat = pat_of(q);
-  const h2 S = __builtin_bit_cast(h2, P);
-  if constexpr (pat == 0) {
-    return (h2){S[0], S[0]};
-  } else if constexpr (pat == 7) {
-    return (h2){S[1], S[1]};
-  } else {
-    return __builtin_bit_cast(h2, Pm[pat - 1]);
-  }
-}
-
-template <int q>
-__device__ inline h2 deq_q(const uint32_t (&w)[4], const Consts &K, uint32_t P, const uint32_t (&Pm)[6]) {
-  constexpr int j = q % 5;
-  return deq_pair<j>(j < 3 ? w[q / 5] : (w[q / 5] >> 9), K, pair_scale<q>(P, Pm));
-}
-
-template <int t>
-__device__ inline h8 quad_a(const uint32_t (&w)[4], const Consts &K, uint32_t P, const uint32_t (&Pm)[6]) {
-  const h2 a0 = deq_q<4 * t + 0>(w, K, P, Pm);
-  const h2 a1 = deq_q<4 * t + 1>(w, K, P, Pm);
-  const h2 a2 = deq_q<4 * t + 2>(w, K, P, Pm);
-  const h2 a3 = deq_q<4 * t + 3>(w, K, P, Pm);
-  return (h8){a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
-}
+using moe::quad_a;
 
 struct MatSb {
   uint32_t w[4];
@@ -539,13 +448,7 @@ __global__ void __launch_bounds__(64 * kWaves, NMAT == 2 ? 3 : 4) ffn_decode_ker
   const int u_end = min((xcd + 1) * per, n_units);
   const Consts K = make_consts();
   uint32_t sel[6];
-#pragma unroll
-  for (int p = 1; p <= 6; ++p) {
-    const int q = pat_rep(p);
-    const uint32_t s0 = cls_sel(pair_cls(0, q)), s1 = cls_sel(pair_cls(1, q)), s2 = cls_sel(pair_cls(2, q)),
-                   s3 = cls_sel(pair_cls(3, q));
-    sel[p - 1] = g == 0 ? s0 : g == 1 ? s1 : g == 2 ? s2 : s3;
-  }
+  moe::pattern_selectors(g, sel);
   // B operand of lane (j, g) at step t of superblock S: slot ((20 S + 5 g +
   // t) * 2 + (j & 7) / 4) * 4 + j % 4, i.e. byte (20 S + t) * 128 + 640 g +
   // 16 (j & 7); the wave's range starts at superblock sb0
@@ -614,44 +517,57 @@ inline int max_entries(int T, int k, int E, int entry_m) {
 // one unit (entry x 4 tiles) per workgroup while that fits in the workgroups
 // the CUs hold at once; beyond, workgroups loop over units
 template <int NSB, int NMAT, int KS = 1>
-hipError_t launch_decode_nsb(const DecodeParams &P, int units, hipStream_t s) {
-  static int per_cu = 0, n_cu = 0;
-  if (!per_cu) {
-    int dev = 0, occ = 0, cus = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess)
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, ffn_decode_kernel<NSB, NMAT, KS>, 64 * kWaves, 0);
-    if (e != hipSuccess) return e;
-    n_cu = cus > 0 ? cus : 1;
-    per_cu = occ > 0 ? occ : 1;
-  }
-  const int cap = per_cu * n_cu;
+hipError_t launch_decode_nsb(const DecodeParams &P, int units, int per_cu, int n_cu, hipStream_t s) {
+  const int cap = (per_cu > 0 ? per_cu : 1) * (n_cu > 0 ? n_cu : 1);
   const int grid = (std::min(units, cap) + kXcds - 1) / kXcds * kXcds;
   hipLaunchKernelGGL((ffn_decode_kernel<NSB, NMAT, KS>), dim3(grid), dim3(64 * kWaves), 0, s, P);
   return hipGetLastError();
 }
 
-template <int NMAT>
-hipError_t launch_decode_mat(int nsb, const DecodeParams &P, int units, hipStream_t s) {
+template <int NSB, int NMAT, int KS = 1>
+hipError_t occupancy_nsb(int *occ) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, ffn_decode_kernel<NSB, NMAT, KS>, 64 * kWaves, 0);
+}
+
+// the kernel built for nsb superblocks: F<NSB>() for nsb = 1..13
+template <template <int> class F, typename... A>
+hipError_t by_nsb(int nsb, A... a) {
   switch (nsb) {
-    case 1: return launch_decode_nsb<1, NMAT>(P, units, s);
-    case 2: return launch_decode_nsb<2, NMAT>(P, units, s);
-    case 3: return launch_decode_nsb<3, NMAT>(P, units, s);
-    case 4: return launch_decode_nsb<4, NMAT>(P, units, s);
-    case 5: return launch_decode_nsb<5, NMAT>(P, units, s);
-    case 6: return launch_decode_nsb<6, NMAT>(P, units, s);
-    case 7: return launch_decode_nsb<7, NMAT>(P, units, s);
-    case 8: return launch_decode_nsb<8, NMAT>(P, units, s);
-    case 9: return launch_decode_nsb<9, NMAT>(P, units, s);
-    case 10: return launch_decode_nsb<10, NMAT>(P, units, s);
-    case 11: return launch_decode_nsb<11, NMAT>(P, units, s);
-    case 12: return launch_decode_nsb<12, NMAT>(P, units, s);
-    case 13: return launch_decode_nsb<13, NMAT>(P, units, s);
+    case 1: return F<1>::run(a...);
+    case 2: return F<2>::run(a...);
+    case 3: return F<3>::run(a...);
+    case 4: return F<4>::run(a...);
+    case 5: return F<5>::run(a...);
+    case 6: return F<6>::run(a...);
+    case 7: return F<7>::run(a...);
+    case 8: return F<8>::run(a...);
+    case 9: return F<9>::run(a...);
+    case 10: return F<10>::run(a...);
+    case 11: return F<11>::run(a...);
+    case 12: return F<12>::run(a...);
+    case 13: return F<13>::run(a...);
     static_assert(moe::kDecodeMaxNsb == 13, "one case per superblock count");
     default: return hipErrorInvalidValue;
   }
 }
+
+template <int NMAT>
+struct LaunchMat {
+  template <int NSB>
+  struct F {
+    static hipError_t run(const DecodeParams *P, int units, int per_cu, int n_cu, hipStream_t s) {
+      return launch_decode_nsb<NSB, NMAT>(*P, units, per_cu, n_cu, s);
+    }
+  };
+};
+
+template <int NMAT>
+struct OccMat {
+  template <int NSB>
+  struct F {
+    static hipError_t run(int *occ) { return occupancy_nsb<NSB, NMAT>(occ); }
+  };
+};
 
 }  // namespace
 
@@ -659,6 +575,16 @@ namespace moe {
 
 hipError_t launch_bucket_ex(const moe_ctx *c, const int32_t *idx, int T, int32_t *offsets, int32_t *perm, bool build,
                             int entry_m, const float *x, uint16_t *xrec, int xrec_h, hipStream_t s);
+
+hipError_t decode_occupancy(moe_ctx *c) {
+  c->decode_occ[0] = c->decode_occ[1] = c->decode_occ[2] = 1;
+  // widths the decode kernels are not built for take the prefill path only
+  if (c->L.gate.nsb > kDecodeMaxNsb || c->L.down.nsb > kDecodeMaxNsb) return hipSuccess;
+  hipError_t e = by_nsb<OccMat<2>::F>(c->L.gate.nsb, &c->decode_occ[0]);
+  if (e == hipSuccess) e = by_nsb<OccMat<1>::F>(c->L.down.nsb, &c->decode_occ[1]);
+  if (e == hipSuccess && c->L.gate.nsb == 13) e = occupancy_nsb<13, 2, 2>(&c->decode_occ[2]);
+  return e;
+}
 
 hipError_t launch_ffn_decode(const moe_ctx *c, int layer, const float *x, int T, const int32_t *idx,
                              const int32_t *slot_of_pair, float *y_pairs, float *y_shared, hipStream_t s) {
@@ -708,12 +634,12 @@ hipError_t launch_ffn_decode(const moe_ctx *c, int layer, const float *x, int T,
   // Built for the 13-superblock rows of d_model = 1,921..2,080.
   if (T <= kSplitMaxTokens && c->L.gate.nsb == 13) {
     const int u1s = ents * ((k.d_ff / 16 + kWaves / 2 - 1) / (kWaves / 2));
-    e = launch_decode_nsb<13, 2, 2>(P, u1s, s);
+    e = launch_decode_nsb<13, 2, 2>(P, u1s, c->decode_occ[2], c->n_cu, s);
   } else {
-    e = launch_decode_mat<2>(c->L.gate.nsb, P, u1, s);
+    e = by_nsb<LaunchMat<2>::F>(c->L.gate.nsb, &P, u1, c->decode_occ[0], c->n_cu, s);
   }
   if (e != hipSuccess) return e;
-  e = launch_decode_mat<1>(c->L.down.nsb, P, u2, s);
+  e = by_nsb<LaunchMat<1>::F>(c->L.down.nsb, &P, u2, c->decode_occ[1], c->n_cu, s);
   if (e != hipSuccess) return e;
   return hipGetLastError();
 }

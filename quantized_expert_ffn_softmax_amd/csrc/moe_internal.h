@@ -105,11 +105,12 @@ struct moe_ctx {
   int32_t *chunk_ws;     // [n_chunks][n_experts] for the large bucketing
   moe::WorkEntry *work;  // [max_work]
   int32_t *n_work;       // [4]: entries, routed entries, -, -
-  uint16_t *xrec;        // [max_tokens][xrec_halves(gate.nsb)]
-  uint16_t *hrec;        // [max_pairs + max_tokens][xrec_halves(down.nsb)]
-  uint16_t *x16;         // prefill: [max_tokens][d_model] fp16
-  uint16_t *h16;         // prefill: [max_pairs + max_tokens][d_ff] fp16
-  int32_t *tile_ws;      // prefill tile list
+  // x record: [max_tokens + 1][xrec_halves(gate.nsb)] (last row zero); the
+  // decode path's layout, or on the prefill path its own layout of the same
+  // size per token (each call rebuilds the rows it uses)
+  uint16_t *xrec;
+  uint16_t *hrec;        // decode h record: [max_pairs + max_tokens + 1][xrec_halves(down.nsb)]
+  uint16_t *h16;         // prefill h record: [max_pairs + max_tokens][down.nsb * 160 * 2] fp16 (hi, lo), pads zero
   int32_t *slot_ws;      // [max_pairs] slots when the caller passes none
   float *route_part;     // [route_ks][route_small_t][n_experts] partial logits (decode-size router)
   int32_t route_ks;      // column slices of the decode-size router
@@ -117,7 +118,8 @@ struct moe_ctx {
   int32_t max_pairs;
   int32_t max_work;
   int32_t n_chunks_max;
-  int32_t max_tiles;
+  int32_t n_cu;          // compute units of the context's device
+  int32_t decode_occ[3]; // decode FFN workgroups per CU: gate/up, down, gate/up K-split (queried at create)
 
   // miss path
   int32_t *dmiss;        // device: [0]=unique, [1]=misses, [2]=error, then (id, slot) pairs
@@ -147,6 +149,7 @@ hipError_t launch_bucket(const moe_ctx *c, const int32_t *idx, int T, int32_t *o
                          bool build_work, hipStream_t s);
 hipError_t launch_resolve(moe_ctx *c, int layer, const int32_t *idx, int T, int32_t *slot_of_pair, bool fill,
                           hipStream_t s);
+hipError_t decode_occupancy(moe_ctx *c);  // fills c->decode_occ for c's superblock counts
 hipError_t launch_ffn_decode(const moe_ctx *c, int layer, const float *x, int T, const int32_t *idx,
                              const int32_t *slot_of_pair, float *y_pairs, float *y_shared, hipStream_t s);
 hipError_t launch_ffn_prefill(const moe_ctx *c, int layer, const float *x, int T, const int32_t *idx,

@@ -187,47 +187,70 @@ def test_decode_exact_identities():
 
 
 def test_prefill_full_chunk_sampled():
+    """The 12,288-token prefill chunk at its full size, in the launch the bench
+    times: full bucketing against the oracle; expert outputs row by row on a
+    sample of pairs -- one pair in every 128-token entry of the hottest expert,
+    up to 20 pairs of each of 20 other experts (8 among the 40 fullest, 12 among
+    the rest; seeded), and one token in every
+    128-token entry of the shared expert plus 64 more -- against the oracle's
+    'fp16_weights' mode (tight) and the exact definition (the stated bar); routing
+    and the combine on the tokens those pairs belong to."""
     T = 12288
     dims = dict(d_model=2048, d_ff=768, n_experts=512, top_k=10)
-    say(f"  prefill chunk T={T} (full size), sampled tokens")
+    say(f"  prefill chunk T={T} (full size), sampled pairs")
     layer = SyntheticLayer(seed=11, n_tokens=T, alpha=0.75, device="cuda:0", **dims)
-    ctx, k = layer.ctx, dims["top_k"]
+    ctx, k, E = layer.ctx, dims["top_k"], dims["n_experts"]
     buf = ctx.buffers(T)
     ctx.layer(0, layer.x, layer.wr, layer.bias, buf, B.MOE_PATH_PREFILL)
     torch.cuda.synchronize()
     idx = buf["idx"].cpu().numpy()
     # full bucketing of the chunk (large path) against the oracle
-    off = torch.empty(513, dtype=torch.int32, device="cuda")
+    off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
     perm = torch.empty(T * k, dtype=torch.int32, device="cuda")
     B.moe_bucket(ctx.ctx, buf["idx"], T, off, perm)
     torch.cuda.synchronize()
-    check_bucket(off.cpu().numpy(), perm.cpu().numpy(), idx, 512)
-    # sampled tokens: routing, expert outputs, combine
+    off_np, perm_np = off.cpu().numpy(), perm.cpu().numpy()
+    check_bucket(off_np, perm_np, idx, E)
+    counts = np.diff(off_np)
     rng = np.random.default_rng(0)
-    toks = np.sort(np.concatenate([[0, T - 1], rng.choice(np.arange(1, T - 1), 2, replace=False)]))
-    lg = buf["logits"][toks].cpu().numpy().astype(np.float64)
+    hot = int(np.argmax(counts))
+    picks = {}  # expert -> pair ids
+    seg = perm_np[off_np[hot]:off_np[hot + 1]]
+    picks[hot] = np.array([seg[i + rng.integers(0, min(128, seg.size - i))] for i in range(0, seg.size, 128)])
+    big = np.argsort(-counts)[1:40]  # well-filled experts after the hottest: 8 of them
+    small = np.flatnonzero((counts > 0) & ~np.isin(np.arange(E), np.append(big, hot)))
+    others = np.concatenate([rng.choice(big, 8, replace=False), rng.choice(small, 12, replace=False)])
+    for e in others:
+        seg = perm_np[off_np[e]:off_np[e + 1]]
+        picks[int(e)] = np.sort(rng.choice(seg, min(20, seg.size), replace=False))
+    n_pairs = sum(v.size for v in picks.values())
+    shared_toks = np.unique(np.concatenate([np.arange(0, T, 128) + rng.integers(0, 128, T // 128),
+                                            rng.choice(T, 64, replace=False), [0, T - 1]]))
+    say(f"    hottest expert {hot}: {counts[hot]} pairs, {picks[hot].size} entries sampled; {n_pairs} pairs over "
+        f"{len(picks)} experts; {shared_toks.size} shared-expert tokens")
+    assert n_pairs >= 256
+    yp_gpu = buf["y_pairs"].cpu().numpy()
+    ys_gpu = buf["y_shared"].cpu().numpy()
+    got, ref_w, ref_x = [], [], []
+    for e, pairs in list(picks.items()) + [(E, None)]:
+        blob = layer.blob_np(e)
+        rows_x = layer.x_np[pairs // k] if pairs is not None else layer.x_np[shared_toks]
+        ref_w.append(oracle.expert_ffn(rows_x, oracle.expert_weights(blob, 2048, 768, True), "fp16_weights"))
+        ref_x.append(oracle.expert_ffn(rows_x, oracle.expert_weights(blob, 2048, 768), "exact"))
+        got.append(yp_gpu[pairs] if pairs is not None else ys_gpu[shared_toks])
+    got, ref_w, ref_x = np.concatenate(got), np.concatenate(ref_w), np.concatenate(ref_x)
+    e_w, e_x = rel_err(got, ref_w), rel_err(got, ref_x)
+    # routing and combine on the tokens of the sampled pairs
+    toks = np.unique(np.concatenate([v // k for v in picks.values()] + [shared_toks]))
+    lg = buf["logits"][torch.from_numpy(toks).cuda()].cpu().numpy().astype(np.float64)
     idx_ref, w_ref = oracle.topk_from_logits(lg, k)
     assert np.array_equal(idx[toks], idx_ref)
-    w_gpu = buf["w"][toks].cpu().numpy()
+    w_gpu = buf["w"][torch.from_numpy(toks).cuda()].cpu().numpy()
     assert np.all(np.abs(w_gpu - w_ref) <= 1e-6 * np.abs(w_ref) + 1e-12)
     rows = (toks[:, None] * k + np.arange(k)[None, :]).reshape(-1)
-    yp = buf["y_pairs"][torch.from_numpy(rows).cuda()].cpu().numpy()
-    ys = buf["y_shared"][torch.from_numpy(toks).cuda()].cpu().numpy()
-    out = buf["out"][torch.from_numpy(toks).cuda()].cpu().numpy()
-    wcache = {}
-
-    def weights(e):
-        if e not in wcache:
-            wcache[e] = oracle.expert_weights(layer.blob_np(e), 2048, 768, True)
-        return wcache[e]
-
-    x = layer.x_np[toks]
-    ref_p = np.stack([oracle.expert_ffn(x[i:i + 1], weights(int(idx[t, j])), "fp16_operands")[0]
-                      for i, t in enumerate(toks) for j in range(k)])
-    ref_s = oracle.expert_ffn(x, weights(512), "fp16_operands")
-    e_p, e_s = rel_err(yp, ref_p), rel_err(ys, ref_s)
-    comb = oracle.combine(yp.astype(np.float64), w_gpu.astype(np.float64), ys.astype(np.float64))
-    e_c = rel_err(out, comb)
-    say(f"    tokens {toks.tolist()}: pairs {e_p:.2e} shared {e_s:.2e} combine {e_c:.2e}")
-    assert e_p <= TOL and e_s <= TOL and e_c <= 1e-6
+    comb = oracle.combine(yp_gpu[rows].astype(np.float64), w_gpu.astype(np.float64), ys_gpu[toks].astype(np.float64))
+    e_c = rel_err(buf["out"][torch.from_numpy(toks).cuda()].cpu().numpy(), comb)
+    say(f"    {got.shape[0]} rows: vs fp16_weights {e_w:.2e}, vs exact {e_x:.2e}; combine on {toks.size} tokens "
+        f"{e_c:.2e}")
+    assert e_w <= 1e-4 and e_x <= TOL and e_c <= 1e-6
     layer.close()

@@ -1,8 +1,9 @@
 """GPU parity of the routed MoE layer against the CPU oracle, through the C ABI.
 
-Decode path: compared with the oracle in 'fp16_weights' mode (the path's
-operand rounding) tightly, and with the exact float64 definition at the stated
-bar.  Prefill path: compared with the 'fp16_operands' mode at the stated bar.
+Both paths round only the dequantised weights to fp16 (activations carried as
+hi + lo fp16 halves, fp32 sums): they are compared with the oracle's
+'fp16_weights' mode at a tight tolerance, and with the exact float64
+definition at the stated bar (max |err| <= 2e-3 x RMS of the call's output).
 """
 import numpy as np
 import pytest
@@ -42,8 +43,7 @@ def _check_layer(layer, path, tight_prec, tight_tol):
     say(f"    near-ties {ties}; vs {tight_prec}: pairs {e_pairs:.2e} shared {e_shared:.2e} out {e_out:.2e}; "
         f"vs exact: out {e_exact:.2e}")
     assert e_pairs <= tight_tol and e_shared <= tight_tol and e_out <= tight_tol
-    if path == B.MOE_PATH_DECODE:
-        assert e_exact <= TOL
+    assert e_exact <= TOL
     # combine on the GPU's own expert outputs
     comb = oracle.combine(gpu["y_pairs"].astype(np.float64), gpu["w"].astype(np.float64),
                           gpu["y_shared"].astype(np.float64))
@@ -83,14 +83,14 @@ def test_decode_width_limit():
     with pytest.raises(B.MoeError) as ei:
         layer.forward_gpu(B.MOE_PATH_DECODE)
     assert ei.value.status == B.MOE_ERR_INVALID
-    _check_layer(layer, B.MOE_PATH_AUTO, "fp16_operands", TOL)
+    _check_layer(layer, B.MOE_PATH_AUTO, "fp16_weights", 1e-4)
     layer.close()
 
 
 @pytest.mark.parametrize("T", [1, 8, 65, 130])
 def test_tiny_prefill(T):
     layer = _layer(T=T, **TINY)
-    _check_layer(layer, B.MOE_PATH_PREFILL, "fp16_operands", TOL)
+    _check_layer(layer, B.MOE_PATH_PREFILL, "fp16_weights", 1e-4)
     layer.close()
 
 
@@ -99,7 +99,7 @@ def test_tiny_k_extremes(k):
     shape = dict(TINY, top_k=k)
     layer = _layer(T=8, **shape)
     _check_layer(layer, B.MOE_PATH_DECODE, "fp16_weights", 1e-4)
-    _check_layer(layer, B.MOE_PATH_PREFILL, "fp16_operands", TOL)
+    _check_layer(layer, B.MOE_PATH_PREFILL, "fp16_weights", 1e-4)
     layer.close()
 
 
@@ -133,7 +133,7 @@ def test_real_layer_decode_T40_zipf():
 
 def test_real_layer_prefill_small():
     layer = _layer(T=200, alpha=0.75, **REAL)
-    _check_layer(layer, B.MOE_PATH_PREFILL, "fp16_operands", TOL)
+    _check_layer(layer, B.MOE_PATH_PREFILL, "fp16_weights", 1e-4)
     layer.close()
 
 

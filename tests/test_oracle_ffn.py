@@ -58,7 +58,7 @@ def test_all_codes_four_gives_zero():
     rng = np.random.default_rng(12)
     blob, _, _ = _blob_from_codes(d, f, rng, code_fn=lambda s: np.full(s, 4))
     x = rng.standard_normal((4, d)).astype(np.float32)
-    for prec in ("exact", "fp16_weights", "fp16_wh"):
+    for prec in ("exact", "fp16_weights"):
         y = oracle.expert_ffn(x, oracle.expert_weights(blob, d, f, prec != "exact"), prec)
         assert np.all(y == 0.0)
 

@@ -1,14 +1,13 @@
-"""Pins for the oracle's reduced-precision modes (CPU only).
+"""Pins for the oracle's reduced-precision mode (CPU only).
 
-'fp16_weights' rounds every dequantised weight (q - 4) * s once to fp16;
-'fp16_wh' also rounds h = silu(g) * u once to fp16 from its float64 value and
-keeps x unrounded.  These tests restate the rounding from the definition of
-IEEE binary16 (11-bit significand, exponents -14..15, subnormal spacing
+'fp16_weights' rounds every dequantised weight (q - 4) * s once to fp16 and
+keeps x and h unrounded.  These tests restate the rounding from the definition
+of IEEE binary16 (11-bit significand, exponents -14..15, subnormal spacing
 2^-24, round to nearest with ties to even) in exact rationals, work small
 cases by hand with ``fractions``, and check that each plausible slip --
-rounding x too, leaving h or W unrounded, rounding (q s) instead of
-((q - 4) s), rounding h through fp32 first, breaking ties away from even --
-moves the result far beyond the tolerance the comparison uses.
+rounding x or h too, leaving W unrounded, rounding (q s) instead of
+((q - 4) s), breaking ties away from even -- moves the result far beyond the
+tolerance the comparison uses.
 """
 import math
 from fractions import Fraction
@@ -111,33 +110,19 @@ def _close(a, b, tol):
     return np.abs(a - b).max() <= tol * np.abs(b).max()
 
 
-def test_fp16_wh_hand_worked():
-    for seed in (21, 22):
+def test_fp16_weights_hand_worked():
+    for seed in (21, 22, 23):
         d, f, codes, scales, x = _worked_case(seed)
         blob = _blob(d, f, codes, scales)
-        got = oracle.expert_ffn(x[None, :], oracle.expert_weights(blob, d, f, True), "fp16_wh")[0]
-        want = _hand_ffn(x, codes, scales, round_w=True, round_h=True, round_x=False)
+        got = oracle.expert_ffn(x[None, :], oracle.expert_weights(blob, d, f, True), "fp16_weights")[0]
+        want = _hand_ffn(x, codes, scales, round_w=True, round_h=False, round_x=False)
         assert _close(got, want, 1e-13)
         # each slip moves the result by far more than the tolerance above
-        for slip in (dict(round_w=False, round_h=True, round_x=False),
-                     dict(round_w="qs", round_h=True, round_x=False),
-                     dict(round_w=True, round_h=False, round_x=False),
-                     dict(round_w=True, round_h=True, round_x=True)):
-            other = _hand_ffn(x, codes, scales, **slip)
-            assert not _close(other, want, 1e-7), slip
-
-
-def test_fp16_weights_hand_worked():
-    d, f, codes, scales, x = _worked_case(23)
-    blob = _blob(d, f, codes, scales)
-    got = oracle.expert_ffn(x[None, :], oracle.expert_weights(blob, d, f, True), "fp16_weights")[0]
-    want = _hand_ffn(x, codes, scales, round_w=True, round_h=False, round_x=False)
-    assert _close(got, want, 1e-13)
-    for slip in (dict(round_w=False, round_h=False, round_x=False),
-                 dict(round_w="qs", round_h=False, round_x=False),
-                 dict(round_w=True, round_h=True, round_x=False),
-                 dict(round_w=True, round_h=False, round_x=True)):
-        assert not _close(_hand_ffn(x, codes, scales, **slip), want, 1e-7), slip
+        for slip in (dict(round_w=False, round_h=False, round_x=False),
+                     dict(round_w="qs", round_h=False, round_x=False),
+                     dict(round_w=True, round_h=True, round_x=False),
+                     dict(round_w=True, round_h=False, round_x=True)):
+            assert not _close(_hand_ffn(x, codes, scales, **slip), want, 1e-7), slip
 
 
 def test_reduced_modes_equal_exact_on_representable_operands():
@@ -146,8 +131,8 @@ def test_reduced_modes_equal_exact_on_representable_operands():
     # 4 + 3 p_c, so g = 3 * 32 * m_t * s_g(r) = 48 m_t 2^(r mod 3) >= 48, where
     # silu(g) == g in float64 (exp(-40) < 2^-53).  u is m_t times a multiple
     # of 2^-5 with |u / m_t| <= 4, so h = g u has at most 10 significant bits:
-    # every h is an fp16 value too, and both reduced modes must give the exact
-    # result bit for bit.
+    # every h is an fp16 value too (no rounding of h could hide here), and the
+    # reduced mode must give the exact result bit for bit.
     d = f = 32
     rng = np.random.default_rng(5)
     p = np.where(rng.random(d) < 0.5, -1, 1)
@@ -165,20 +150,8 @@ def test_reduced_modes_equal_exact_on_representable_operands():
     h = oracle.silu(g) * (x.astype(np.float64) @ we[1].T)
     assert np.array_equal(h, h.astype(np.float16).astype(np.float64))  # h representable
     ex = oracle.expert_ffn(x, we, "exact")
-    for prec in ("fp16_weights", "fp16_wh"):
-        got = oracle.expert_ffn(x, oracle.expert_weights(blob, d, f, True), prec)
-        assert np.array_equal(got, ex), prec
-
-
-def test_h_rounded_from_float64_not_through_fp32():
-    # 1 + 2^-11 + 2^-40 is above the fp16 tie between 1 and 1 + 2^-10: rounding
-    # it directly gives 1 + 2^-10; rounding through fp32 first drops the 2^-40
-    # and the tie then goes to 1.0
-    v = 1 + 2.0 ** -11 + 2.0 ** -40
-    assert float(rne_fp16(Fraction(v))) == 1 + 2.0 ** -10
-    from oracle import moe_oracle
-    assert moe_oracle._f16(np.array([v]))[0] == 1 + 2.0 ** -10
-    assert moe_oracle._f16(np.array([np.float32(v)], dtype=np.float64))[0] == 1.0
+    got = oracle.expert_ffn(x, oracle.expert_weights(blob, d, f, True), "fp16_weights")
+    assert np.array_equal(got, ex)
 
 
 def test_unknown_precision_is_refused():
@@ -188,4 +161,4 @@ def test_unknown_precision_is_refused():
     blob = _blob(d, f, [rng.integers(0, 8, (f, d)), rng.integers(0, 8, (f, d)), rng.integers(0, 8, (d, f))],
                  [np.full((f, 1), 0.03), np.full((f, 1), 0.03), np.full((d, 1), 0.03)])
     with pytest.raises(ValueError):
-        oracle.expert_ffn(np.ones((1, d), np.float32), oracle.expert_weights(blob, d, f, True), "fp16_operands")
+        oracle.expert_ffn(np.ones((1, d), np.float32), oracle.expert_weights(blob, d, f, True), "fp16_wh")
