@@ -177,6 +177,19 @@ moe_status moe_combine(moe_ctx *ctx, const float *y_pairs, const float *w,
 moe_status moe_bucket(moe_ctx *ctx, const int32_t *idx, int32_t T, int32_t *offsets,
                       int32_t *perm, void *stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): moe_bucket without a
+ * context.  offsets [n_experts+1] and perm [T*top_k] as moe_bucket writes
+ * them for idx [T][top_k] (out-of-range expert ids ignored).  Past 1,024 pairs
+ * the per-chunk expert counts live in a static device array of 2 MiB per GPU
+ * (512 chunks x 1,024 experts), so T*top_k must be <= 131,072 and
+ * n_experts <= 1,024 (MOE_ERR_INVALID otherwise, nothing enqueued); no call
+ * allocates.  Every call on one GPU shares that array: calls that overlap in
+ * time on one GPU (different streams, or host threads) race and must be
+ * ordered by the caller.  Asynchronous on `stream`. */
+moe_status moe_bucket_noalloc(const int32_t *idx, int32_t T, int32_t top_k, int32_t n_experts,
+                              int32_t *offsets, int32_t *perm, void *stream);
+
 /* Copies the slot table to host arrays (any may be NULL): slot_of
  * [n_layers*n_experts], id_of [n_slots], stamp [n_slots].  Synchronises the
  * device.  In resident mode the table is the identity and stamps are 0. */

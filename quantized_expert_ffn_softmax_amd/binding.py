@@ -74,6 +74,7 @@ _SIGS = {
     "moe_expert_ffn": (_I, [_P, _I, _P, _I, _P, _P, _P, _P, _I, _P]),
     "moe_combine": (_I, [_P, _P, _P, _P, _I, _P, _P]),
     "moe_bucket": (_I, [_P, _P, _I, _P, _P, _P]),
+    "moe_bucket_noalloc": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "moe_cache_snapshot": (_I, [_P, _P, _P, _P]),
     "moe_cache_reset": (_I, [_P]),
     "moe_get_stats": (_I, [_P, ctypes.POINTER(moe_resolve_info)]),
@@ -186,6 +187,11 @@ def moe_combine(ctx, y_pairs, w, y_shared, T, out, stream=None):
 
 def moe_bucket(ctx, idx, T, offsets, perm, stream=None):
     _check(load().moe_bucket(ctx, _ptr(idx), T, _ptr(offsets), _ptr(perm), _stream(stream)), "moe_bucket")
+
+
+def moe_bucket_noalloc(idx, T, top_k, n_experts, offsets, perm, stream=None):
+    _check(load().moe_bucket_noalloc(_ptr(idx), T, top_k, n_experts, _ptr(offsets), _ptr(perm), _stream(stream)),
+           "moe_bucket_noalloc")
 
 
 def moe_cache_snapshot(ctx, slot_of=None, id_of=None, stamp=None):

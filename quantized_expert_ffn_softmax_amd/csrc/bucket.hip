@@ -2,6 +2,8 @@
 // (offsets[E+1]) and a stable scatter of pair ids (perm), plus the list of
 // work entries (<= entry_m tokens of one expert each, then the shared
 // expert's tokens) that the FFN kernels walk.
+#include <mutex>
+
 #include "device_util.h"
 #include "moe_internal.h"
 #include "record.h"
@@ -239,3 +241,73 @@ hipError_t launch_bucket(const moe_ctx *c, const int32_t *idx, int T, int32_t *o
 }
 
 }  // namespace moe
+
+// ---------------------------------------------------------------------------
+// Allocation-free bucketing.  Past 1,024 pairs the bucketing keeps per-chunk
+// expert counts in a scratch buffer; this entry point takes it from a
+// file-scope device array instead of a context's workspace, so it needs no
+// context and calls no allocator.  Every chunk row the kernels read is
+// written first in the same call (the histogram writes all E counts of each
+// chunk), so nothing has to be cleared between calls.  One array per GPU,
+// shared by every call on that GPU: calls that overlap on one GPU race.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int kNoAllocMaxPairs = 131072;  // 512 chunks of 256 pairs
+constexpr int kNoAllocMaxExperts = 1024;
+constexpr int kMaxDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) int32_t scratch[(kNoAllocMaxPairs / kChunk) * kNoAllocMaxExperts];  // 2 MiB
+
+// The array's device address, looked up once per device with that device
+// current; host code uses only this address, never the symbol itself.
+static std::mutex g_scratch_mu;
+static int32_t *g_scratch_addr[kMaxDevices];
+
+static hipError_t scratch_addr(int32_t **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev] = static_cast<int32_t *>(p);
+  }
+  *out = g_scratch_addr[dev];
+  return hipSuccess;
+}
+
+extern "C" moe_status moe_bucket_noalloc(const int32_t *idx, int32_t T, int32_t top_k, int32_t n_experts,
+                                         int32_t *offsets, int32_t *perm, void *stream) {
+  MOE_CHECK(idx && offsets && perm, MOE_ERR_INVALID, "moe_bucket_noalloc: null idx, offsets or perm");
+  MOE_CHECK(T >= 1 && top_k >= 1 && top_k <= 32, MOE_ERR_INVALID, "moe_bucket_noalloc: need T >= 1 and 1 <= top_k <= 32");
+  MOE_CHECK(n_experts >= 1 && n_experts <= kNoAllocMaxExperts, MOE_ERR_INVALID,
+            "moe_bucket_noalloc: n_experts must be 1..1024");
+  MOE_CHECK((int64_t)T * top_k <= kNoAllocMaxPairs, MOE_ERR_INVALID,
+            "moe_bucket_noalloc: at most 131,072 pairs (T * top_k): the static scratch holds 512 chunks x 1,024 "
+            "expert counts (2 MiB)");
+  const int n = T * top_k, E = n_experts;
+  hipStream_t s = (hipStream_t)stream;
+  if (n <= kSmallMax) {  // one workgroup, no scratch
+    const int nt = ((n > E ? n : E) + 63) / 64 * 64;
+    hipLaunchKernelGGL(bucket_small, dim3(1), dim3(nt), 0, s, idx, n, E, T, offsets, perm, 0, 1,
+                       (moe::WorkEntry *)nullptr, (int32_t *)nullptr, (const float *)nullptr, 0, 0,
+                       (uint16_t *)nullptr, 0);
+    MOE_HIP(hipGetLastError());
+    return MOE_OK;
+  }
+  int32_t *chunk = nullptr;
+  MOE_HIP(scratch_addr(&chunk));
+  const int nch = (n + kChunk - 1) / kChunk;
+  hipLaunchKernelGGL(bucket_hist, dim3(nch), dim3(kChunk), 0, s, idx, n, E, chunk);
+  hipLaunchKernelGGL(bucket_scan, dim3(1), dim3(kBucketThreads), 0, s, chunk, nch, E, T, offsets, 0, 1,
+                     (moe::WorkEntry *)nullptr, (int32_t *)nullptr);
+  hipLaunchKernelGGL(bucket_scatter, dim3(nch), dim3(kChunk), 0, s, idx, n, E, (const int32_t *)chunk,
+                     (const int32_t *)offsets, perm);
+  MOE_HIP(hipGetLastError());
+  return MOE_OK;
+}

@@ -92,3 +92,14 @@ def test_null_context_calls(lib):
     assert lib.moe_combine_norm(None, None, None, None, 1, None, None, None) == B.MOE_ERR_INVALID
     with pytest.raises(B.MoeError):
         B.moe_destroy(None)
+
+
+def test_noalloc_bucket_validation(lib):
+    # refused before any HIP call: null pointers, sizes past the static scratch
+    p = 4096
+    assert lib.moe_bucket_noalloc(None, 1, 1, 1, p, p, None) == B.MOE_ERR_INVALID
+    assert lib.moe_bucket_noalloc(p, 13108, 10, 512, p, p, None) == B.MOE_ERR_INVALID  # 131,080 pairs
+    assert lib.moe_bucket_noalloc(p, 8, 2, 1025, p, p, None) == B.MOE_ERR_INVALID
+    assert lib.moe_bucket_noalloc(p, 0, 2, 16, p, p, None) == B.MOE_ERR_INVALID
+    assert lib.moe_bucket_noalloc(p, 8, 33, 64, p, p, None) == B.MOE_ERR_INVALID
+    assert "131,072" in B.moe_last_error() or B.moe_last_error()
