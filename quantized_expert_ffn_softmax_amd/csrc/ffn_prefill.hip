@@ -218,14 +218,17 @@ __device__ __attribute__((always_inline)) inline void k_step(int S, int nsb, con
   if constexpr (t >= 2) load_word(R, min(S + 1, nsb - 1), t - 2, W);
   if constexpr (t == 2) load_scales<SP ^ 1>(R, min(S + 1, nsb - 1), g, W);
   if (!wact) return;  // wave-uniform: rows past the matrix
+  // B operands one read ahead of their MFMAs: the next half is requested
+  // before the current one's four MFMAs, so LDS latency overlaps them
   const uint8_t *tile = xs[PAR];
+  h8 cur = *reinterpret_cast<const h8 *>(tile + rl_hi);
 #pragma unroll
   for (int nt = 0; nt < kTT; ++nt) {
     if (nt < ntt) {  // wave-uniform: token tiles holding tokens
-      const h8 bh = *reinterpret_cast<const h8 *>(tile + nt * 16 * G::kRowB + rl_hi);
-#pragma unroll
-      for (int a = 0; a < 4; ++a) acc[a][nt] = mfma(A[a], bh, acc[a][nt]);
       const h8 bl = *reinterpret_cast<const h8 *>(tile + nt * 16 * G::kRowB + rl_lo);
+#pragma unroll
+      for (int a = 0; a < 4; ++a) acc[a][nt] = mfma(A[a], cur, acc[a][nt]);
+      if (nt + 1 < ntt) cur = *reinterpret_cast<const h8 *>(tile + (nt + 1) * 16 * G::kRowB + rl_hi);
 #pragma unroll
       for (int a = 0; a < 4; ++a) acc[a][nt] = mfma(A[a], bl, acc[a][nt]);
     }
