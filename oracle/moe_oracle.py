@@ -209,8 +209,8 @@ class LRUCache:
 
     def reset(self):
         self.slot_of = [-1] * (self.L * self.E)
-        self.id_of = [-1] * self.S
-        self.stamp = [0] * self.S
+        self.id_of = np.full(self.S, -1, dtype=np.int64)
+        self.stamp = np.zeros(self.S, dtype=np.int64)
         self.clock = 0
         self.lookups = 0
         self.hits = 0
@@ -237,20 +237,14 @@ class LRUCache:
         for i in uniq:
             if self.slot_of[i] >= 0:
                 continue
-            victim = -1
-            for s in range(self.S):
-                if self.id_of[s] == -1:
-                    victim = s
-                    break
-            if victim < 0:
-                best = None
-                for s in range(self.S):
-                    if self.stamp[s] < self.clock:
-                        key = (self.stamp[s], s)
-                        if best is None or key < best:
-                            best = key
-                victim = best[1]
-                self.slot_of[self.id_of[victim]] = -1
+            free = np.flatnonzero(self.id_of == -1)
+            if free.size:
+                victim = int(free[0])  # the lowest-index free slot
+            else:
+                # the smallest (stamp, slot) among slots not touched in this call
+                elig = np.flatnonzero(self.stamp < self.clock)
+                victim = int(elig[np.argmin(self.stamp[elig])])  # argmin takes the first (lowest slot) of equal stamps
+                self.slot_of[int(self.id_of[victim])] = -1
             self.id_of[victim] = i
             self.slot_of[i] = victim
             self.stamp[victim] = self.clock

@@ -73,7 +73,7 @@ def test_async_resolve_matches_sync_and_oracle():
     for ctx in (a, b):
         so_, io_, st_ = np.zeros(L * E, np.int32), np.zeros(S, np.int32), np.zeros(S, np.uint32)
         B.moe_cache_snapshot(ctx.ctx, so_, io_, st_)
-        assert so_.tolist() == orc.slot_of and io_.tolist() == orc.id_of and st_.tolist() == orc.stamp
+        assert so_.tolist() == orc.slot_of and io_.tolist() == orc.id_of.tolist() and st_.tolist() == orc.stamp.tolist()
         st = B.moe_get_stats(ctx.ctx)
         assert (st["lookups"], st["hits"], st["misses"]) == (orc.lookups, orc.hits, orc.misses)
         assert st["bytes_h2d"] == orc.misses * stride and st["failed_calls"] == 0

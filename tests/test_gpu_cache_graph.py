@@ -81,7 +81,7 @@ def test_lru_cache_matches_oracle_and_feeds_the_ffn():
     io_ = np.zeros(S, np.int32)
     st_ = np.zeros(S, np.uint32)
     B.moe_cache_snapshot(cap.ctx, so_, io_, st_)
-    assert so_.tolist() == orc.slot_of and io_.tolist() == orc.id_of and st_.tolist() == orc.stamp
+    assert so_.tolist() == orc.slot_of and io_.tolist() == orc.id_of.tolist() and st_.tolist() == orc.stamp.tolist()
     st = B.moe_get_stats(cap.ctx)
     assert (st["lookups"], st["hits"], st["misses"]) == (orc.lookups, orc.hits, orc.misses)
     say(f"    hits {orc.hits}/{orc.lookups}, misses {orc.misses}")

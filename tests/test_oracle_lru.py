@@ -53,15 +53,15 @@ def test_hand_trace():
             continue
         slots, misses = c.resolve(0, np.array(call["idx"]))
         assert [list(m) for m in misses] == call["misses"]
-        assert c.stamp == call["stamp"]
-        assert c.id_of == call["id_of"]
+        assert c.stamp.tolist() == call["stamp"]
+        assert c.id_of.tolist() == call["id_of"]
         for i, s in enumerate(c.id_of):
             if s >= 0:
                 assert c.slot_of[s] == i
         assert np.array_equal(slots, np.vectorize(lambda e: c.slot_of[e])(np.array(call["idx"])))
     # the failing call changed nothing: state, clock and counts are call 4's
     last = g["calls"][3]
-    assert c.stamp == last["stamp"] and c.id_of == last["id_of"] and c.clock == 4
+    assert c.stamp.tolist() == last["stamp"] and c.id_of.tolist() == last["id_of"] and c.clock == 4
     assert c.lookups == g["lookups_after_4"] and c.hits == g["hits_after_4"]
 
 
