@@ -172,9 +172,9 @@ def _median_ms(pairs):
 
 def measure_peaks(buf, read_bytes=4 << 30, reps=5):
     """Achievable peaks on this device: a streaming read of `read_bytes` of the
-    (already filled) expert pool, and a loop of independent fp16 MFMAs
-    (v_mfma_f32_16x16x32_f16, the instruction of the FFN kernels).  Median of
-    `reps` timed launches after one warm-up each."""
+    (already filled) expert pool, and a loop of independent dense fp16 MFMAs
+    (v_mfma_f32_32x32x16_f16).  Median of `reps` timed launches after one
+    warm-up each."""
     import torch
 
     from quantized_expert_ffn_softmax_amd import binding as B
@@ -190,8 +190,8 @@ def measure_peaks(buf, read_bytes=4 << 30, reps=5):
         b.record()
     torch.cuda.synchronize()
     hbm_ms = _median_ms(ev[1:])
-    iters, mblocks = 4096, n_cu * 2
-    flops = mblocks * 4 * iters * 8 * 16384.0
+    iters, mblocks = 32768, n_cu * 2  # ~2 ms a launch: long enough for clocks to settle
+    flops = mblocks * 4 * iters * 4 * 32768.0
     for a, b in ev:
         a.record()
         B.moe_peak_mfma_f16(iters, mblocks, sink)
@@ -203,7 +203,7 @@ def measure_peaks(buf, read_bytes=4 << 30, reps=5):
            "mfma_f16_tflops": round(flops / (mfma_ms * 1e-3) / 1e12, 1),
            "mfma_frac_of_spec": round(flops / (mfma_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
            "how": f"moe_peak_hbm_read over {nbytes >> 20} MiB ({blocks} workgroups); moe_peak_mfma_f16 "
-                  f"{mblocks} x 4 waves x {iters} x 8 v_mfma_f32_16x16x32_f16; median of {reps} launches"}
+                  f"{mblocks} x 4 waves x {iters} x 4 v_mfma_f32_32x32x16_f16; median of {reps} launches"}
     log(f"[bench] measured peaks: HBM read {out['hbm_read_gbs']} GB/s, fp16 MFMA {out['mfma_f16_tflops']} TFLOP/s")
     return out
 

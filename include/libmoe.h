@@ -231,8 +231,8 @@ moe_status moe_combine_norm(moe_ctx *ctx, const float *y_pairs, const float *w,
  * 256 MiB last-level cache so that the figure is HBM's.
  *
  * moe_peak_mfma_f16: n_blocks workgroups of 4 waves; every wave runs `iters`
- * rounds of 8 independent v_mfma_f32_16x16x32_f16 on register operands, so
- * one launch is n_blocks * 4 * iters * 8 * 16384 flops; sink [n_blocks]
+ * rounds of 4 independent v_mfma_f32_32x32x16_f16 on register operands, so
+ * one launch is n_blocks * 4 * iters * 4 * 32768 flops; sink [n_blocks]
  * float is scratch (written only under a condition no run meets).
  * Invalid arguments return MOE_ERR_INVALID and enqueue nothing. */
 moe_status moe_peak_hbm_read(const void *buf, uint64_t bytes, uint32_t *sink, int32_t n_blocks, void *stream);

@@ -1,5 +1,5 @@
 // Achievable-peak probes of the device the layer runs on: a streaming HBM
-// read and a loop of the fp16 MFMA the expert FFN kernels use.  The layer's
+// read and a loop of dense fp16 MFMAs.  The layer's
 // roofline fractions are quoted against the data-sheet peaks and against
 // these measured ones (the pages give no hardware figure for this part).
 #include "moe_internal.h"
@@ -35,12 +35,15 @@ __global__ void __launch_bounds__(kReadThreads) hbm_read_kernel(const uint4 *__r
   if (acc == 0x9e3779b9u) sink[blockIdx.x] = acc;
 }
 
-constexpr int kMfmaChains = 8;  // independent accumulators per wave
+typedef float f16v __attribute__((ext_vector_type(16)));
 
-// Each wave runs `iters` rounds of kMfmaChains independent
-// v_mfma_f32_16x16x32_f16 on register operands (16,384 flops each).  The
-// operands change every round so that no result is loop-invariant; the sums
-// are stored only under a condition no run meets, which keeps them live.
+// Each wave runs `iters` rounds of 4 independent v_mfma_f32_32x32x16_f16 on
+// register operands (32,768 flops each; four chains are more than its
+// latency needs).  The operands are made opaque every round so that no result
+// is loop-invariant; the sums are stored only under a condition no run meets,
+// which keeps them live.  (This shape compiles to a loop of the four MFMAs
+// alone; eight 16x16x32 chains were compiled with accumulator copies between
+// the MFMAs, which measured the copies instead.)
 __global__ void __launch_bounds__(256) mfma_loop_kernel(int iters, float *__restrict__ sink) {
   h8 a, b;
 #pragma unroll
@@ -48,18 +51,22 @@ __global__ void __launch_bounds__(256) mfma_loop_kernel(int iters, float *__rest
     a[i] = (_Float16)(0.001f * (threadIdx.x + i));
     b[i] = (_Float16)(0.002f * (i - (int)threadIdx.x % 7));
   }
-  f4 acc[kMfmaChains];
+  f16v c0, c1, c2, c3;
 #pragma unroll
-  for (int c = 0; c < kMfmaChains; ++c) acc[c] = (f4){0.f, 0.f, 0.f, (float)c};
-  const h8 da = {(_Float16)1e-3f, 0, 0, 0, 0, 0, 0, 0};
-  for (int it = 0; it < iters; ++it) {
-#pragma unroll
-    for (int c = 0; c < kMfmaChains; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[c], 0, 0, 0);
-    a += da;
+  for (int i = 0; i < 16; ++i) {
+    c0[i] = 0.f;
+    c1[i] = 1.f;
+    c2[i] = 2.f;
+    c3[i] = 3.f;
   }
-  float s = 0.f;
-#pragma unroll
-  for (int c = 0; c < kMfmaChains; ++c) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+  for (int it = 0; it < iters; ++it) {
+    asm volatile("" : "+v"(a));
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c3, 0, 0, 0);
+  }
+  const float s = c0[0] + c1[5] + c2[10] + c3[15];
   if (s == -12345.678f) sink[blockIdx.x] = s;
 }
 
