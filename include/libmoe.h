@@ -31,7 +31,9 @@
  * wpr = ceil(cols/10) rounded up to a multiple of 4.  Weight (r, c) has code
  * q = (codes[r][c/10] >> sh(c%10)) & 7 with sh(j) = 3j for j < 5 and
  * 16 + 3(j-5) otherwise, and value (q - 4) * scales[r][c/32].  Unused code
- * slots and pad words are zero.
+ * slots and pad words are zero.  Block scales must satisfy
+ * 2^-14 <= |s| <= 255.875 or s = 0: the FFN kernels form f * fp16((q - 4) * s)
+ * with f = 1, 8 or 64, which leaves fp16's normal range outside it.
  */
 #ifndef LIBMOE_H
 #define LIBMOE_H

@@ -184,7 +184,8 @@ __global__ void __launch_bounds__(kBucketThreads) bucket_scan(int32_t *__restric
   if (e < E) off[e] = excl;
   if (e == 0) off[E] = total;
   __syncthreads();
-  if (e <= E) offsets[e] = off[e];
+  if (e < E) offsets[e] = off[e];
+  if (e == 0) offsets[E] = off[E];  // thread E does not exist when E == 1024
   if (build) build_work(cnt, off, E, T, entry_m, work, n_work, sh);
 }
 

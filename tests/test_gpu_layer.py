@@ -103,6 +103,51 @@ def test_tiny_k_extremes(k):
     layer.close()
 
 
+def _set_scales(layer, lo, hi, seed):
+    """Overwrite every block scale of the layer's blobs (routed and shared) with
+    seeded fp16 values of magnitude in [lo, hi] and random sign, on the GPU
+    pools and in the copies the oracle reads."""
+    rng = np.random.default_rng(seed)
+    secs, _stride = oracle.blob_sections(layer.d_model, layer.d_ff)
+    for e in range(layer.E + 1):
+        blob = layer.blob_np(e)
+        for _name, rows, cols, _co, so in secs:
+            n = rows * (cols // 32)
+            mag = rng.uniform(lo, hi, n) * rng.choice([-1.0, 1.0], n)
+            blob[so:so + 2 * n] = np.frombuffer(mag.astype(np.float16).tobytes(), dtype=np.uint8)
+        pool = layer.ctx.shared_pool[0] if e == layer.E else layer.ctx.slot_pool[e]
+        pool.copy_(torch.from_numpy(blob).to(pool.device))
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("path", [B.MOE_PATH_DECODE, B.MOE_PATH_PREFILL])
+@pytest.mark.parametrize("scales", ["large", "small"])
+def test_block_scale_range_edges(path, scales):
+    # the valid scale range is 2^-14 <= |s| <= 255.875: the kernels form
+    # f fp16((q - 4) s) with f up to 64 in the in-place code slots.  x and h
+    # travel as hi + lo fp16 halves of v / f, exact to ~2^-22 |v| while the lo
+    # half is a normal fp16 number (|v| >= 1/8) and to an absolute 2^-25
+    # below that: f 2^-25 = 2^-19 in x's units at f = 64.  Near 255.875
+    # (|w| ~ 440) h stays below fp16's overflow only for |x| <~ 0.01 at
+    # d_model 256 (h ~ (16 * 440 |x|)^2), so x there is a random sign times
+    # U(0.004, 0.008) -- v / f still normal -- and the floor is
+    # 2^-19 / 0.004 = 4.8e-4 of an element of x: tolerance 1e-3 against
+    # 'fp16_weights' (plus the exact bar).  The smallest scales take x ~ 1000
+    # and the usual 1e-4.
+    x = moe_synth.gen_x(7, 0, 9, TINY["d_model"])
+    if scales == "large":
+        lo, hi, tol = 128.0, 255.875, 1e-3
+        mag = np.random.default_rng(9).uniform(0.004, 0.008, x.shape)
+        x = (np.where(x < 0, -1.0, 1.0) * mag).astype(np.float32)
+    else:
+        lo, hi, tol = 2.0 ** -14, 2.0 ** -10, 1e-4
+        x = (x * 1e3).astype(np.float32)
+    layer = _layer(seed=7, T=9, x=x, **TINY)
+    _set_scales(layer, lo, hi, seed=8)
+    _check_layer(layer, path, "fp16_weights", tol)
+    layer.close()
+
+
 def test_real_layer_decode_T5():
     layer = _layer(T=5, **REAL)
     _check_layer(layer, B.MOE_PATH_DECODE, "fp16_weights", 1e-4)
@@ -191,6 +236,28 @@ def test_bucket_small_path_edges(case):
     B.moe_bucket(ctx.ctx, torch.from_numpy(idx).cuda(), T, off, perm)
     torch.cuda.synchronize()
     check_bucket(off.cpu().numpy(), perm.cpu().numpy(), idx, E)
+    ctx.close()
+
+
+@pytest.mark.parametrize("E", [1000, 1024])
+def test_bucket_large_path_expert_limit(E):
+    # the histogram/scan/scatter bucketing (> 1024 pairs) up to 1,024 experts:
+    # offsets[E] (the pair total) comes from thread 0, as no thread E exists
+    # at E = 1024; the output buffers start poisoned so an unwritten entry shows
+    from quantized_expert_ffn_softmax_amd.runtime import MoeContext
+    k, T = 10, 300
+    rng = np.random.default_rng(E)
+    idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    say(f"  bucketing past 1024 pairs: E={E} k={k} T={T}")
+    ctx = MoeContext(256, 128, E, k, 1, None, T)
+    off = torch.full((E + 1,), -7, dtype=torch.int32, device="cuda")
+    perm = torch.full((T * k,), -7, dtype=torch.int32, device="cuda")
+    B.moe_bucket(ctx.ctx, torch.from_numpy(idx).cuda(), T, off, perm)
+    off2, perm2 = torch.full_like(off, -9), torch.full_like(perm, -9)
+    B.moe_bucket_noalloc(torch.from_numpy(idx).cuda(), T, k, E, off2, perm2)
+    torch.cuda.synchronize()
+    check_bucket(off.cpu().numpy(), perm.cpu().numpy(), idx, E)
+    assert torch.equal(off, off2) and torch.equal(perm, perm2)
     ctx.close()
 
 
