@@ -222,6 +222,15 @@ def bench_stack(ctx, routers, biases, seed, d, f, L, T, W, K, use_graph, peaks):
     xa = torch.empty((T, d), dtype=torch.float32, device="cuda")
     xb = torch.empty_like(xa)
 
+    def step_fused(x0):
+        # the same layers, six launches each (moe_decode_layer)
+        x = x0
+        for l in range(L):
+            xn = xa if (l % 2 == 0) else xb
+            B.moe_decode_layer(c, l, x, T, routers[l], biases[l], None, buf["idx"], buf["w"], buf["y_pairs"],
+                               buf["y_shared"], buf["out"], xn)
+            x = xn
+
     def step(x0, ev=None):
         x = x0
         for l in range(L):
@@ -264,21 +273,22 @@ def bench_stack(ctx, routers, biases, seed, d, f, L, T, W, K, use_graph, peaks):
         f"call {ffn_avg_ms * 1e3:.1f} us for {bytes_per_call / 1e6:.1f} MB -> {achieved:.0f} GB/s; "
         f"distinct experts/layer {uniq / calls:.1f}")
 
-    # the same step captured once in a HIP graph (the deployable form of a
-    # fixed-shape decode step), replayed on fresh inputs copied in beforehand
-    graph_ms = None
-    if use_graph:
+    # the step captured once in a HIP graph (the deployable form of a
+    # fixed-shape decode step), replayed on fresh inputs copied in beforehand:
+    # first as the seven launches per layer of the separate calls, then as the
+    # six of moe_decode_layer (the headline)
+    def graph_time(fn):
         xin = torch.empty((T, d), dtype=torch.float32, device="cuda")
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
             xin.copy_(xs[0])
-            step(xin)
+            fn(xin)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            step(xin)
+            fn(xin)
         torch.cuda.synchronize()
         for s_ in range(W):
             xin.copy_(xs[s_])
@@ -291,9 +301,17 @@ def bench_stack(ctx, routers, biases, seed, d, f, L, T, W, K, use_graph, peaks):
             graph.replay()
             gev[s_][1].record()
         torch.cuda.synchronize()
-        graph_ms = float(np.mean([a.elapsed_time(b) for a, b in gev]))
         del graph
-        log(f"[bench] decode stack (graph): {graph_ms:.3f} ms/step, {T / (graph_ms * 1e-3):.0f} tok/s")
+        return float(np.mean([a.elapsed_time(b) for a, b in gev]))
+
+    graph_ms = sep_graph_ms = None
+    if use_graph:
+        sep_graph_ms = graph_time(step)
+        log(f"[bench] decode stack (graph, separate calls, 7 launches/layer): {sep_graph_ms:.3f} ms/step, "
+            f"{T / (sep_graph_ms * 1e-3):.0f} tok/s")
+        graph_ms = graph_time(step_fused)
+        log(f"[bench] decode stack (graph, moe_decode_layer, 6 launches/layer): {graph_ms:.3f} ms/step, "
+            f"{T / (graph_ms * 1e-3):.0f} tok/s")
     ms_per_step = graph_ms if graph_ms is not None else eager_ms
     roof = {"bound": "hbm", "kernel": "moe_expert_ffn (decode path)",
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -307,8 +325,14 @@ def bench_stack(ctx, routers, biases, seed, d, f, L, T, W, K, use_graph, peaks):
     if peaks is not None:
         roof["measured_peak"] = peaks["hbm_read_gbs"]
         roof["frac_of_measured"] = round(achieved / peaks["hbm_read_gbs"], 4)
-    return {"value": round(T / (ms_per_step * 1e-3), 1), "ms_per_step": round(ms_per_step, 4), "roofline": roof,
-            "eager_ms_per_step": round(eager_ms, 4), "step_mode": "hip_graph" if graph_ms is not None else "eager"}
+    res = {"value": round(T / (ms_per_step * 1e-3), 1), "ms_per_step": round(ms_per_step, 4), "roofline": roof,
+           "eager_ms_per_step": round(eager_ms, 4),
+           "step_mode": "hip_graph, moe_decode_layer (6 launches per layer)" if graph_ms is not None
+           else "eager, separate calls (7 launches per layer)"}
+    if sep_graph_ms is not None:
+        res["separate_calls_graph_ms_per_step"] = round(sep_graph_ms, 4)
+        res["separate_calls_tok_per_s"] = round(T / (sep_graph_ms * 1e-3), 1)
+    return res
 
 
 def bench_prefill(ctx, router, bias, seed, d, f, k, T, reps, peaks):

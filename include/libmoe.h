@@ -170,6 +170,27 @@ moe_status moe_expert_ffn(moe_ctx *ctx, int32_t layer, const float *x, int32_t T
 moe_status moe_combine(moe_ctx *ctx, const float *y_pairs, const float *w,
                        const float *y_shared, int32_t T, float *out, void *stream);
 
+/* One whole decode layer on a resident cache in six launches instead of the
+ * seven of the separate calls (the pages' engine has a fused-kernel mode,
+ * "融合核": "从一张到四张 RTX 4090 ...", section 调参：前后 40 多次重启):
+ * the router's two launches; one launch for the resident lookup count, the
+ * bucketing and the activation record; the two FFN kernels; the combine
+ * (and, with x_next, the normalisation that chains layers).  Results, bit for
+ * bit, and counters (moe_get_stats: lookups, hits, resolve calls) are those of
+ *   moe_route(ctx, layer, x, T, w_router, bias, logits, idx, w)
+ *   moe_cache_resolve(ctx, layer, idx, T, NULL, NULL)
+ *   moe_expert_ffn(ctx, layer, x, T, idx, NULL, y_pairs, y_shared, MOE_PATH_DECODE)
+ *   x_next ? moe_combine_norm(ctx, y_pairs, w, y_shared, T, out, x_next)
+ *          : moe_combine(ctx, y_pairs, w, y_shared, T, out).
+ * Arguments as there; logits and x_next may be NULL; x_next must differ from
+ * x and out.  Needs a resident cache (n_slots == n_layers * n_experts),
+ * T * top_k <= 1,024 and d_model, d_ff <= 2048; MOE_ERR_INVALID otherwise,
+ * nothing enqueued.  Asynchronous; uses the context's workspace. */
+moe_status moe_decode_layer(moe_ctx *ctx, int32_t layer, const float *x, int32_t T,
+                            const float *w_router, const float *bias, float *logits,
+                            int32_t *idx, float *w, float *y_pairs, float *y_shared,
+                            float *out, float *x_next, void *stream);
+
 /* --- observability and test support ------------------------------------- */
 
 /* Token -> expert bucketing as moe_expert_ffn does it internally:

@@ -71,6 +71,7 @@ _SIGS = {
     "moe_cache_resolve": (_I, [_P, _I, _P, _I, _P, ctypes.POINTER(moe_resolve_info), _P]),
     "moe_cache_resolve_async": (_I, [_P, _I, _P, _I, _P, _P]),
     "moe_combine_norm": (_I, [_P, _P, _P, _P, _I, _P, _P, _P]),
+    "moe_decode_layer": (_I, [_P, _I, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_expert_ffn": (_I, [_P, _I, _P, _I, _P, _P, _P, _P, _I, _P]),
     "moe_combine": (_I, [_P, _P, _P, _P, _I, _P, _P]),
     "moe_bucket": (_I, [_P, _P, _I, _P, _P, _P]),
@@ -214,6 +215,13 @@ def moe_get_stats(ctx) -> dict:
 def moe_combine_norm(ctx, y_pairs, w, y_shared, T, out, x_next, stream=None):
     _check(load().moe_combine_norm(ctx, _ptr(y_pairs), _ptr(w), _ptr(y_shared), T, _ptr(out), _ptr(x_next),
                                    _stream(stream)), "moe_combine_norm")
+
+
+def moe_decode_layer(ctx, layer, x, T, w_router, bias, logits, idx, w, y_pairs, y_shared, out, x_next=None,
+                     stream=None):
+    _check(load().moe_decode_layer(ctx, layer, _ptr(x), T, _ptr(w_router), _ptr(bias), _ptr(logits), _ptr(idx),
+                                   _ptr(w), _ptr(y_pairs), _ptr(y_shared), _ptr(out), _ptr(x_next), _stream(stream)),
+           "moe_decode_layer")
 
 
 def moe_chain_norm(ctx, out, T, x_next, stream=None):

@@ -391,3 +391,34 @@ extern "C" moe_status moe_combine_norm(moe_ctx *c, const float *y_pairs, const f
   if (e != hipSuccess) return moe_fail(MOE_ERR_HIP, std::string("moe_combine_norm: ") + hipGetErrorString(e));
   return MOE_OK;
 }
+
+extern "C" moe_status moe_decode_layer(moe_ctx *c, int32_t layer, const float *x, int32_t T, const float *w_router,
+                                       const float *bias, float *logits, int32_t *idx, float *w, float *y_pairs,
+                                       float *y_shared, float *out, float *x_next, void *stream) {
+  MOE_CHECK(c, MOE_ERR_INVALID, "moe_decode_layer: null ctx");
+  MOE_CHECK(c->resident, MOE_ERR_INVALID,
+            "moe_decode_layer: needs a resident cache (n_slots == n_layers * n_experts); a capped cache resolves "
+            "between the router and the FFN: use the separate calls");
+  MOE_CHECK(layer >= 0 && layer < c->cfg.n_layers, MOE_ERR_INVALID, "moe_decode_layer: layer out of range");
+  MOE_CHECK(T >= 1 && T <= c->cfg.max_tokens, MOE_ERR_INVALID, "moe_decode_layer: T must be 1..max_tokens");
+  MOE_CHECK(x && w_router && idx && w && y_pairs && y_shared && out, MOE_ERR_INVALID,
+            "moe_decode_layer: null x, w_router, idx, w, y_pairs, y_shared or out");
+  MOE_CHECK(aligned(x, 16) && aligned(w_router, 16) && aligned(y_pairs, 16) && aligned(y_shared, 16) &&
+                aligned(out, 16) && (!x_next || aligned(x_next, 16)),
+            MOE_ERR_ALIGN, "moe_decode_layer: x, w_router, y_pairs, y_shared, out and x_next must be 16-byte aligned");
+  MOE_CHECK(out != x_next && x != x_next, MOE_ERR_INVALID, "moe_decode_layer: x_next must differ from x and out");
+  MOE_CHECK(c->L.gate.nsb <= moe::kDecodeMaxNsb && c->L.down.nsb <= moe::kDecodeMaxNsb, MOE_ERR_INVALID,
+            "moe_decode_layer: the decode path takes d_model and d_ff up to 2048");
+  MOE_CHECK(T * c->cfg.top_k <= 1024 && c->cfg.n_experts <= 1024, MOE_ERR_INVALID,
+            "moe_decode_layer: needs T * top_k <= 1024");
+  hipStream_t s = as_stream(stream);
+  const int xh = moe::xrec_halves(c->L.gate.nsb);
+  hipError_t e = moe::launch_router(c, x, T, w_router, bias, logits ? logits : c->logits_ws, idx, w, s);
+  if (e == hipSuccess) e = moe::launch_bucket_lookup(c, idx, T, moe::kEntryTokens, x, c->xrec, xh, s);
+  if (e == hipSuccess) e = moe::launch_ffn_decode_kernels(c, layer, T, nullptr, y_pairs, y_shared, s);
+  if (e == hipSuccess)
+    e = x_next ? moe::launch_combine_norm(y_pairs, w, y_shared, T, c->cfg.top_k, c->cfg.d_model, out, x_next, s)
+               : moe::launch_combine(y_pairs, w, y_shared, T, c->cfg.top_k, c->cfg.d_model, out, s);
+  if (e != hipSuccess) return moe_fail(MOE_ERR_HIP, std::string("moe_decode_layer: ") + hipGetErrorString(e));
+  return MOE_OK;
+}

@@ -49,7 +49,7 @@ __device__ void build_work(const int *cnt_sh, const int *off_sh, int E, int T, i
   }
 }
 
-// n = T*k <= 1024 pairs, E <= 1024: workgroup 0 does the bucketing with
+// n = T*k <= 1024 pairs, E <= 1024: one workgroup does the bucketing with
 // blockDim.x >= max(n, E) threads (thread i holds pair i and expert i).
 //   1. each pair takes a slot in its expert by an LDS atomic (arrival order)
 //   2. one scan over the experts of (entries << 16 | pairs) gives the offsets
@@ -58,21 +58,17 @@ __device__ void build_work(const int *cnt_sh, const int *off_sh, int E, int T, i
 //      place is its rank among the ids of its segment: perm is the stable
 //      order (ascending expert, then ascending pair id), at a cost of the
 //      segment's length instead of the number of pairs.
-// The other workgroups of the launch build the record of x (decode path).
-__global__ void __launch_bounds__(kBucketThreads) bucket_small(const int32_t *__restrict__ idx, int n, int E, int T,
-                                                       int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
-                                                       int build, int entry_m, moe::WorkEntry *work,
-                                                       int32_t *n_work, const float *__restrict__ x, int d, int nsb,
-                                                       uint16_t *__restrict__ xrec, int xrec_h) {
+// idx may point to global memory or to LDS.  With nuniq (LDS, zeroed and
+// published by a barrier before the call) the number of experts with at least
+// one pair is added to it; every thread of the block must call this.
+__device__ void bucket_block(const int32_t *idx, int n, int E, int T, int32_t *__restrict__ offsets,
+                             int32_t *__restrict__ perm, int build, int entry_m, moe::WorkEntry *work,
+                             int32_t *n_work, int *nuniq) {
   __shared__ int cnt[1024];
   __shared__ int off[1024];
   __shared__ int ids[kSmallMax];
   __shared__ int wsum[kBucketThreads / 64];
   const int tid = threadIdx.x, nt = blockDim.x;
-  if (blockIdx.x > 0) {
-    moe::build_xrec_range(x, T, d, nsb, xrec, xrec_h, (blockIdx.x - 1) * nt + tid, (gridDim.x - 1) * nt);
-    return;
-  }
   const int lane = tid & 63, wave = tid >> 6, nwaves = nt >> 6;
   int ex = -1;
   if (tid < n) {
@@ -84,6 +80,10 @@ __global__ void __launch_bounds__(kBucketThreads) bucket_small(const int32_t *__
   const int slot = ex >= 0 ? atomicAdd(&cnt[ex], 1) : 0;
   __syncthreads();
   const int c = tid < E ? cnt[tid] : 0;
+  if (nuniq) {
+    const uint64_t used = __ballot(c > 0);
+    if (lane == 0 && used) atomicAdd(nuniq, __popcll(used));
+  }
   const int ne = build ? (c + entry_m - 1) / entry_m : 0;
   const int packed = (ne << 16) | c;
   const int incl = moe::wave_incl_scan(packed);
@@ -135,6 +135,37 @@ __global__ void __launch_bounds__(kBucketThreads) bucket_small(const int32_t *__
     int r = 0;
     for (int j = 0; j < len; ++j) r += ids[base + j] < tid;
     perm[base + r] = tid;
+  }
+}
+
+// Workgroup 0 buckets (bucket_block); the other workgroups of the launch
+// build the record of x (decode path).  With stats (a resident cache, whose
+// slots are the identities), workgroup 0 also records what the resolve
+// kernel records for a resident call: the number of distinct experts touched
+// as this call's lookups and hits, and one call -- so the lookup needs no
+// launch of its own.
+__global__ void __launch_bounds__(kBucketThreads) bucket_small(const int32_t *__restrict__ idx, int n, int E, int T,
+                                                       int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
+                                                       int build, int entry_m, moe::WorkEntry *work,
+                                                       int32_t *n_work, const float *__restrict__ x, int d, int nsb,
+                                                       uint16_t *__restrict__ xrec, int xrec_h,
+                                                       int32_t *__restrict__ dmiss, int64_t *__restrict__ stats) {
+  if (blockIdx.x > 0) {
+    moe::build_xrec_range(x, T, d, nsb, xrec, xrec_h, (blockIdx.x - 1) * blockDim.x + threadIdx.x,
+                          (gridDim.x - 1) * blockDim.x);
+    return;
+  }
+  __shared__ int nuniq_sh;
+  if (threadIdx.x == 0) nuniq_sh = 0;  // published by bucket_block's first barrier
+  bucket_block(idx, n, E, T, offsets, perm, build, entry_m, work, n_work, stats ? &nuniq_sh : nullptr);
+  if (stats && threadIdx.x == 0) {
+    const int nu = nuniq_sh;
+    dmiss[0] = nu;
+    dmiss[1] = 0;
+    dmiss[2] = 0;
+    atomicAdd(reinterpret_cast<unsigned long long *>(stats + 0), (unsigned long long)nu);
+    atomicAdd(reinterpret_cast<unsigned long long *>(stats + 1), (unsigned long long)nu);
+    atomicAdd(reinterpret_cast<unsigned long long *>(stats + 3), 1ull);
   }
 }
 
@@ -225,7 +256,8 @@ hipError_t launch_bucket_ex(const moe_ctx *c, const int32_t *idx, int T, int32_t
       blocks += (vals + nt - 1) / nt;
     }
     hipLaunchKernelGGL(bucket_small, dim3(blocks), dim3(nt), 0, s, idx, n, E, T, offsets, perm,
-                       build ? 1 : 0, entry_m, c->work, c->n_work, x, c->cfg.d_model, c->L.gate.nsb, xrec, xrec_h);
+                       build ? 1 : 0, entry_m, c->work, c->n_work, x, c->cfg.d_model, c->L.gate.nsb, xrec, xrec_h,
+                       (int32_t *)nullptr, (int64_t *)nullptr);
     return hipGetLastError();
   }
   const int nch = (n + kChunk - 1) / kChunk;
@@ -239,6 +271,18 @@ hipError_t launch_bucket_ex(const moe_ctx *c, const int32_t *idx, int T, int32_t
 hipError_t launch_bucket(const moe_ctx *c, const int32_t *idx, int T, int32_t *offsets, int32_t *perm, bool build,
                          hipStream_t s) {
   return launch_bucket_ex(c, idx, T, offsets, perm, build, 16, nullptr, nullptr, 0, s);
+}
+
+hipError_t launch_bucket_lookup(const moe_ctx *c, const int32_t *idx, int T, int entry_m, const float *x,
+                                uint16_t *xrec, int xrec_h, hipStream_t s) {
+  const int E = c->cfg.n_experts, n = T * c->cfg.top_k;
+  if (n > kSmallMax || E > 1024 || !c->resident) return hipErrorInvalidValue;
+  const int nt = ((n > E ? n : E) + 63) / 64 * 64;
+  const int vals = T * c->L.gate.nsb * moe::kSteps * 8;
+  const int blocks = 1 + (vals + nt - 1) / nt;
+  hipLaunchKernelGGL(bucket_small, dim3(blocks), dim3(nt), 0, s, idx, n, E, T, c->offsets_ws, c->perm_ws, 1, entry_m,
+                     c->work, c->n_work, x, c->cfg.d_model, c->L.gate.nsb, xrec, xrec_h, c->dmiss, c->dstats);
+  return hipGetLastError();
 }
 
 }  // namespace moe
@@ -297,7 +341,7 @@ extern "C" moe_status moe_bucket_noalloc(const int32_t *idx, int32_t T, int32_t 
     const int nt = ((n > E ? n : E) + 63) / 64 * 64;
     hipLaunchKernelGGL(bucket_small, dim3(1), dim3(nt), 0, s, idx, n, E, T, offsets, perm, 0, 1,
                        (moe::WorkEntry *)nullptr, (int32_t *)nullptr, (const float *)nullptr, 0, 0,
-                       (uint16_t *)nullptr, 0);
+                       (uint16_t *)nullptr, 0, (int32_t *)nullptr, (int64_t *)nullptr);
     MOE_HIP(hipGetLastError());
     return MOE_OK;
   }

@@ -70,4 +70,19 @@ __device__ inline float wave_sum(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// Top-k order of router logits as one 64-bit key: (the logit mapped to an
+// order-preserving uint32) << 32 | ~expert, so a larger key is a larger logit,
+// and equal logits order the lower expert index first; -0 and +0 are equal.
+// Every expert of a row has a distinct key; 0 orders after every real key.
+__device__ inline uint64_t order_key(float v, int e) {
+  const uint32_t b = v == 0.f ? 0u : __float_as_uint(v);
+  const uint32_t mono = (b & 0x80000000u) ? ~b : (b | 0x80000000u);  // larger float -> larger uint
+  return ((uint64_t)mono << 32) | (uint32_t)~(uint32_t)e;
+}
+__device__ inline float key_logit(uint64_t key) {
+  const uint32_t mono = (uint32_t)(key >> 32);
+  return __uint_as_float((mono & 0x80000000u) ? (mono & 0x7fffffffu) : ~mono);
+}
+__device__ inline int key_expert(uint64_t key) { return (int)~(uint32_t)key; }
+
 }  // namespace moe

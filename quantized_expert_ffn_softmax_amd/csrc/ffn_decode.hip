@@ -598,6 +598,14 @@ hipError_t launch_ffn_decode(const moe_ctx *c, int layer, const float *x, int T,
     hipLaunchKernelGGL(build_xrec_kernel, dim3((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096), dim3(256), 0, s, x,
                        T, k.d_model, c->L.gate.nsb, c->xrec, xh);
   }
+  return launch_ffn_decode_kernels(c, layer, T, slot_of_pair, y_pairs, y_shared, s);
+}
+
+hipError_t launch_ffn_decode_kernels(const moe_ctx *c, int layer, int T, const int32_t *slot_of_pair, float *y_pairs,
+                                     float *y_shared, hipStream_t s) {
+  const moe_config &k = c->cfg;
+  const int xh = xrec_halves(c->L.gate.nsb);
+  hipError_t e = hipSuccess;
   DecodeParams P;
   P.work = c->work;
   P.n_work = c->n_work;

@@ -152,6 +152,16 @@ hipError_t launch_resolve(moe_ctx *c, int layer, const int32_t *idx, int T, int3
 hipError_t decode_occupancy(moe_ctx *c);  // fills c->decode_occ for c's superblock counts
 hipError_t launch_ffn_decode(const moe_ctx *c, int layer, const float *x, int T, const int32_t *idx,
                              const int32_t *slot_of_pair, float *y_pairs, float *y_shared, hipStream_t s);
+// the decode FFN kernels alone, on the work list, perm and x record already
+// in the context's workspace (from launch_ffn_decode's bucketing or from
+// launch_route_bucket)
+hipError_t launch_ffn_decode_kernels(const moe_ctx *c, int layer, int T, const int32_t *slot_of_pair, float *y_pairs,
+                                     float *y_shared, hipStream_t s);
+// resident cache: the lookup count (as launch_resolve records it) + the
+// bucketing with its work list (entry_m) + the x record, in one launch;
+// T * top_k <= 1024, n_experts <= 1024
+hipError_t launch_bucket_lookup(const moe_ctx *c, const int32_t *idx, int T, int entry_m, const float *x,
+                                uint16_t *xrec, int xrec_h, hipStream_t s);
 hipError_t launch_ffn_prefill(const moe_ctx *c, int layer, const float *x, int T, const int32_t *idx,
                               const int32_t *slot_of_pair, float *y_pairs, float *y_shared, hipStream_t s);
 hipError_t launch_combine(const float *y_pairs, const float *w, const float *y_shared, int T, int k, int d,

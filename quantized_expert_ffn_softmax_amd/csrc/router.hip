@@ -4,6 +4,7 @@
 // The pages fix the shape (10 of 512 experts per token plus one shared
 // expert: "一张 RTX 4090 跑千亿模型，Strata 实测 155 tok/s", section
 // 如何做到：三层存储); the scoring function is the softmax reading.
+#include "device_util.h"
 #include "moe_internal.h"
 
 namespace {
@@ -264,11 +265,7 @@ __global__ void __launch_bounds__(64 * kRouteWaves) router_logits_mfma(const flo
 // for a candidate in the global top-k that rank is its global rank (every
 // expert ordered before it is a candidate too).  Weights: softmax of the k
 // chosen logits.
-__device__ inline uint64_t order_key(float v, int e) {
-  const uint32_t b = v == 0.f ? 0u : __float_as_uint(v);  // -0 and +0 are equal logits
-  const uint32_t mono = (b & 0x80000000u) ? ~b : (b | 0x80000000u);  // larger float -> larger uint
-  return ((uint64_t)mono << 32) | (uint32_t)~(uint32_t)e;               // equal logits: lower index larger
-}
+using moe::order_key;
 
 __global__ void __launch_bounds__(1024) router_finish_small(const float *__restrict__ part, int T, int E, int KS,
                                                             const float *__restrict__ bias, int k,
@@ -324,9 +321,8 @@ __global__ void __launch_bounds__(1024) router_finish_small(const float *__restr
       }
       if (nc & 1) r += ck[nc - 1] > ce;
       if (r < k) {
-        const uint32_t mono = (uint32_t)(ce >> 32);
-        top_v[r] = __uint_as_float((mono & 0x80000000u) ? (mono & 0x7fffffffu) : ~mono);
-        top_e[r] = (int)~(uint32_t)ce;
+        top_v[r] = moe::key_logit(ce);
+        top_e[r] = moe::key_expert(ce);
       }
     }
   }

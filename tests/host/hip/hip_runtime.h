@@ -20,6 +20,7 @@
 #include <ucontext.h>
 
 #include <algorithm>
+#include <cmath>
 #include <atomic>
 #include <cstdint>
 #include <cstdio>
@@ -71,6 +72,17 @@ template <typename T>
 inline hipError_t hipGetSymbolAddress(void **p, T &sym) {
   *p = (void *)&sym;
   return hipSuccess;
+}
+
+inline unsigned __float_as_uint(float f) {
+  unsigned u;
+  std::memcpy(&u, &f, 4);
+  return u;
+}
+inline float __uint_as_float(unsigned u) {
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
 }
 
 template <typename A, typename B>

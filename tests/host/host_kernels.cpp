@@ -10,6 +10,7 @@
 //   host_kernels bucket   E T k entry_m build d  in.bin out.bin
 //   host_kernels noalloc  E T k                  in.bin out.bin
 //   host_kernels resolve  L E S T k calls fill resident d_model d_ff  in.bin out.bin
+//   host_kernels bucket_lookup  E T k d_model  in.bin out.bin
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -229,6 +230,65 @@ int run_resolve(char **a) {
   return 0;
 }
 
+// The bucketing launch of a resident decode layer, which also records the
+// lookup (as the resolve kernel does for a resident call).  Input: idx [T][k],
+// x [T][d] (float32 bits).
+int run_bucket_lookup(char **a) {
+  const int E = std::atoi(a[0]), T = std::atoi(a[1]), k = std::atoi(a[2]), d = std::atoi(a[3]);
+  const char *in = a[4], *out = a[5];
+  const int n = T * k;
+  std::vector<int32_t> iv = read_i32(in, (size_t)n + (size_t)T * d);
+  moe_ctx c{};
+  c.cfg.n_experts = E;
+  c.cfg.top_k = k;
+  c.cfg.max_tokens = T;
+  c.cfg.d_model = d;
+  c.cfg.d_ff = 64;
+  c.cfg.n_layers = 1;
+  c.cfg.n_slots = E;
+  c.resident = true;
+  c.L = moe::make_layout(d, c.cfg.d_ff);
+  const Sizes z = ctx_sizes(T, k, E);
+  c.max_pairs = z.max_pairs;
+  c.max_work = z.max_work;
+  int32_t *idx = exact<int32_t>(n, 0);
+  std::memcpy(idx, iv.data(), (size_t)n * 4);
+  float *x = exact<float>((size_t)T * d, 0);
+  std::memcpy(x, iv.data() + n, (size_t)T * d * 4);
+  const int xh = moe::xrec_halves(c.L.gate.nsb);
+  const size_t xrec_n = (size_t)(T + 1) * xh;
+  uint16_t *xrec = exact<uint16_t>(xrec_n, 0);
+  c.dmiss = exact<int32_t>(3 + 2 * (size_t)z.max_pairs + 2 * (size_t)E, 0xa5);
+  c.dstats = exact<int64_t>(8, 0);
+  c.offsets_ws = exact<int32_t>(E + 1, 0xa5);
+  c.perm_ws = exact<int32_t>(z.max_pairs, 0xa5);
+  c.work = exact<moe::WorkEntry>(z.max_work, 0xa5);
+  c.n_work = exact<int32_t>(4, 0xa5);
+  for (int call = 0; call < 2; ++call)  // twice: the counters accumulate
+    if (moe::launch_bucket_lookup(&c, idx, T, moe::kEntryTokens, x, xrec, xh, (hipStream_t) nullptr) != hipSuccess)
+      die("launch_bucket_lookup refused the shape");
+  Out o(out);
+  o.put(c.offsets_ws, E + 1);
+  o.put(c.perm_ws, n);
+  const int nw = c.n_work[0];
+  if (nw < 0 || nw > z.max_work) die("n_work outside the work list");
+  o.put(c.n_work, 2);
+  o.put(reinterpret_cast<const int32_t *>(c.work), (size_t)nw * 4);
+  o.put(xrec, xrec_n);
+  o.put(c.dmiss, 3);
+  o.put(c.dstats, 6);
+  std::free(idx);
+  std::free(x);
+  std::free(xrec);
+  std::free(c.dmiss);
+  std::free(c.dstats);
+  std::free(c.offsets_ws);
+  std::free(c.perm_ws);
+  std::free(c.work);
+  std::free(c.n_work);
+  return 0;
+}
+
 }  // namespace
 
 int main(int argc, char **argv) {
@@ -240,5 +300,6 @@ int main(int argc, char **argv) {
   if (mode == "bucket" && argc == 10) return run_bucket(argv + 2);
   if (mode == "noalloc" && argc == 7) return run_noalloc(argv + 2);
   if (mode == "resolve" && argc == 14) return run_resolve(argv + 2);
+  if (mode == "bucket_lookup" && argc == 8) return run_bucket_lookup(argv + 2);
   die("bad arguments");
 }

@@ -321,3 +321,30 @@ def test_resolve_more_slots_than_threads(exe, tmp_path):
     per_call, stats, tail = _resolve(exe, tmp_path, L, E, S, T, k, calls, fill=1, dm=64, dff=64)
     orc = _check_lru(per_call, stats, tail, L, E, S, calls)
     assert int(np.sum(orc.id_of >= 0)) == S and orc.misses > S
+
+
+# ---------------------------------------------------------------------------
+# the bucketing launch of a resident decode layer, with its lookup count
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("E,T,k,d", [(512, 15, 10, 2048), (64, 128, 8, 96), (1024, 1, 1, 160)],
+                         ids=["decode_workload", "1024_pairs", "1024_experts"])
+def test_bucket_lookup(exe, tmp_path, E, T, k, d):
+    rng = np.random.default_rng(E + T)
+    idx = _routing(rng, T, k, E, zipf=0.8)
+    x = (rng.standard_normal((T, d)) * 2.0).astype(np.float32)
+    out = _Reader(_run(exe, tmp_path, ["bucket_lookup", E, T, k, d], [idx, x.view(np.int32)]))
+    counts, offsets, perm = _bucket_expected(idx, E)
+    assert np.array_equal(out.take(E + 1), offsets)
+    assert np.array_equal(out.take(T * k), perm)
+    n_work = out.take(2)
+    work, routed = _work_expected(counts, offsets, T, 4)
+    assert n_work.tolist() == [len(work), routed]
+    assert np.array_equal(out.take(len(work) * 4).reshape(-1, 4), work)
+    nsb = -(-d // 160)
+    assert np.array_equal(out.take((T + 1) * nsb * 320, np.uint16).reshape(T + 1, -1), _xrec_expected(x, nsb))
+    # what the resolve kernel records for a resident call, twice
+    nuniq = len(np.unique(idx))
+    assert out.take(3).tolist() == [nuniq, 0, 0]
+    assert out.take(6, np.int64).tolist() == [2 * nuniq, 2 * nuniq, 0, 2, 0, 0]
+    out.done()
