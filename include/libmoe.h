@@ -154,8 +154,9 @@ moe_status moe_cache_resolve_async(moe_ctx *ctx, int32_t layer, const int32_t *i
  * path: MOE_PATH_DECODE -- dequantised weights rounded once to fp16,
  * activations kept at fp32 accuracy (split in two fp16 halves), fp32
  * accumulation; takes d_model and d_ff up to 2048 (13 superblocks of 160
- * columns), MOE_ERR_INVALID above; MOE_PATH_PREFILL -- x, dequantised weights
- * and h each rounded to fp16, fp32 accumulation, needs d_model and d_ff to be
+ * columns), MOE_ERR_INVALID above; MOE_PATH_PREFILL -- the same precision
+ * (dequantised weights rounded once to fp16, x and h carried as two fp16
+ * halves, fp32 accumulation) as a grouped GEMM, needs d_model and d_ff to be
  * multiples of 64; MOE_PATH_AUTO -- decode for T <= 64 when the dims allow
  * it, prefill otherwise.  Expert ids outside [0, n_experts) are ignored
  * (their y_pairs rows are not written).  Uses the context's workspace: calls

@@ -290,8 +290,9 @@ def test_router_exact_ties(T):
 @pytest.mark.parametrize("shape,T", [("tiny", 8), ("real", 1), ("real", 15), ("real", 64), ("k20_d1088", 5),
                                      ("d8192", 3)])
 def test_combine_norm_equals_the_two_calls(shape, T):
-    # k20_d1088: more than 16 pair rows (the looped path) and a row whose last
-    # column pair is half past the end; d8192: eight columns per thread
+    # k20_d1088: more than 16 pair rows (the looped path) and a row whose
+    # columns end part-way through the threads; d8192: four float4 columns
+    # per thread
     dims = {"tiny": TINY, "real": REAL,
             "k20_d1088": dict(d_model=1088, d_ff=128, n_experts=64, top_k=20),
             "d8192": dict(d_model=8192, d_ff=128, n_experts=16, top_k=4)}[shape]
