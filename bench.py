@@ -460,10 +460,39 @@ def bench_lru(seed, d, f, E, k, L, routers, biases, shared_pool, warmup, steps):
     del dst
     log(f"[bench] lru: setup {time.time() - t0:.0f}s; pinned H2D peak {h2d_peak:.1f} GB/s")
 
-    def step(x0, zero_copy):
+    # the miss path's link rate through the library's own calls: from an empty
+    # cache, moe_cache_resolve_async calls whose ids all miss (1 or 10 distinct
+    # experts of a layer, never seen before), timed with events; bytes = the
+    # blobs the fill kernel copies, time = the call (resolve + fill kernels)
+    def fill_rate(n_miss, reps=8):
+        B.moe_cache_reset(c)
+        torch.cuda.synchronize()
+        ids = torch.empty((reps, 1, k), dtype=torch.int32, device="cuda")
+        for r in range(reps):
+            row = [(r * n_miss + j) % E for j in range(n_miss)]
+            row += [row[-1]] * (k - n_miss)  # repeats of the last id: n_miss distinct
+            ids[r, 0] = torch.tensor(row, dtype=torch.int32)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        st0 = B.moe_get_stats(c)
+        for r in range(reps):
+            ev[r][0].record()
+            B.moe_cache_resolve_async(c, 1 + r % (L - 1), ids[r], 1, buf["slot"])
+            ev[r][1].record()
+        torch.cuda.synchronize()
+        st1 = B.moe_get_stats(c)
+        assert st1["misses"] - st0["misses"] == reps * n_miss
+        us = float(np.median([a_.elapsed_time(b_) for a_, b_ in ev])) * 1e3
+        return {"misses_per_call": n_miss, "call_us": round(us, 1),
+                "gbs": round(n_miss * stride / (us * 1e-6) / 1e9, 2)}
+
+    fill_link = [fill_rate(1), fill_rate(10)]
+    log(f"[bench] lru: miss fill through moe_cache_resolve_async: " +
+        ", ".join(f"{r['misses_per_call']} blob(s) in {r['call_us']} us = {r['gbs']} GB/s" for r in fill_link))
+
+    def step(x0, zero_copy, bl=biases):
         x = x0
         for l in range(L):
-            B.moe_route(c, l, x, T, routers[l], biases[l], None, buf["idx"], buf["w"])
+            B.moe_route(c, l, x, T, routers[l], bl[l], None, buf["idx"], buf["w"])
             if zero_copy:
                 B.moe_cache_resolve_async(c, l, buf["idx"], T, buf["slot"])
             else:
@@ -476,7 +505,7 @@ def bench_lru(seed, d, f, E, k, L, routers, biases, shared_pool, warmup, steps):
 
     xs = [torch.from_numpy(moe_synth.gen_x(seed, 300000 + s, T, d)).cuda() for s in range(warmup + steps)]
 
-    def run(mode):
+    def run(mode, bl=biases, n_steps=steps):
         """Cold start (cache reset), warm-up steps, then the timed steps.
         'copy': moe_cache_resolve -- the host reads each layer's miss list back
         and copies the missed blobs with hipMemcpyAsync.  'zero_copy_graph':
@@ -490,7 +519,7 @@ def bench_lru(seed, d, f, E, k, L, routers, biases, shared_pool, warmup, steps):
             cs = torch.cuda.Stream()
             cs.wait_stream(torch.cuda.current_stream())
             with torch.cuda.graph(graph, stream=cs):
-                step(x_static, True)
+                step(x_static, True, bl)
             torch.cuda.synchronize()
 
             def one(x0):
@@ -498,14 +527,14 @@ def bench_lru(seed, d, f, E, k, L, routers, biases, shared_pool, warmup, steps):
                 graph.replay()
         else:
             def one(x0):
-                step(x0, False)
+                step(x0, False, bl)
         st0 = B.moe_get_stats(c)
         for s_ in range(warmup):
             one(xs[s_])
         torch.cuda.synchronize()
         st1 = B.moe_get_stats(c)
         t1 = time.time()
-        for s_ in range(steps):
+        for s_ in range(n_steps):
             one(xs[warmup + s_])
         torch.cuda.synchronize()
         wall = time.time() - t1
@@ -533,6 +562,24 @@ def bench_lru(seed, d, f, E, k, L, routers, biases, shared_pool, warmup, steps):
                          "h2d_gbs": round(h2d / cw / 1e9, 2)},
            "same_hits_and_misses": same,
            "timing": "host wall clock over the timed steps"}
+    out["fill_link"] = fill_link
+    # tok/s against hit rate: the same cache and steps under other Zipf skews
+    # of the router bias (the pages' hit rates, 94-99%, sit in this range)
+    sweep = []
+    for alpha in (0.5, 1.0):
+        bl = [torch.from_numpy(moe_synth.gen_bias(seed, l, E, alpha)).cuda() for l in range(L)]
+        n_sw = max(1, steps // 2)
+        w_, _s0, s1_, s2_ = run("zero_copy_graph", bl, n_sw)
+        lk, ht = s2_["lookups"] - s1_["lookups"], s2_["hits"] - s1_["hits"]
+        sweep.append({"zipf_alpha": alpha, "hit_rate": round(ht / max(1, lk), 4),
+                      "misses_per_token": round((lk - ht) / (T * n_sw), 2), "tok_per_s": round(T * n_sw / w_, 2),
+                      "ms_per_step": round(w_ / n_sw * 1e3, 3),
+                      "h2d_gbs": round((s2_["bytes_h2d"] - s1_["bytes_h2d"]) / w_ / 1e9, 2)})
+    sweep.insert(1, {"zipf_alpha": 0.75, "hit_rate": out["hit_rate"], "misses_per_token": out["misses_per_token"],
+                     "tok_per_s": out["tok_per_s"], "ms_per_step": out["ms_per_step"], "h2d_gbs": out["h2d_gbs"]})
+    out["hit_rate_sweep"] = sweep
+    log("[bench] lru: tok/s against hit rate: " +
+        ", ".join(f"alpha {r['zipf_alpha']}: hit {r['hit_rate']:.4f} -> {r['tok_per_s']} tok/s" for r in sweep))
     log(f"[bench] lru: zero-copy+graph {out['tok_per_s']} tok/s ({out['ms_per_step']} ms/step), copy path "
         f"{out['copy_path']['tok_per_s']} tok/s; hit rate {out['hit_rate']:.4f} (cold start {cold:.4f}), "
         f"{out['misses_per_token']} misses/token, H2D {out['h2d_gbs']} GB/s (peak {h2d_peak:.1f}); "
