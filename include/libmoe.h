@@ -192,6 +192,78 @@ moe_status moe_decode_layer(moe_ctx *ctx, int32_t layer, const float *x, int32_t
                             int32_t *idx, float *w, float *y_pairs, float *y_shared,
                             float *out, float *x_next, void *stream);
 
+/* --- KV tier --------------------------------------------------------------
+ * The pages' engine keeps the KV cache as int8 at 1,056 bytes per cell, locks
+ * only the first 32,768 of a layer's 131,072 cells in VRAM and streams the
+ * rest from pinned host RAM, with an optional prefetch ("单卡5090跑125B 大模型
+ * ...", section 2.2; "一张 RTX 4090 跑千亿模型，Strata 实测 155 tok/s",
+ * section 四个发现); it reports the share of block reads served from VRAM
+ * (section 7.2 of the first page: 98.8%).  The cell layout is not printed;
+ * the reading: `values` int8 codes in groups of 64, then one fp16 scale per
+ * group (1,024 values: 1,024 + 32 = 1,056 bytes); a group's scale is
+ * s = fp16(absmax / 127) and its codes q = clamp(rint(v / s), -127, 127)
+ * (float32 division, ties to even; s = 0 stores zero codes); a value reads
+ * back as q * s.  Cell c of a layer lives in HBM when c < cells_resident,
+ * else in host memory at index c - cells_resident.  The caller owns both
+ * stores; the handle owns a staging buffer of two slots of stage_cells cells
+ * and the counters.  One host thread uses a handle at a time. */
+typedef struct moe_kv moe_kv;
+
+typedef struct {
+  int32_t n_layers;
+  int32_t values;          /* per cell: 1,024, 2,048, 3,072 or 4,096 */
+  int32_t cells_total;     /* per layer */
+  int32_t cells_resident;  /* the first cells of each layer kept in HBM, 0..cells_total */
+  int32_t block_cells;     /* cells per block of the read accounting, >= 1 */
+  int32_t stage_cells;     /* capacity of each of the two staging slots, 1..cells_total */
+  void *resident;          /* device [n_layers][cells_resident][cell_bytes], 16-byte aligned */
+  void *host;              /* (host, pinned by hipHostMalloc) [n_layers][cells_total - cells_resident][cell_bytes] */
+} moe_kv_config;
+
+typedef struct {
+  int64_t cells_written;
+  int64_t cells_read;
+  int64_t block_reads;       /* blocks touched by reads (a read of a block's cells counts once) */
+  int64_t vram_block_reads;  /* of those, served entirely from HBM (resident or staged cells) */
+  int64_t host_bytes;        /* bytes reads took from host memory over the link */
+  int64_t prefetch_bytes;    /* bytes prefetches copied into the staging slots */
+} moe_kv_stats;
+
+/* Bytes per cell (values + 2 * values / 64), 0 for an unsupported `values`. */
+size_t moe_kv_cell_bytes(int32_t values);
+
+/* Validates cfg, maps `host` into the device address space and allocates the
+ * staging buffer.  MOE_ERR_INVALID for a bad cfg or a host buffer that is not
+ * mapped pinned memory; MOE_ERR_OOM if the staging buffer cannot be made. */
+moe_status moe_kv_create(const moe_kv_config *cfg, moe_kv **out);
+moe_status moe_kv_destroy(moe_kv *kv);
+
+/* Quantises vals [n][values] (device, fp32) into cells [first, first + n) of
+ * `layer`: resident cells in HBM, the others straight into host memory
+ * (stores over the link), and into a staging copy too when one holds them.
+ * Asynchronous on `stream`. */
+moe_status moe_kv_write(moe_kv *kv, int32_t layer, int32_t first, int32_t n,
+                        const float *vals, void *stream);
+
+/* Reads cells [first, first + n) of `layer` back into out [n][values]
+ * (device, fp32, q * s): resident cells from HBM, the others from a staging
+ * slot that holds them, else from host memory (loads over the link).  The
+ * block accounting (moe_kv_get_stats) is done at enqueue, from the staging
+ * state at that moment.  Asynchronous on `stream`. */
+moe_status moe_kv_read(moe_kv *kv, int32_t layer, int32_t first, int32_t n,
+                       float *out, void *stream);
+
+/* Brings the host cells of [first, first + n) (n <= stage_cells) into the
+ * older of the two staging slots by one hipMemcpyAsync on `stream`; reads
+ * enqueued after it use that copy.  The slot's previous range is dropped at
+ * enqueue: a read of it must be ordered before this call's copy (same stream,
+ * or an event), and a read of the new range after it.  Writes keep staged
+ * copies equal to host memory. */
+moe_status moe_kv_prefetch(moe_kv *kv, int32_t layer, int32_t first, int32_t n, void *stream);
+
+/* Cumulative counters (host state; no synchronisation). */
+moe_status moe_kv_get_stats(moe_kv *kv, moe_kv_stats *out);
+
 /* --- observability and test support ------------------------------------- */
 
 /* Token -> expert bucketing as moe_expert_ffn does it internally:

@@ -34,6 +34,7 @@ TAG_BLOB = 1
 TAG_ROUTER = 2
 TAG_BIAS = 3
 TAG_X = 4
+TAG_KV = 5
 
 BLOB_ALIGN = 256
 
@@ -162,6 +163,36 @@ def gen_x(seed: int, step: int, n_tokens: int, d_model: int) -> np.ndarray:
 # Workloads.  Sizes are those of the pages' engine (48 layers x 512 experts,
 # top-10 + 1 shared) at d_model=2048, d_ff=768, plus a tiny case for parity.
 # ---------------------------------------------------------------------------
+KV_BLOCK = 256  # cells drawn together (any split of a range gives the same values)
+
+
+def gen_kv(seed: int, layer: int, first: int, n: int, values: int = 1024) -> np.ndarray:
+    """KV cell values [n][values] float32 for cells first .. first + n - 1 of a
+    layer: Gaussian rows times a per-channel scale that is log-normal over the
+    channels (a few channels carry most of the magnitude, as attention keys
+    do), the same channel scales for every cell of the layer.  Every 97th cell
+    gets the special groups the quantiser has to get right: an all-zero group,
+    a group far below fp16's normal range, a group of multiples of 0.125 whose
+    largest is 31.75 (scale exactly 0.25: halves of the step are rounding
+    ties), and one group 1e4 larger than the rest."""
+    chan = np.exp(_rng(seed, TAG_KV, layer, 1 << 30).normal(0.0, 1.0, values)).astype(np.float32)
+    out = np.empty((n, values), dtype=np.float32)
+    b0, b1 = first // KV_BLOCK, (first + n - 1) // KV_BLOCK
+    for b in range(b0, b1 + 1):
+        rows = _rng(seed, TAG_KV, layer, b).standard_normal((KV_BLOCK, values)).astype(np.float32) * chan
+        lo, hi = max(first, b * KV_BLOCK), min(first + n, (b + 1) * KV_BLOCK)
+        out[lo - first:hi - first] = rows[lo - b * KV_BLOCK:hi - b * KV_BLOCK]
+    for c in range(-(-first // 97) * 97, first + n, 97):
+        v = out[c - first]
+        r = _rng(seed, TAG_KV, layer, (1 << 30) + 1 + c)
+        v[0:64] = 0.0
+        v[64:128] *= np.float32(1e-9)
+        v[128:192] = (np.round(r.uniform(-254.0, 254.0, 64)) / 8.0).astype(np.float32)
+        v[128] = np.float32(31.75)
+        v[192:256] *= np.float32(1e4)
+    return out
+
+
 WORKLOADS = {
     "tiny": dict(d_model=256, d_ff=128, n_experts=16, top_k=2, n_layers=1, n_tokens=8,
                  n_slots=None, alpha=0.0, steps=1),
@@ -173,4 +204,7 @@ WORKLOADS = {
                           n_slots=None, alpha=0.75, steps=1),
     "batched_decode_stack": dict(d_model=2048, d_ff=768, n_experts=512, top_k=10, n_layers=48, n_tokens=15,
                                  n_slots=None, alpha=0.75, steps=64),
+    # KV tier: 131,072 cells per layer, the first 32,768 resident, int8 cells
+    # of 1,024 values (1,056 bytes); read in 4,096-cell chunks
+    "kv_tier": dict(cells_total=131072, cells_resident=32768, values=1024, block_cells=256, chunk_cells=4096),
 }

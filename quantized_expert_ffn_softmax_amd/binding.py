@@ -55,6 +55,33 @@ class moe_resolve_info(ctypes.Structure):
         return {k: int(getattr(self, k)) for k, _ in self._fields_}
 
 
+class moe_kv_config(ctypes.Structure):
+    _fields_ = [
+        ("n_layers", ctypes.c_int32),
+        ("values", ctypes.c_int32),
+        ("cells_total", ctypes.c_int32),
+        ("cells_resident", ctypes.c_int32),
+        ("block_cells", ctypes.c_int32),
+        ("stage_cells", ctypes.c_int32),
+        ("resident", ctypes.c_void_p),
+        ("host", ctypes.c_void_p),
+    ]
+
+
+class moe_kv_stats(ctypes.Structure):
+    _fields_ = [
+        ("cells_written", ctypes.c_int64),
+        ("cells_read", ctypes.c_int64),
+        ("block_reads", ctypes.c_int64),
+        ("vram_block_reads", ctypes.c_int64),
+        ("host_bytes", ctypes.c_int64),
+        ("prefetch_bytes", ctypes.c_int64),
+    ]
+
+    def as_dict(self):
+        return {k: int(getattr(self, k)) for k, _ in self._fields_}
+
+
 class MoeError(RuntimeError):
     def __init__(self, status: int, where: str, detail: str):
         super().__init__(f"{where}: status {status} ({detail})")
@@ -82,6 +109,13 @@ _SIGS = {
     "moe_chain_norm": (_I, [_P, _P, _I, _P, _P]),
     "moe_peak_hbm_read": (_I, [_P, ctypes.c_uint64, _P, _I, _P]),
     "moe_peak_mfma_f16": (_I, [_I, _I, _P, _P]),
+    "moe_kv_cell_bytes": (ctypes.c_size_t, [_I]),
+    "moe_kv_create": (_I, [ctypes.POINTER(moe_kv_config), ctypes.POINTER(_P)]),
+    "moe_kv_destroy": (_I, [_P]),
+    "moe_kv_write": (_I, [_P, _I, _I, _I, _P, _P]),
+    "moe_kv_read": (_I, [_P, _I, _I, _I, _P, _P]),
+    "moe_kv_prefetch": (_I, [_P, _I, _I, _I, _P]),
+    "moe_kv_get_stats": (_I, [_P, ctypes.POINTER(moe_kv_stats)]),
     "moe_status_str": (ctypes.c_char_p, [_I]),
     "moe_last_error": (ctypes.c_char_p, []),
 }
@@ -248,3 +282,37 @@ def moe_peak_hbm_read(buf, nbytes, sink, n_blocks, stream=None):
 
 def moe_peak_mfma_f16(iters, n_blocks, sink, stream=None):
     _check(load().moe_peak_mfma_f16(iters, n_blocks, _ptr(sink), _stream(stream)), "moe_peak_mfma_f16")
+
+
+# --- KV tier ------------------------------------------------------------------
+
+def moe_kv_cell_bytes(values: int) -> int:
+    return int(load().moe_kv_cell_bytes(values))
+
+
+def moe_kv_create(cfg: moe_kv_config) -> int:
+    out = _P()
+    _check(load().moe_kv_create(ctypes.byref(cfg), ctypes.byref(out)), "moe_kv_create")
+    return out.value
+
+
+def moe_kv_destroy(kv: int) -> None:
+    _check(load().moe_kv_destroy(kv), "moe_kv_destroy")
+
+
+def moe_kv_write(kv, layer, first, n, vals, stream=None):
+    _check(load().moe_kv_write(kv, layer, first, n, _ptr(vals), _stream(stream)), "moe_kv_write")
+
+
+def moe_kv_read(kv, layer, first, n, out, stream=None):
+    _check(load().moe_kv_read(kv, layer, first, n, _ptr(out), _stream(stream)), "moe_kv_read")
+
+
+def moe_kv_prefetch(kv, layer, first, n, stream=None):
+    _check(load().moe_kv_prefetch(kv, layer, first, n, _stream(stream)), "moe_kv_prefetch")
+
+
+def moe_kv_get_stats(kv) -> dict:
+    st = moe_kv_stats()
+    _check(load().moe_kv_get_stats(kv, ctypes.byref(st)), "moe_kv_get_stats")
+    return st.as_dict()

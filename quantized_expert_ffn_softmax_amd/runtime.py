@@ -76,3 +76,27 @@ class MoeContext:
         B.moe_expert_ffn(self.ctx, layer, x, T, buf["idx"], slot, buf["y_pairs"], buf["y_shared"], path, stream)
         B.moe_combine(self.ctx, buf["y_pairs"], buf["w"], buf["y_shared"], T, buf["out"], stream)
         return ri
+
+
+class KvTier:
+    """The stores of a moe_kv handle, allocated with torch: the resident window
+    in device memory and the streamed cells in pinned host memory (torch's
+    pinned allocations come from hipHostMalloc, so the library can map them)."""
+
+    def __init__(self, n_layers, cells_total, cells_resident, values=1024, block_cells=256, stage_cells=4096,
+                 device="cuda:0"):
+        self.cb = B.moe_kv_cell_bytes(values)
+        if self.cb == 0:
+            raise ValueError("unsupported values per cell")
+        self.values, self.cells_total, self.cells_resident = values, cells_total, cells_resident
+        self.resident = torch.empty((n_layers, max(cells_resident, 1), self.cb), dtype=torch.uint8, device=device)
+        self.host = torch.empty((n_layers, max(cells_total - cells_resident, 1), self.cb), dtype=torch.uint8,
+                                pin_memory=True)
+        cfg = B.moe_kv_config(n_layers, values, cells_total, cells_resident, block_cells, stage_cells,
+                              self.resident.data_ptr(), self.host.data_ptr())
+        self.kv = B.moe_kv_create(cfg)
+
+    def close(self):
+        if self.kv:
+            B.moe_kv_destroy(self.kv)
+            self.kv = None
