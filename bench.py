@@ -75,6 +75,7 @@ def main():
     ap.add_argument("--no-layer", action="store_true", help="skip the single-layer T=5 decode measurement")
     ap.add_argument("--no-lru", action="store_true", help="skip the T=1 stack through the 8,445-slot LRU cache")
     ap.add_argument("--no-sweep", action="store_true", help="skip the speculative-verify batch sweep")
+    ap.add_argument("--no-kv", action="store_true", help="skip the KV-tier leg (131,072-cell context reads)")
     ap.add_argument("--no-stack", action="store_true",
                     help="skip the 48-layer decode stack (the headline figure is then null; for profiling other legs)")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured HBM-read and MFMA-loop peaks")
@@ -159,6 +160,8 @@ def main():
     if not args.no_lru:
         result["decode_lru"] = bench_lru(seed, d, f, E, k, L, routers, biases, shared_pool, args.lru_warmup,
                                          args.lru_steps)
+    if not args.no_kv:
+        result["kv_tier"] = bench_kv(seed, peaks)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(seed, d, f, E, k, T, alpha, args.cpu_sample_layers, args.warmup,
                                               prefill_T)
@@ -587,6 +590,130 @@ def bench_lru(seed, d, f, E, k, L, routers, biases, shared_pool, warmup, steps):
     ctx.close()
     del host, slot_pool
     return out
+
+
+def bench_kv(seed, peaks, reps=5):
+    """The KV tier at the pages' shape: one layer of 131,072 int8 cells of
+    1,024 values, the first 32,768 resident in HBM, the rest in pinned host
+    memory.  A whole-context read (what a prefill chunk's attention takes) in
+    4,096-cell chunks: without prefetch (host cells read over the link by the
+    read kernel) and with prefetch (the next host chunk DMA-copied into a
+    staging slot on a side stream while the current chunk is read).  Also
+    the read kernel alone on resident chunks against the HBM roofline, and the
+    write (quantise) rate."""
+    import numpy as np
+    import torch
+
+    import moe_synth
+    from quantized_expert_ffn_softmax_amd import binding as B
+    from quantized_expert_ffn_softmax_amd.runtime import KvTier
+    wl = moe_synth.WORKLOADS["kv_tier"]
+    total, R, V, blk, ch = wl["cells_total"], wl["cells_resident"], wl["values"], wl["block_cells"], wl["chunk_cells"]
+    big = 4 * ch  # the sweep is also run in chunks this size (larger DMA copies)
+    t = KvTier(1, total, R, V, blk, big)
+    kv, cb = t.kv, t.cb
+    src = torch.empty((ch, V), dtype=torch.float32, device="cuda")
+    wev = []
+    for first in range(0, total, ch):
+        src.copy_(torch.from_numpy(moe_synth.gen_kv(seed, 0, first, ch, V)))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        B.moe_kv_write(kv, 0, first, ch, src)
+        b.record()
+        wev.append((first, a, b))
+    torch.cuda.synchronize()
+    w_res = float(np.median([a.elapsed_time(b) for f_, a, b in wev if f_ < R]))
+    w_host = float(np.median([a.elapsed_time(b) for f_, a, b in wev if f_ >= R]))
+    out = torch.empty((big, V), dtype=torch.float32, device="cuda")
+    # reads and prefetches on two streams of their own (the default stream
+    # would serialise with the side stream)
+    main, side = torch.cuda.Stream(), torch.cuda.Stream()
+    main.wait_stream(torch.cuda.current_stream())
+
+    def context_read(prefetch, ch):
+        chunks = list(range(0, total, ch))
+        ev_read = {}
+        ev_pref = {}
+        if prefetch:
+            side.wait_stream(main)
+            first_host = [c for c in chunks if c >= R]
+            with torch.cuda.stream(side):
+                for c in first_host[:1]:
+                    B.moe_kv_prefetch(kv, 0, c, ch, side)
+                    ev_pref[c] = torch.cuda.Event()
+                    ev_pref[c].record(side)
+        for i, c in enumerate(chunks):
+            if prefetch and c in ev_pref:
+                main.wait_event(ev_pref[c])
+            B.moe_kv_read(kv, 0, c, ch, out, main)
+            ev_read[c] = torch.cuda.Event()
+            ev_read[c].record(main)
+            nxt = c + ch
+            if prefetch and nxt < total and nxt >= R and nxt not in ev_pref:
+                # the slot it takes held the chunk read two steps ago
+                prev = c - ch
+                if prev in ev_read:
+                    side.wait_event(ev_read[prev])
+                B.moe_kv_prefetch(kv, 0, nxt, ch, side)
+                ev_pref[nxt] = torch.cuda.Event()
+                ev_pref[nxt].record(side)
+
+    res = {}
+    # (the runs without prefetch first: a staging slot keeps its copy until a
+    # later prefetch replaces it, and reads use it)
+    for mode, csz in (("no_prefetch", ch), ("no_prefetch_16k", big), ("prefetch", ch), ("prefetch_16k", big)):
+        st0 = B.moe_kv_get_stats(kv)
+        context_read(mode.startswith("prefetch"), csz)  # warm-up
+        torch.cuda.synchronize()
+        st1 = B.moe_kv_get_stats(kv)
+        ms = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(main)
+            context_read(mode.startswith("prefetch"), csz)
+            b.record(main)
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        st2 = B.moe_kv_get_stats(kv)
+        blocks = st2["block_reads"] - st1["block_reads"]
+        m = float(np.median(ms))
+        res[mode] = {"chunk_cells": csz, "ms_per_context_read": round(m, 3), "cells_per_s": round(total / (m * 1e-3), 0),
+                     "cell_gbs": round(total * cb / (m * 1e-3) / 1e9, 1),
+                     "vram_block_read_rate": round((st2["vram_block_reads"] - st1["vram_block_reads"]) / blocks, 4),
+                     "host_gbs": round((st2["host_bytes"] - st1["host_bytes"]) / reps / (m * 1e-3) / 1e9, 2),
+                     "prefetch_gbs": round((st2["prefetch_bytes"] - st1["prefetch_bytes"]) / reps / (m * 1e-3) / 1e9,
+                                           2)}
+        del st0
+    # the read kernel alone on resident chunks: HBM-bound, 1,056 B in + 4,096 B out per cell
+    ev = []
+    torch.cuda.synchronize()
+    for r in range(reps * 2):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(main)
+        B.moe_kv_read(kv, 0, (r % (R // ch)) * ch, ch, out, main)
+        b.record(main)
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    rd = _median_ms(ev)
+    per_cell = cb + 4 * V
+    achieved = ch * per_cell / (rd * 1e-3) / 1e9
+    roof = {"bound": "hbm", "kernel": "kv_read_kernel (resident cells)", "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "bytes_per_launch": ch * per_cell, "avg_launch_us": round(rd * 1e3, 2)}
+    if peaks is not None:
+        roof["measured_peak"] = peaks["hbm_read_gbs"]
+        roof["frac_of_measured"] = round(achieved / peaks["hbm_read_gbs"], 4)
+    out_d = {"workload": "kv_tier", "cells_total": total, "cells_resident": R, "values_per_cell": V,
+             "cell_bytes": cb, "block_cells": blk, "chunk_cells": ch, "stage_cells": big,
+             "write_us_per_chunk": {"resident": round(w_res * 1e3, 1), "host": round(w_host * 1e3, 1)},
+             "write_host_gbs": round(ch * cb / (w_host * 1e-3) / 1e9, 2),
+             "context_read": res, "roofline": roof,
+             "timing": "HIP events on the read stream around each whole-context read (median of reps)"}
+    log("[bench] kv: context read " + ", ".join(
+        f"{k_}: {r_['ms_per_context_read']} ms ({r_['vram_block_read_rate']:.3f} of block reads from HBM)"
+        for k_, r_ in res.items()) + f"; resident read kernel {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.3f} of HBM peak)")
+    t.close()
+    return out_d
 
 
 def verify_sweep(ctx, routers, biases, seed, d, f, L, reps=5, warm=2):

@@ -11,9 +11,11 @@
 // 64, then one fp16 scale per group; s = fp16(absmax / 127),
 // q = clamp(rint(v / s), -127, 127), a value reads back as q * s.
 //
-// One wave per cell: lane l holds values 16 l .. 16 l + 15 of each
-// 1,024-value chunk, so a group of 64 values is four lanes (absmax by two
-// shuffles) and the lane's codes are one 16-byte store.
+// One wave per cell, in chunks of 1,024 values: at step q (0..3) of a chunk
+// lane l holds values 256 q + 4 l .. 256 q + 4 l + 3, so every load and store
+// instruction of the wave covers one contiguous span (1 KB of fp32, 256 B of
+// codes); a group of 64 values is 16 lanes of one step (absmax by four
+// shuffles).
 #include <mutex>
 
 #include "moe_internal.h"
@@ -58,7 +60,6 @@ __device__ inline uint8_t *staged_cell(const KvPlace &K, int c) {
 }
 
 typedef float f4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 // quantise cells [first, first + n) from vals [n][V] fp32
 __global__ void __launch_bounds__(64 * kKvWaves) kv_write_kernel(KvPlace K, int first, int n, int V,
@@ -70,21 +71,18 @@ __global__ void __launch_bounds__(64 * kKvWaves) kv_write_kernel(KvPlace K, int 
   uint8_t *dst = c < K.R ? resident_cell(K, c) : host_cell(K, c);
   uint8_t *dst2 = c < K.R ? nullptr : staged_cell(K, c);  // a staged copy is kept equal
   for (int j0 = 0; j0 < V; j0 += 1024) {
-    const f4 *src = reinterpret_cast<const f4 *>(vals + (size_t)i * V + j0 + 16 * lane);
     f4 v[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) v[q] = src[q];
-    float m = 0.f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      m = fmaxf(m, fmaxf(fmaxf(fabsf(v[q].x), fabsf(v[q].y)), fmaxf(fabsf(v[q].z), fabsf(v[q].w))));
-    m = fmaxf(m, __shfl_xor(m, 1, 64));
-    m = fmaxf(m, __shfl_xor(m, 2, 64));  // the group's absmax (lanes 4g .. 4g + 3)
-    const _Float16 s16 = (_Float16)(m / 127.0f);
-    const float s = (float)s16;
-    uint32_t w[4];
+    for (int q = 0; q < 4; ++q) v[q] = *reinterpret_cast<const f4 *>(vals + (size_t)i * V + j0 + 256 * q + 4 * lane);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
+      float m = fmaxf(fmaxf(fabsf(v[q].x), fabsf(v[q].y)), fmaxf(fabsf(v[q].z), fabsf(v[q].w)));
+      m = fmaxf(m, __shfl_xor(m, 1, 64));
+      m = fmaxf(m, __shfl_xor(m, 2, 64));
+      m = fmaxf(m, __shfl_xor(m, 4, 64));
+      m = fmaxf(m, __shfl_xor(m, 8, 64));  // the group's absmax (lanes 16 h .. 16 h + 15)
+      const _Float16 s16 = (_Float16)(m / 127.0f);
+      const float s = (float)s16;
       const float e[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
       uint32_t packed = 0;
 #pragma unroll
@@ -92,15 +90,14 @@ __global__ void __launch_bounds__(64 * kKvWaves) kv_write_kernel(KvPlace K, int 
         const float r = s == 0.f ? 0.f : fminf(fmaxf(rintf(e[t] / s), -127.f), 127.f);
         packed |= (uint32_t)(uint8_t)(int8_t)(int)r << (8 * t);
       }
-      w[q] = packed;
-    }
-    const u4 codes = {w[0], w[1], w[2], w[3]};
-    *reinterpret_cast<u4 *>(dst + j0 + 16 * lane) = codes;
-    if (dst2) *reinterpret_cast<u4 *>(dst2 + j0 + 16 * lane) = codes;
-    if ((lane & 3) == 0) {
-      const int g = (j0 + 16 * lane) / kKvGroup;
-      *reinterpret_cast<_Float16 *>(dst + V + 2 * g) = s16;
-      if (dst2) *reinterpret_cast<_Float16 *>(dst2 + V + 2 * g) = s16;
+      const int off = j0 + 256 * q + 4 * lane;
+      *reinterpret_cast<uint32_t *>(dst + off) = packed;
+      if (dst2) *reinterpret_cast<uint32_t *>(dst2 + off) = packed;
+      if ((lane & 15) == 0) {
+        const int g = off / kKvGroup;
+        *reinterpret_cast<_Float16 *>(dst + V + 2 * g) = s16;
+        if (dst2) *reinterpret_cast<_Float16 *>(dst2 + V + 2 * g) = s16;
+      }
     }
   }
 }
@@ -118,15 +115,19 @@ __global__ void __launch_bounds__(64 * kKvWaves) kv_read_kernel(KvPlace K, int f
   if (!src) src = staged_cell(K, c);
   if (!src) src = host_cell(K, c);
   for (int j0 = 0; j0 < V; j0 += 1024) {
-    const u4 codes = *reinterpret_cast<const u4 *>(src + j0 + 16 * lane);
-    const float s = (float)*reinterpret_cast<const _Float16 *>(src + V + 2 * ((j0 + 16 * lane) / kKvGroup));
-    f4 *o = reinterpret_cast<f4 *>(out + (size_t)i * V + j0 + 16 * lane);
+    uint32_t w[4];
+    float s[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint32_t wq = codes[q];
-      o[q] = (f4){(float)(int8_t)(wq & 0xff) * s, (float)(int8_t)((wq >> 8) & 0xff) * s,
-                  (float)(int8_t)((wq >> 16) & 0xff) * s, (float)(int8_t)(wq >> 24) * s};
+      const int off = j0 + 256 * q + 4 * lane;
+      w[q] = *reinterpret_cast<const uint32_t *>(src + off);
+      s[q] = (float)*reinterpret_cast<const _Float16 *>(src + V + 2 * (off / kKvGroup));
     }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<f4 *>(out + (size_t)i * V + j0 + 256 * q + 4 * lane) =
+          (f4){(float)(int8_t)(w[q] & 0xff) * s[q], (float)(int8_t)((w[q] >> 8) & 0xff) * s[q],
+               (float)(int8_t)((w[q] >> 16) & 0xff) * s[q], (float)(int8_t)(w[q] >> 24) * s[q]};
   }
 }
 
