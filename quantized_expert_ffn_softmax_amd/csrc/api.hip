@@ -50,7 +50,7 @@ static hipError_t dalloc(T **p, size_t n) {
 static void free_ctx(moe_ctx *c) {
   if (!c) return;
   void *dev[] = {c->slot_of, c->id_of, c->stamp, c->dstats, c->logits_ws, c->offsets_ws, c->perm_ws,
-                 c->chunk_ws, c->work, c->n_work, c->xrec, c->hrec, c->h16,
+                 c->chunk_ws, c->work, c->work8, c->n_work, c->xrec, c->hrec, c->h16,
                  c->slot_ws, c->dmiss, c->route_part};
   for (void *p : dev)
     if (p) (void)hipFree(p);
@@ -97,6 +97,8 @@ extern "C" moe_status moe_create(const moe_config *cfg, moe_ctx **out) {
   c->max_pairs = k.max_tokens * k.top_k;
   c->max_work = c->max_pairs / moe::kEntryTokens + (c->max_pairs < k.n_experts ? c->max_pairs : k.n_experts) +
                 k.max_tokens / moe::kEntryTokens + 4;
+  c->max_work8 = c->max_pairs / moe::kEntryTokens8 + (c->max_pairs < k.n_experts ? c->max_pairs : k.n_experts) +
+                 k.max_tokens / moe::kEntryTokens8 + 4;
   c->n_chunks_max = (c->max_pairs + 255) / 256;
   const int gsb = c->L.gate.nsb, dsb = c->L.down.nsb;
   if (e == hipSuccess) e = moe::decode_occupancy(c);
@@ -114,6 +116,7 @@ extern "C" moe_status moe_create(const moe_config *cfg, moe_ctx **out) {
   TRY(dalloc(&c->perm_ws, c->max_pairs));
   TRY(dalloc(&c->chunk_ws, (size_t)c->n_chunks_max * k.n_experts));
   TRY(dalloc(&c->work, c->max_work));
+  TRY(dalloc(&c->work8, c->max_work8));
   TRY(dalloc(&c->n_work, 4));
   // activation records carry one extra all-zero row (for MFMA columns without a token)
   const size_t xrec_n = (size_t)(k.max_tokens + 1) * moe::xrec_halves(gsb);

@@ -63,11 +63,12 @@ __device__ void build_work(const int *cnt_sh, const int *off_sh, int E, int T, i
 // one pair is added to it; every thread of the block must call this.
 __device__ void bucket_block(const int32_t *idx, int n, int E, int T, int32_t *__restrict__ offsets,
                              int32_t *__restrict__ perm, int build, int entry_m, moe::WorkEntry *work,
-                             int32_t *n_work, int *nuniq) {
+                             int32_t *n_work, int *nuniq, moe::WorkEntry *work8) {
   __shared__ int cnt[1024];
   __shared__ int off[1024];
   __shared__ int ids[kSmallMax];
   __shared__ int wsum[kBucketThreads / 64];
+  __shared__ int wsum8[kBucketThreads / 64];
   const int tid = threadIdx.x, nt = blockDim.x;
   const int lane = tid & 63, wave = tid >> 6, nwaves = nt >> 6;
   int ex = -1;
@@ -88,12 +89,18 @@ __device__ void bucket_block(const int32_t *idx, int n, int E, int T, int32_t *_
   const int packed = (ne << 16) | c;
   const int incl = moe::wave_incl_scan(packed);
   if (lane == 63) wsum[wave] = incl;
+  // the second list's entries per expert (8 pairs each), scanned alongside
+  const int ne8 = work8 ? (c + moe::kEntryTokens8 - 1) / moe::kEntryTokens8 : 0;
+  const int incl8 = moe::wave_incl_scan(ne8);
+  if (lane == 63) wsum8[wave] = incl8;
   __syncthreads();
-  int before = 0, total = 0;
+  int before = 0, total = 0, before8 = 0, total8 = 0;
   for (int w = 0; w < nwaves; ++w) {
-    const int v = wsum[w];
+    const int v = wsum[w], v8 = wsum8[w];
     before += w < wave ? v : 0;
     total += v;
+    before8 += w < wave ? v8 : 0;
+    total8 += v8;
   }
   const int excl = before + incl - packed;
   const int oe = excl & 0xffff, total_pairs = total & 0xffff;
@@ -126,6 +133,31 @@ __device__ void bucket_block(const int32_t *idx, int n, int E, int T, int32_t *_
       n_work[0] = total_ents + ns;
       n_work[1] = total_ents;
     }
+    if (work8) {
+      constexpr int m8 = moe::kEntryTokens8;
+      const int eb8 = before8 + incl8 - ne8;
+      for (int i = 0; i < ne8; ++i) {
+        moe::WorkEntry w;
+        w.expert = tid;
+        w.first = oe + i * m8;
+        w.m = min(m8, c - i * m8);
+        w.pad = 0;
+        work8[eb8 + i] = w;
+      }
+      const int ns8 = (T + m8 - 1) / m8;
+      for (int i = tid; i < ns8; i += nt) {
+        moe::WorkEntry w;
+        w.expert = -1;
+        w.first = i * m8;
+        w.m = min(m8, T - i * m8);
+        w.pad = 0;
+        work8[total8 + i] = w;
+      }
+      if (tid == 0) {
+        n_work[2] = total8 + ns8;
+        n_work[3] = total8;
+      }
+    }
   }
   __syncthreads();
   if (ex >= 0) ids[off[ex] + slot] = tid;
@@ -149,7 +181,8 @@ __global__ void __launch_bounds__(kBucketThreads) bucket_small(const int32_t *__
                                                        int build, int entry_m, moe::WorkEntry *work,
                                                        int32_t *n_work, const float *__restrict__ x, int d, int nsb,
                                                        uint16_t *__restrict__ xrec, int xrec_h,
-                                                       int32_t *__restrict__ dmiss, int64_t *__restrict__ stats) {
+                                                       int32_t *__restrict__ dmiss, int64_t *__restrict__ stats,
+                                                       moe::WorkEntry *work8) {
   if (blockIdx.x > 0) {
     moe::build_xrec_range(x, T, d, nsb, xrec, xrec_h, (blockIdx.x - 1) * blockDim.x + threadIdx.x,
                           (gridDim.x - 1) * blockDim.x);
@@ -157,7 +190,7 @@ __global__ void __launch_bounds__(kBucketThreads) bucket_small(const int32_t *__
   }
   __shared__ int nuniq_sh;
   if (threadIdx.x == 0) nuniq_sh = 0;  // published by bucket_block's first barrier
-  bucket_block(idx, n, E, T, offsets, perm, build, entry_m, work, n_work, stats ? &nuniq_sh : nullptr);
+  bucket_block(idx, n, E, T, offsets, perm, build, entry_m, work, n_work, stats ? &nuniq_sh : nullptr, work8);
   if (stats && threadIdx.x == 0) {
     const int nu = nuniq_sh;
     dmiss[0] = nu;
@@ -188,7 +221,7 @@ __global__ void __launch_bounds__(kChunk) bucket_hist(const int32_t *__restrict_
 // expert), writes offsets and builds the work list.
 __global__ void __launch_bounds__(kBucketThreads) bucket_scan(int32_t *__restrict__ chunk_cnt, int nchunks, int E, int T,
                                                       int32_t *__restrict__ offsets, int build, int entry_m,
-                                                      moe::WorkEntry *work, int32_t *n_work) {
+                                                      moe::WorkEntry *work, int32_t *n_work, moe::WorkEntry *work8) {
   __shared__ int cnt[1024];
   __shared__ int off[1025];
   __shared__ int sh[17];
@@ -218,6 +251,7 @@ __global__ void __launch_bounds__(kBucketThreads) bucket_scan(int32_t *__restric
   if (e < E) offsets[e] = off[e];
   if (e == 0) offsets[E] = off[E];  // thread E does not exist when E == 1024
   if (build) build_work(cnt, off, E, T, entry_m, work, n_work, sh);
+  if (build && work8) build_work(cnt, off, E, T, moe::kEntryTokens8, work8, n_work + 2, sh);
 }
 
 // Phase 3: stable scatter; rank inside the chunk by counting earlier equal ids.
@@ -243,7 +277,8 @@ __global__ void __launch_bounds__(kChunk) bucket_scatter(const int32_t *__restri
 namespace moe {
 
 hipError_t launch_bucket_ex(const moe_ctx *c, const int32_t *idx, int T, int32_t *offsets, int32_t *perm, bool build,
-                            int entry_m, const float *x, uint16_t *xrec, int xrec_h, hipStream_t s) {
+                            int entry_m, const float *x, uint16_t *xrec, int xrec_h, hipStream_t s,
+                            moe::WorkEntry *work8) {
   const int E = c->cfg.n_experts, n = T * c->cfg.top_k;
   if (n <= kSmallMax) {
     // one thread per pair and per expert; with x, 1 + enough workgroups to
@@ -257,20 +292,20 @@ hipError_t launch_bucket_ex(const moe_ctx *c, const int32_t *idx, int T, int32_t
     }
     hipLaunchKernelGGL(bucket_small, dim3(blocks), dim3(nt), 0, s, idx, n, E, T, offsets, perm,
                        build ? 1 : 0, entry_m, c->work, c->n_work, x, c->cfg.d_model, c->L.gate.nsb, xrec, xrec_h,
-                       (int32_t *)nullptr, (int64_t *)nullptr);
+                       (int32_t *)nullptr, (int64_t *)nullptr, work8);
     return hipGetLastError();
   }
   const int nch = (n + kChunk - 1) / kChunk;
   hipLaunchKernelGGL(bucket_hist, dim3(nch), dim3(kChunk), 0, s, idx, n, E, c->chunk_ws);
   hipLaunchKernelGGL(bucket_scan, dim3(1), dim3(kBucketThreads), 0, s, c->chunk_ws, nch, E, T, offsets, build ? 1 : 0,
-                     entry_m, c->work, c->n_work);
+                     entry_m, c->work, c->n_work, work8);
   hipLaunchKernelGGL(bucket_scatter, dim3(nch), dim3(kChunk), 0, s, idx, n, E, c->chunk_ws, offsets, perm);
   return hipGetLastError();
 }
 
 hipError_t launch_bucket(const moe_ctx *c, const int32_t *idx, int T, int32_t *offsets, int32_t *perm, bool build,
                          hipStream_t s) {
-  return launch_bucket_ex(c, idx, T, offsets, perm, build, 16, nullptr, nullptr, 0, s);
+  return launch_bucket_ex(c, idx, T, offsets, perm, build, 16, nullptr, nullptr, 0, s, nullptr);
 }
 
 hipError_t launch_bucket_lookup(const moe_ctx *c, const int32_t *idx, int T, int entry_m, const float *x,
@@ -281,7 +316,8 @@ hipError_t launch_bucket_lookup(const moe_ctx *c, const int32_t *idx, int T, int
   const int vals = T * c->L.gate.nsb * moe::kSteps * 8;
   const int blocks = 1 + (vals + nt - 1) / nt;
   hipLaunchKernelGGL(bucket_small, dim3(blocks), dim3(nt), 0, s, idx, n, E, T, c->offsets_ws, c->perm_ws, 1, entry_m,
-                     c->work, c->n_work, x, c->cfg.d_model, c->L.gate.nsb, xrec, xrec_h, c->dmiss, c->dstats);
+                     c->work, c->n_work, x, c->cfg.d_model, c->L.gate.nsb, xrec, xrec_h, c->dmiss, c->dstats,
+                     c->work8);
   return hipGetLastError();
 }
 
@@ -341,7 +377,7 @@ extern "C" moe_status moe_bucket_noalloc(const int32_t *idx, int32_t T, int32_t 
     const int nt = ((n > E ? n : E) + 63) / 64 * 64;
     hipLaunchKernelGGL(bucket_small, dim3(1), dim3(nt), 0, s, idx, n, E, T, offsets, perm, 0, 1,
                        (moe::WorkEntry *)nullptr, (int32_t *)nullptr, (const float *)nullptr, 0, 0,
-                       (uint16_t *)nullptr, 0, (int32_t *)nullptr, (int64_t *)nullptr);
+                       (uint16_t *)nullptr, 0, (int32_t *)nullptr, (int64_t *)nullptr, (moe::WorkEntry *)nullptr);
     MOE_HIP(hipGetLastError());
     return MOE_OK;
   }
@@ -350,7 +386,7 @@ extern "C" moe_status moe_bucket_noalloc(const int32_t *idx, int32_t T, int32_t 
   const int nch = (n + kChunk - 1) / kChunk;
   hipLaunchKernelGGL(bucket_hist, dim3(nch), dim3(kChunk), 0, s, idx, n, E, chunk);
   hipLaunchKernelGGL(bucket_scan, dim3(1), dim3(kBucketThreads), 0, s, chunk, nch, E, T, offsets, 0, 1,
-                     (moe::WorkEntry *)nullptr, (int32_t *)nullptr);
+                     (moe::WorkEntry *)nullptr, (int32_t *)nullptr, (moe::WorkEntry *)nullptr);
   hipLaunchKernelGGL(bucket_scatter, dim3(nch), dim3(kChunk), 0, s, idx, n, E, (const int32_t *)chunk,
                      (const int32_t *)offsets, perm);
   MOE_HIP(hipGetLastError());

@@ -34,8 +34,9 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 using moe::pair_col;
 
 struct DecodeParams {
-  const moe::WorkEntry *work;
-  const int32_t *n_work;
+  const moe::WorkEntry *work;   // entries of <= 4 tokens
+  const moe::WorkEntry *work8;  // entries of <= 8 tokens
+  const int32_t *n_work;        // [0]: entries of work, [2]: entries of work8
   const int32_t *perm;
   const int32_t *slot_of_pair;
   const uint8_t *slot_pool;
@@ -43,7 +44,7 @@ struct DecodeParams {
   uint32_t stride;
   int layer, E, k, T;
   int n_slots;
-  int max_work;  // bound on n_work[0] (workspace size)
+  int max_work, max_work8;  // bounds on n_work[0] and n_work[2] (workspace sizes)
   moe::MatLayout gate, up, down;
   const uint16_t *xrec;    // [T + 1][xrec_h], last row zero
   int xrec_h;
@@ -69,8 +70,8 @@ __device__ inline f4 mfma(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_1
 using moe::rec_pos;
 
 // a work entry is used only if it indexes inside this call's pairs / tokens
-__device__ inline bool entry_ok(const DecodeParams &P, const moe::WorkEntry &we) {
-  if (we.m < 1 || we.m > moe::kEntryTokens || we.first < 0) return false;
+__device__ inline bool entry_ok(const DecodeParams &P, const moe::WorkEntry &we, int cols) {
+  if (we.m < 1 || we.m > cols || we.first < 0) return false;
   return we.expert >= 0 ? (we.expert < P.E && we.first + we.m <= P.T * P.k) : (we.first + we.m <= P.T);
 }
 
@@ -118,8 +119,15 @@ __device__ inline bool entry_token(const DecodeParams &P, const moe::WorkEntry &
 constexpr int kWaves = 4;
 constexpr int kXcds = 8;      // accelerator dies of MI355X, each with its own L2
 constexpr int kSplitMaxTokens = 32;  // gate/up splits K over the waves up to this batch
-constexpr int kCols = moe::kEntryTokens;                 // entry columns held in LDS
-constexpr int kSbBytes = moe::kSteps * 2 * kCols * 16;   // one superblock of an entry's activations: 2,560 B
+// An entry of COLS tokens (4 or 8) fills MFMA B columns n (token n's hi
+// half) and n + COLS (its lo half); at COLS = 4 columns 8..15 repeat 0..7 and
+// their outputs are dropped.  In LDS a record step of the entry is 2 COLS
+// slots of 16 bytes (hi then lo, token-minor): SB bytes.
+template <int COLS>
+struct Cols {
+  static constexpr int SB = 2 * COLS * 16;        // bytes per record step
+  static constexpr int kSbBytes = moe::kSteps * SB;  // one superblock: 2,560 B at COLS = 4
+};
 
 struct Unit {
   const uint8_t *blob;  // the expert's blob (a readable stand-in when the entry is unusable)
@@ -154,11 +162,12 @@ __device__ inline Mats<NMAT> mats_of(const DecodeParams &P) {
   return Mt;
 }
 
+template <int COLS>
 __device__ inline void unit_setup(const DecodeParams &P, int u, int tpu, int tiles, int col, Unit &U) {
-  const moe::WorkEntry we = P.work[u / tpu];
+  const moe::WorkEntry we = (COLS == 8 ? P.work8 : P.work)[u / tpu];
   U.tile0 = (u % tpu) * tiles;
   U.routed = we.expert >= 0;
-  const uint8_t *blob = entry_ok(P, we) ? entry_blob(P, we) : nullptr;
+  const uint8_t *blob = entry_ok(P, we, COLS) ? entry_blob(P, we) : nullptr;
   U.m = blob ? we.m : 0;
   U.blob = blob ? blob : P.shared_pool + (size_t)P.layer * P.stride;
   U.tok = 0;
@@ -202,30 +211,30 @@ __host__ __device__ constexpr int sc_pitch(int nblk) {
 }
 
 // number of 16-byte-per-lane copies one thread issues for the unit's LDS data
-template <int NSB, int NMAT>
+template <int NSB, int NMAT, int COLS>
 struct CopyCounts {
-  static constexpr int act = (NSB * moe::kSteps * 2 * kCols + 64 * kWaves - 1) / (64 * kWaves);
+  static constexpr int act = (NSB * moe::kSteps * 2 * COLS + 64 * kWaves - 1) / (64 * kWaves);
   // scales: <= 64 rows x sc_pitch(nblk) per matrix, nblk <= 5 NSB
   static constexpr int sc = (64 * sc_pitch(5 * NSB + 8) + 16 * 64 * kWaves - 1) / (16 * 64 * kWaves);
 };
 
-// activation slot p = (superblock * 20 + step) * 8 + half * 4 + col holds the
-// 8 halves of that record step for entry column col
-template <int NSB, int NMAT>
+// activation slot p = (superblock * 20 + step) * 2 COLS + half * COLS + col
+// holds the 8 halves of that record step for entry column col
+template <int NSB, int NMAT, int COLS>
 __device__ inline void copy_unit_lds(const Mats<NMAT> &Mt, const Unit &U, int tid, uint32_t row_off, int unit_rows,
                                      int sc_mat_bytes, uint8_t *lact, uint8_t *lsc) {
   const uint8_t *rec = reinterpret_cast<const uint8_t *>(Mt.rec);
-  const int col = tid & 3, half = (tid >> 2) & 1, w = tid >> 6;
-  (void)col;
+  const int half = (tid / COLS) & 1, w = tid >> 6;
   const uint32_t a0 = lds_addr(lact) + 1024u * w;
 #pragma unroll
-  for (int i = 0; i < CopyCounts<NSB, NMAT>::act; ++i) {
+  for (int i = 0; i < CopyCounts<NSB, NMAT, COLS>::act; ++i) {
     const int p = tid + 64 * kWaves * i;
-    const int ms = p >> 3;
+    const int ms = p / (2 * COLS);
     // columns past the entry's tokens are not copied: an MFMA output column
     // depends only on its own B column and the epilogue writes only the
     // entry's tokens, so those slots may hold anything
-    if (U.has_tok && p < NSB * moe::kSteps * 2 * kCols) lds_copy16(rec + row_off + (ms * 16 + half * 8) * 2, a0 + 4096u * i);
+    if (U.has_tok && p < NSB * moe::kSteps * 2 * COLS)
+      lds_copy16(rec + row_off + (ms * 16 + half * 8) * 2, a0 + 4096u * i);
   }
   // scales: LDS row pitch sc_pitch(nblk) (see there); granule k of a matrix's
   // region holds 16 bytes of row k / (pitch / 16) -- the copy picks each
@@ -236,7 +245,7 @@ __device__ inline void copy_unit_lds(const Mats<NMAT> &Mt, const Unit &U, int ti
   for (int mat = 0; mat < NMAT; ++mat) {
     const uint8_t *src = U.blob + Mt.m[mat].scale_off + (uint32_t)U.tile0 * 16 * rb;
 #pragma unroll
-    for (int i = 0; i < CopyCounts<NSB, NMAT>::sc; ++i) {
+    for (int i = 0; i < CopyCounts<NSB, NMAT, COLS>::sc; ++i) {
       const int k = tid + 64 * kWaves * i;
       if (pitch == rb) {  // rows copied as they lie (any row size)
         if (16 * k < unit_rows * rb) lds_copy16(src + 16 * k, s0 + (uint32_t)(mat * sc_mat_bytes) + 4096u * i);
@@ -274,9 +283,9 @@ __device__ inline MatSb mat_sb(const uint4 &wq, const uint8_t *srow, int b, int 
   return M;
 }
 
-template <int NMAT, int t>
+template <int NMAT, int t, int COLS>
 __device__ inline void sb_step(const MatSb (&M)[NMAT], const Consts &K, const uint8_t *xb, f4 &acc0, f4 &acc1) {
-  const h8 x = lds_h8(xb + t * 128);
+  const h8 x = lds_h8(xb + t * Cols<COLS>::SB);
   if constexpr (NMAT == 2) {
     acc0 = mfma(quad_a<t>(M[0].w, K, M[0].P, M[0].Pm), x, acc0);
     acc1 = mfma(quad_a<t>(M[1].w, K, M[1].P, M[1].Pm), x, acc1);
@@ -288,20 +297,20 @@ __device__ inline void sb_step(const MatSb (&M)[NMAT], const Consts &K, const ui
 }
 
 // gate/up: h = silu(g) u into the h record; down: y
-template <int NMAT>
+template <int NMAT, int COLS>
 __device__ inline void unit_epilogue(const DecodeParams &P, const Unit &U, int w, int lane, f4 acc0, f4 acc1) {
   const int r16 = lane & 15, g = lane >> 4;
   const int rows = NMAT == 2 ? P.d_ff : P.d_model;
   const int rt = U.tile0 + w;
   // D layout: lane holds rows 4g + i of the tile for MFMA column r16; token
-  // n's value is column n (hi) + column n + 4 (lo)
+  // n's value is column n (hi) + column n + COLS (lo)
   if constexpr (NMAT == 1) acc0 += acc1;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    acc0[i] += __shfl_xor(acc0[i], 4, 64);
-    if constexpr (NMAT == 2) acc1[i] += __shfl_xor(acc1[i], 4, 64);
+    acc0[i] += __shfl_xor(acc0[i], COLS, 64);
+    if constexpr (NMAT == 2) acc1[i] += __shfl_xor(acc1[i], COLS, 64);
   }
-  if (!(U.has_tok && r16 < kCols && rt * 16 < rows)) return;
+  if (!(U.has_tok && r16 < COLS && rt * 16 < rows)) return;
   if constexpr (NMAT == 2) {
     uint16_t *hr = P.hrec + (size_t)U.rrow * P.hrec_h;
 #pragma unroll
@@ -366,7 +375,7 @@ __device__ inline void refill(uint4 (&W)[NSB][NMAT], const WordSrc<NSB, NMAT> &S
 // superblocks S and S + 1 together, their steps interleaved (twice the
 // independent dequantise-and-MFMA chains per wave); a last odd superblock
 // alone
-template <int NSB, int NMAT, int S>
+template <int NSB, int NMAT, int COLS, int S>
 __device__ inline void compute_pair(uint4 (&W)[NSB][NMAT], const WordSrc<NSB, NMAT> &Src,
                                     const uint8_t *(&srow)[NMAT], int g, int nblk, const uint32_t (&sel)[6],
                                     const Consts &K, const uint8_t *xb, f4 &acc0, f4 &acc1, f4 &acc2, f4 &acc3) {
@@ -378,39 +387,39 @@ __device__ inline void compute_pair(uint4 (&W)[NSB][NMAT], const WordSrc<NSB, NM
 #pragma unroll
   for (int mat = 0; mat < NMAT; ++mat) M[mat] = mat_sb<S + 2 >= NSB>(W[S][mat], srow[mat], 5 * S + g, nblk, sel);
   refill<NSB, NMAT, S>(W, Src);
-  const uint8_t *xs = xb + S * moe::kSteps * 128;
+  const uint8_t *xs = xb + S * Cols<COLS>::kSbBytes;
   if constexpr (S + 1 < NSB) {
     MatSb M2[NMAT];
 #pragma unroll
     for (int mat = 0; mat < NMAT; ++mat)
       M2[mat] = mat_sb<S + 3 >= NSB>(W[S + 1][mat], srow[mat], 5 * (S + 1) + g, nblk, sel);
     refill<NSB, NMAT, S + 1>(W, Src);
-    const uint8_t *xs2 = xs + moe::kSteps * 128;
-    sb_step<NMAT, 0>(M, K, xs, acc0, acc1);
-    sb_step<NMAT, 0>(M2, K, xs2, acc2, acc3);
-    sb_step<NMAT, 1>(M, K, xs, acc0, acc1);
-    sb_step<NMAT, 1>(M2, K, xs2, acc2, acc3);
-    sb_step<NMAT, 2>(M, K, xs, acc0, acc1);
-    sb_step<NMAT, 2>(M2, K, xs2, acc2, acc3);
-    sb_step<NMAT, 3>(M, K, xs, acc0, acc1);
-    sb_step<NMAT, 3>(M2, K, xs2, acc2, acc3);
-    sb_step<NMAT, 4>(M, K, xs, acc0, acc1);
-    sb_step<NMAT, 4>(M2, K, xs2, acc2, acc3);
+    const uint8_t *xs2 = xs + Cols<COLS>::kSbBytes;
+    sb_step<NMAT, 0, COLS>(M, K, xs, acc0, acc1);
+    sb_step<NMAT, 0, COLS>(M2, K, xs2, acc2, acc3);
+    sb_step<NMAT, 1, COLS>(M, K, xs, acc0, acc1);
+    sb_step<NMAT, 1, COLS>(M2, K, xs2, acc2, acc3);
+    sb_step<NMAT, 2, COLS>(M, K, xs, acc0, acc1);
+    sb_step<NMAT, 2, COLS>(M2, K, xs2, acc2, acc3);
+    sb_step<NMAT, 3, COLS>(M, K, xs, acc0, acc1);
+    sb_step<NMAT, 3, COLS>(M2, K, xs2, acc2, acc3);
+    sb_step<NMAT, 4, COLS>(M, K, xs, acc0, acc1);
+    sb_step<NMAT, 4, COLS>(M2, K, xs2, acc2, acc3);
   } else {
-    sb_step<NMAT, 0>(M, K, xs, acc0, acc1);
-    sb_step<NMAT, 1>(M, K, xs, acc0, acc1);
-    sb_step<NMAT, 2>(M, K, xs, acc0, acc1);
-    sb_step<NMAT, 3>(M, K, xs, acc0, acc1);
-    sb_step<NMAT, 4>(M, K, xs, acc0, acc1);
+    sb_step<NMAT, 0, COLS>(M, K, xs, acc0, acc1);
+    sb_step<NMAT, 1, COLS>(M, K, xs, acc0, acc1);
+    sb_step<NMAT, 2, COLS>(M, K, xs, acc0, acc1);
+    sb_step<NMAT, 3, COLS>(M, K, xs, acc0, acc1);
+    sb_step<NMAT, 4, COLS>(M, K, xs, acc0, acc1);
   }
 }
 
-template <int NSB, int NMAT, int... Ps>
+template <int NSB, int NMAT, int COLS, int... Ps>
 __device__ inline void compute_all(std::integer_sequence<int, Ps...>, uint4 (&W)[NSB][NMAT],
                                    const WordSrc<NSB, NMAT> &Src, const uint8_t *(&srow)[NMAT], int g, int nblk,
                                    const uint32_t (&sel)[6], const Consts &K, const uint8_t *xb, f4 &acc0, f4 &acc1,
                                    f4 &acc2, f4 &acc3) {
-  (compute_pair<NSB, NMAT, 2 * Ps>(W, Src, srow, g, nblk, sel, K, xb, acc0, acc1, acc2, acc3), ...);
+  (compute_pair<NSB, NMAT, COLS, 2 * Ps>(W, Src, srow, g, nblk, sel, K, xb, acc0, acc1, acc2, acc3), ...);
 }
 
 // KS = 2 (gate/up of small batches): K split in two halves over the waves of a
@@ -418,12 +427,13 @@ __device__ inline void compute_all(std::integer_sequence<int, Ps...>, uint4 (&W)
 // [h H, min((h + 1) H, NSB)) with H = ceil(NSB / 2) -- and the halves' sums
 // added through LDS before the epilogue.  Twice the waves in flight and half
 // the chain per wave, for batches whose units leave CUs idle.
-template <int NSB, int NMAT, int KS>
+template <int NSB, int NMAT, int KS, int COLS>
 __global__ void __launch_bounds__(64 * kWaves, NMAT == 2 ? 3 : 4) ffn_decode_kernel(DecodeParams P) {
   static_assert(KS == 1 || (NMAT == 2 && ((NSB + 1) / 2) % 2 == 1), "K split: gate/up, an odd half length");
+  static_assert(COLS == 4 || COLS == 8, "entries of 4 or 8 tokens");
   constexpr int NS = KS == 2 ? (NSB + 1) / 2 : NSB;  // superblocks of a wave's range
   constexpr int kTiles = kWaves / KS;                 // 16-row tiles of a unit
-  constexpr int kActBytes = NSB * kSbBytes;
+  constexpr int kActBytes = NSB * Cols<COLS>::kSbBytes;
   constexpr int kScMat = 16 * kTiles * sc_pitch(5 * NSB + 8);  // one matrix's scales of the unit's rows (nblk <= 5 NSB)
   constexpr int kScBytes = NMAT * kScMat;
   __shared__ __attribute__((aligned(1024))) uint8_t lact[kActBytes];
@@ -438,7 +448,7 @@ __global__ void __launch_bounds__(64 * kWaves, NMAT == 2 ? 3 : 4) ffn_decode_ker
   const int ntile = Mt.m[0].rows / 16;
   const int tpu = (ntile + kTiles - 1) / kTiles;
   const int nblk = Mt.m[0].nblk;
-  const int n_units = min(P.n_work[0], P.max_work) * tpu;
+  const int n_units = (COLS == 8 ? min(P.n_work[2], P.max_work8) : min(P.n_work[0], P.max_work)) * tpu;
   // Workgroup b runs on XCD b % 8 (round-robin dispatch).  Each XCD takes a
   // contiguous range of units, so the tiles of neighbouring entries -- the
   // entries of an expert with more than 4 tokens, or of the shared expert --
@@ -449,18 +459,20 @@ __global__ void __launch_bounds__(64 * kWaves, NMAT == 2 ? 3 : 4) ffn_decode_ker
   const Consts K = make_consts();
   uint32_t sel[6];
   moe::pattern_selectors(g, sel);
-  // B operand of lane (j, g) at step t of superblock S: slot ((20 S + 5 g +
-  // t) * 2 + (j & 7) / 4) * 4 + j % 4, i.e. byte (20 S + t) * 128 + 640 g +
-  // 16 (j & 7); the wave's range starts at superblock sb0
-  const uint8_t *xb = lact + 640 * g + 16 * (r16 & 7) + sb0 * moe::kSteps * 128;
+  // B operand of lane (j, g) at step t of superblock S: record step
+  // ms = 20 S + 5 g + t, slot ms * 2 COLS + (j mod 2 COLS), i.e. byte
+  // (20 S + t) * SB + 5 SB g + 16 (j mod 2 COLS); the wave's range starts at
+  // superblock sb0
+  constexpr int SB = Cols<COLS>::SB;
+  const uint8_t *xb = lact + 5 * SB * g + 16 * (r16 & (2 * COLS - 1)) + sb0 * moe::kSteps * SB;
   bool first = true;
   for (int u = xcd * per + blockIdx.x / kXcds; u < u_end; u += u_step) {
     if (!first) __syncthreads();  // every wave is done with the previous unit's LDS data
     first = false;
     Unit U;
-    unit_setup(P, u, tpu, kTiles, tid & 3, U);
+    unit_setup<COLS>(P, u, tpu, kTiles, tid & (COLS - 1), U);
     const uint32_t row_off = (uint32_t)(NMAT == 2 ? U.tok : U.rrow) * (uint32_t)Mt.rec_h * 2u;
-    copy_unit_lds<NSB, NMAT>(Mt, U, tid, row_off, 16 * kTiles, kScMat, lact, lsc);
+    copy_unit_lds<NSB, NMAT, COLS>(Mt, U, tid, row_off, 16 * kTiles, kScMat, lact, lsc);
     // the word quads of this wave's rows, as many superblocks as fit
     const int row = min((U.tile0 + ltile) * 16 + r16, Mt.m[0].rows - 1);
     WordSrc<NS, NMAT> Src;
@@ -481,8 +493,8 @@ __global__ void __launch_bounds__(64 * kWaves, NMAT == 2 ? 3 : 4) ffn_decode_ker
     for (int mat = 0; mat < NMAT; ++mat)
       srow[mat] = lsc + mat * kScMat + (ltile * 16 + r16) * sc_pitch(nblk);
     f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f}, acc2 = acc0, acc3 = acc0;
-    compute_all<NS, NMAT>(std::make_integer_sequence<int, (NS + 1) / 2>{}, W, Src, srow, 5 * sb0 + g, nblk, sel, K,
-                          xb, acc0, acc1, acc2, acc3);
+    compute_all<NS, NMAT, COLS>(std::make_integer_sequence<int, (NS + 1) / 2>{}, W, Src, srow, 5 * sb0 + g, nblk,
+                                sel, K, xb, acc0, acc1, acc2, acc3);
     acc0 += acc2;
     acc1 += acc3;
     if constexpr (KS == 2) {
@@ -496,7 +508,7 @@ __global__ void __launch_bounds__(64 * kWaves, NMAT == 2 ? 3 : 4) ffn_decode_ker
       acc0 += red[(ltile * 64 + lane) * 2 + 0];
       acc1 += red[(ltile * 64 + lane) * 2 + 1];
     }
-    unit_epilogue<NMAT>(P, U, ltile, lane, acc0, acc1);
+    unit_epilogue<NMAT, COLS>(P, U, ltile, lane, acc0, acc1);
   }
 }
 
@@ -514,19 +526,29 @@ inline int max_entries(int T, int k, int E, int entry_m) {
 }
 
 
+// Tokens per work entry of each matrix: gate/up keeps 4 (its unit holds the
+// entry's whole x record in LDS: 8 tokens at 13 superblocks would leave room
+// for one workgroup per CU); down takes 8 (a 5-superblock h record), so every
+// MFMA column is in use and an expert with 5..8 tokens is one entry.
+template <int NMAT>
+constexpr int cols_of() {
+  return NMAT == 2 ? moe::kEntryTokens : moe::kEntryTokens8;
+}
+
 // one unit (entry x 4 tiles) per workgroup while that fits in the workgroups
 // the CUs hold at once; beyond, workgroups loop over units
 template <int NSB, int NMAT, int KS = 1>
 hipError_t launch_decode_nsb(const DecodeParams &P, int units, int per_cu, int n_cu, hipStream_t s) {
   const int cap = (per_cu > 0 ? per_cu : 1) * (n_cu > 0 ? n_cu : 1);
   const int grid = (std::min(units, cap) + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL((ffn_decode_kernel<NSB, NMAT, KS>), dim3(grid), dim3(64 * kWaves), 0, s, P);
+  hipLaunchKernelGGL((ffn_decode_kernel<NSB, NMAT, KS, cols_of<NMAT>()>), dim3(grid), dim3(64 * kWaves), 0, s, P);
   return hipGetLastError();
 }
 
 template <int NSB, int NMAT, int KS = 1>
 hipError_t occupancy_nsb(int *occ) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, ffn_decode_kernel<NSB, NMAT, KS>, 64 * kWaves, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, ffn_decode_kernel<NSB, NMAT, KS, cols_of<NMAT>()>,
+                                                      64 * kWaves, 0);
 }
 
 // the kernel built for nsb superblocks: F<NSB>() for nsb = 1..13
@@ -573,9 +595,6 @@ struct OccMat {
 
 namespace moe {
 
-hipError_t launch_bucket_ex(const moe_ctx *c, const int32_t *idx, int T, int32_t *offsets, int32_t *perm, bool build,
-                            int entry_m, const float *x, uint16_t *xrec, int xrec_h, hipStream_t s);
-
 hipError_t decode_occupancy(moe_ctx *c) {
   c->decode_occ[0] = c->decode_occ[1] = c->decode_occ[2] = 1;
   // widths the decode kernels are not built for take the prefill path only
@@ -591,7 +610,8 @@ hipError_t launch_ffn_decode(const moe_ctx *c, int layer, const float *x, int T,
   const moe_config &k = c->cfg;
   const int xh = xrec_halves(c->L.gate.nsb);
   // bucketing, work list and (on the single-workgroup path) the x record in one launch
-  hipError_t e = launch_bucket_ex(c, idx, T, c->offsets_ws, c->perm_ws, true, moe::kEntryTokens, x, c->xrec, xh, s);
+  hipError_t e =
+      launch_bucket_ex(c, idx, T, c->offsets_ws, c->perm_ws, true, moe::kEntryTokens, x, c->xrec, xh, s, c->work8);
   if (e != hipSuccess) return e;
   if (T * k.top_k > 1024) {
     const int n = T * c->L.gate.nsb * kSteps * 8;
@@ -608,6 +628,7 @@ hipError_t launch_ffn_decode_kernels(const moe_ctx *c, int layer, int T, const i
   hipError_t e = hipSuccess;
   DecodeParams P;
   P.work = c->work;
+  P.work8 = c->work8;
   P.n_work = c->n_work;
   P.perm = c->perm_ws;
   P.slot_of_pair = slot_of_pair;
@@ -617,6 +638,7 @@ hipError_t launch_ffn_decode_kernels(const moe_ctx *c, int layer, int T, const i
   P.layer = layer;
   P.n_slots = k.n_slots;
   P.max_work = c->max_work;
+  P.max_work8 = c->max_work8;
   P.E = k.n_experts;
   P.k = k.top_k;
   P.T = T;
@@ -633,8 +655,9 @@ hipError_t launch_ffn_decode_kernels(const moe_ctx *c, int layer, int T, const i
   P.y_shared = y_shared;
   P.d_model = k.d_model;
   P.d_ff = k.d_ff;
-  const int ents = max_entries(T, k.top_k, k.n_experts, moe::kEntryTokens);
-  const int u1 = ents * ((k.d_ff / 16 + kWaves - 1) / kWaves), u2 = ents * ((k.d_model / 16 + kWaves - 1) / kWaves);
+  const int ents = max_entries(T, k.top_k, k.n_experts, cols_of<2>());
+  const int ents_d = max_entries(T, k.top_k, k.n_experts, cols_of<1>());
+  const int u1 = ents * ((k.d_ff / 16 + kWaves - 1) / kWaves), u2 = ents_d * ((k.d_model / 16 + kWaves - 1) / kWaves);
   // Small batches (a single request's 1 + 4 verified tokens, ~30 entries)
   // leave most CUs idle in gate/up: split its K over the waves instead.  Up
   // to 32 tokens the split is also ahead on average (half-length chains in

@@ -426,14 +426,11 @@ __global__ void __launch_bounds__(256) build_xrec_prefill(const float *__restric
 
 namespace moe {
 
-hipError_t launch_bucket_ex(const moe_ctx *c, const int32_t *idx, int T, int32_t *offsets, int32_t *perm, bool build,
-                            int entry_m, const float *x, uint16_t *xrec, int xrec_h, hipStream_t s);
-
 hipError_t launch_ffn_prefill(const moe_ctx *c, int layer, const float *x, int T, const int32_t *idx,
                               const int32_t *slot_of_pair, float *y_pairs, float *y_shared, hipStream_t s) {
   const moe_config &k = c->cfg;
   if (k.d_ff % 64 || k.d_model % 64) return hipErrorInvalidValue;
-  hipError_t e = launch_bucket_ex(c, idx, T, c->offsets_ws, c->perm_ws, true, kPM, nullptr, nullptr, 0, s);
+  hipError_t e = launch_bucket_ex(c, idx, T, c->offsets_ws, c->perm_ws, true, kPM, nullptr, nullptr, 0, s, nullptr);
   if (e != hipSuccess) return e;
   // the x record shares the decode path's record buffer (the same bytes per
   // token: nsb x 5 steps x 128 B); calls on one context never overlap

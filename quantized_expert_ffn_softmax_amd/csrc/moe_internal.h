@@ -73,6 +73,10 @@ inline int xrec_halves(int nsb) { return nsb * kSteps * 16; }
 // MFMA column n and its lo half in column n + 4, and keep an entry's whole
 // activation record (4 columns) in LDS, hence 4.
 constexpr int kEntryTokens = 4;
+// The second work list of the decode path: entries of up to 8 tokens (the
+// kernels built for it put token n's hi half in MFMA column n and its lo half
+// in column n + 8, every column in use).
+constexpr int kEntryTokens8 = 8;
 // Superblocks per row the decode kernels are built for: all of a unit's
 // word quads are requested at once, which bounds K (d_model, d_ff <= 2048).
 constexpr int kDecodeMaxNsb = 13;
@@ -104,7 +108,8 @@ struct moe_ctx {
   int32_t *perm_ws;      // [max_pairs]
   int32_t *chunk_ws;     // [n_chunks][n_experts] for the large bucketing
   moe::WorkEntry *work;  // [max_work]
-  int32_t *n_work;       // [4]: entries, routed entries, -, -
+  moe::WorkEntry *work8; // [max_work8]: the decode path's second list, entries of <= kEntryTokens8
+  int32_t *n_work;       // [4]: entries, routed entries (work), then the same for work8
   // x record: [max_tokens + 1][xrec_halves(gate.nsb)] (last row zero); the
   // decode path's layout, or on the prefill path its own layout of the same
   // size per token (each call rebuilds the rows it uses)
@@ -117,6 +122,7 @@ struct moe_ctx {
   int32_t route_small_t; // largest T routed by the decode-size router (<= 64)
   int32_t max_pairs;
   int32_t max_work;
+  int32_t max_work8;
   int32_t n_chunks_max;
   int32_t n_cu;          // compute units of the context's device
   int32_t decode_occ[3]; // decode FFN workgroups per CU: gate/up, down, gate/up K-split (queried at create)
@@ -147,6 +153,11 @@ hipError_t launch_router(const moe_ctx *c, const float *x, int T, const float *w
                          float *logits, int32_t *idx, float *w, hipStream_t s);
 hipError_t launch_bucket(const moe_ctx *c, const int32_t *idx, int T, int32_t *offsets, int32_t *perm,
                          bool build_work, hipStream_t s);
+// bucketing with the work list of entry_m-token entries (and, with work8, the
+// second list of kEntryTokens8-token entries) and, with x, the decode record
+hipError_t launch_bucket_ex(const moe_ctx *c, const int32_t *idx, int T, int32_t *offsets, int32_t *perm, bool build,
+                            int entry_m, const float *x, uint16_t *xrec, int xrec_h, hipStream_t s,
+                            moe::WorkEntry *work8);
 hipError_t launch_resolve(moe_ctx *c, int layer, const int32_t *idx, int T, int32_t *slot_of_pair, bool fill,
                           hipStream_t s);
 hipError_t decode_occupancy(moe_ctx *c);  // fills c->decode_occ for c's superblock counts

@@ -65,12 +65,14 @@ struct Out {
 
 // the context sizes moe_create gives a call of at most max_tokens tokens
 struct Sizes {
-  int max_pairs, max_work, n_chunks_max;
+  int max_pairs, max_work, max_work8, n_chunks_max;
 };
 Sizes ctx_sizes(int max_tokens, int k, int E) {
   Sizes z;
   z.max_pairs = max_tokens * k;
   z.max_work = z.max_pairs / moe::kEntryTokens + (z.max_pairs < E ? z.max_pairs : E) + max_tokens / moe::kEntryTokens + 4;
+  z.max_work8 =
+      z.max_pairs / moe::kEntryTokens8 + (z.max_pairs < E ? z.max_pairs : E) + max_tokens / moe::kEntryTokens8 + 4;
   z.n_chunks_max = (z.max_pairs + 255) / 256;
   return z;
 }
@@ -96,6 +98,7 @@ int run_bucket(char **a) {
   std::memcpy(idx, iv.data(), (size_t)n * 4);
   c.chunk_ws = exact<int32_t>((size_t)z.n_chunks_max * E, 0xa5);
   c.work = exact<moe::WorkEntry>(z.max_work, 0xa5);
+  c.work8 = exact<moe::WorkEntry>(z.max_work8, 0xa5);
   c.n_work = exact<int32_t>(4, 0xa5);
   int32_t *offsets = exact<int32_t>(E + 1, 0xa5);
   int32_t *perm = exact<int32_t>(n, 0xa5);
@@ -108,8 +111,10 @@ int run_bucket(char **a) {
     std::memcpy(x, iv.data() + n, (size_t)T * d * 4);
     xrec = exact<uint16_t>(xrec_n, 0);  // zeroed at create, as the library does
   }
+  // the decode entry size also builds the second list (8-token entries)
+  moe::WorkEntry *w8 = entry_m == moe::kEntryTokens ? c.work8 : nullptr;
   const hipError_t e =
-      moe::launch_bucket_ex(&c, idx, T, offsets, perm, build != 0, entry_m, x, xrec, xh, (hipStream_t) nullptr);
+      moe::launch_bucket_ex(&c, idx, T, offsets, perm, build != 0, entry_m, x, xrec, xh, (hipStream_t) nullptr, w8);
   if (e != hipSuccess) die("launch_bucket_ex failed");
   Out o(out);
   o.put(offsets, E + 1);
@@ -119,11 +124,18 @@ int run_bucket(char **a) {
     if (nw < 0 || nw > z.max_work) die("n_work outside the work list");
     o.put(c.n_work, 2);
     o.put(reinterpret_cast<const int32_t *>(c.work), (size_t)nw * 4);
+    if (w8) {
+      const int nw8 = c.n_work[2];
+      if (nw8 < 0 || nw8 > z.max_work8) die("n_work[2] outside the second work list");
+      o.put(c.n_work + 2, 2);
+      o.put(reinterpret_cast<const int32_t *>(c.work8), (size_t)nw8 * 4);
+    }
   }
   if (d > 0) o.put(xrec, xrec_n);
   std::free(idx);
   std::free(c.chunk_ws);
   std::free(c.work);
+  std::free(c.work8);
   std::free(c.n_work);
   std::free(offsets);
   std::free(perm);
@@ -263,6 +275,7 @@ int run_bucket_lookup(char **a) {
   c.offsets_ws = exact<int32_t>(E + 1, 0xa5);
   c.perm_ws = exact<int32_t>(z.max_pairs, 0xa5);
   c.work = exact<moe::WorkEntry>(z.max_work, 0xa5);
+  c.work8 = exact<moe::WorkEntry>(z.max_work8, 0xa5);
   c.n_work = exact<int32_t>(4, 0xa5);
   for (int call = 0; call < 2; ++call)  // twice: the counters accumulate
     if (moe::launch_bucket_lookup(&c, idx, T, moe::kEntryTokens, x, xrec, xh, (hipStream_t) nullptr) != hipSuccess)
@@ -274,6 +287,10 @@ int run_bucket_lookup(char **a) {
   if (nw < 0 || nw > z.max_work) die("n_work outside the work list");
   o.put(c.n_work, 2);
   o.put(reinterpret_cast<const int32_t *>(c.work), (size_t)nw * 4);
+  const int nw8 = c.n_work[2];
+  if (nw8 < 0 || nw8 > z.max_work8) die("n_work[2] outside the second work list");
+  o.put(c.n_work + 2, 2);
+  o.put(reinterpret_cast<const int32_t *>(c.work8), (size_t)nw8 * 4);
   o.put(xrec, xrec_n);
   o.put(c.dmiss, 3);
   o.put(c.dstats, 6);
@@ -285,6 +302,7 @@ int run_bucket_lookup(char **a) {
   std::free(c.offsets_ws);
   std::free(c.perm_ws);
   std::free(c.work);
+  std::free(c.work8);
   std::free(c.n_work);
   return 0;
 }

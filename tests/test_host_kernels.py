@@ -171,6 +171,10 @@ def test_bucket_and_work_list(exe, tmp_path, E, T, k, m, d, what):
     work, routed = _work_expected(counts, offsets, T, m)
     assert n_work.tolist() == [len(work), routed]
     assert np.array_equal(out.take(len(work) * 4).reshape(-1, 4), work)
+    if m == 4:  # the decode path's second list: entries of up to 8 pairs
+        work8, routed8 = _work_expected(counts, offsets, T, 8)
+        assert out.take(2).tolist() == [len(work8), routed8]
+        assert np.array_equal(out.take(len(work8) * 4).reshape(-1, 4), work8)
     if d:
         nsb = -(-d // 160)
         got = out.take((T + 1) * nsb * 320, np.uint16).reshape(T + 1, -1)
@@ -193,6 +197,9 @@ def test_bucket_ignores_ids_outside_range(exe, tmp_path, T, k, E):
     work, routed = _work_expected(counts, offsets, T, 4)
     assert n_work.tolist() == [len(work), routed]
     assert np.array_equal(out.take(len(work) * 4).reshape(-1, 4), work)
+    work8, routed8 = _work_expected(counts, offsets, T, 8)
+    assert out.take(2).tolist() == [len(work8), routed8]
+    assert np.array_equal(out.take(len(work8) * 4).reshape(-1, 4), work8)
     out.done()
 
 
@@ -341,6 +348,9 @@ def test_bucket_lookup(exe, tmp_path, E, T, k, d):
     work, routed = _work_expected(counts, offsets, T, 4)
     assert n_work.tolist() == [len(work), routed]
     assert np.array_equal(out.take(len(work) * 4).reshape(-1, 4), work)
+    work8, routed8 = _work_expected(counts, offsets, T, 8)
+    assert out.take(2).tolist() == [len(work8), routed8]
+    assert np.array_equal(out.take(len(work8) * 4).reshape(-1, 4), work8)
     nsb = -(-d // 160)
     assert np.array_equal(out.take((T + 1) * nsb * 320, np.uint16).reshape(T + 1, -1), _xrec_expected(x, nsb))
     # what the resolve kernel records for a resident call, twice
