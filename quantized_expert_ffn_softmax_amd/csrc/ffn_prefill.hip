@@ -125,14 +125,12 @@ __device__ __attribute__((always_inline)) inline bool entry_token(const PrefillP
 
 __device__ __attribute__((always_inline)) inline f4 mfma(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 
-// The lane's 4 weight rows: word quad g of each (one superblock at a time)
-// and the scale pairs of the current and the next superblock.  Step t of a
-// superblock reads words (4t) / 5 .. (4t + 3) / 5 of the quad, so word j is
-// dead after step j + 1: the next superblock's word j is requested at step
-// j + 2 (word 3 at step 0 of its own superblock), three steps before use,
-// without a second buffer.
+// The lane's 4 weight rows: word quad g of each and the scale pairs, for the
+// current and the next superblock (indexed by superblock parity).  Each
+// quad is one 16-byte load per row, requested at step 0 of the superblock
+// before its use, five steps ahead.
 struct WSb {
-  uint32_t w[4][4];  // [tile][word]
+  u4 q[2][4];        // [superblock parity][tile]: words 4g .. 4g + 3
   uint32_t s[2][4];  // [superblock parity][tile]: s_b | s_b+1 << 16
 };
 
@@ -147,9 +145,10 @@ struct WRows {
 
 // every load is unconditional (callers clamp S), so the compiler's waits count
 // exactly the loads issued after the one they wait for
-__device__ __attribute__((always_inline)) inline void load_word(const WRows &R, int S, int j, WSb &o) {
+template <int SP>
+__device__ __attribute__((always_inline)) inline void load_quads(const WRows &R, int S, WSb &o) {
 #pragma unroll
-  for (int a = 0; a < 4; ++a) o.w[a][j] = *reinterpret_cast<const uint32_t *>(R.code + (R.coff[a] + S * 64 + 4 * j));
+  for (int a = 0; a < 4; ++a) o.q[SP][a] = *reinterpret_cast<const u4 *>(R.code + (R.coff[a] + S * 64));
 }
 
 template <int SP>
@@ -210,13 +209,17 @@ __device__ __attribute__((always_inline)) inline void k_step(int S, int nsb, con
   // conditional
   store_x<kHL>(XR, XS[PAR ^ 1], xs[PAR ^ 1]);
   load_x<kHL>(XR, min(s + 3, nsteps - 1), XS[PAR ^ 1]);
+  // the next superblock's quads and scales, a superblock ahead of their use
+  if constexpr (t == 0) {
+    load_quads<SP ^ 1>(R, min(S + 1, nsb - 1), W);
+    load_scales<SP ^ 1>(R, min(S + 1, nsb - 1), g, W);
+  }
   h8 A[4];  // (a wave past the matrix dequantises its clamped rows and drops them)
 #pragma unroll
-  for (int a = 0; a < 4; ++a) A[a] = moe::quad_a_sel<t>(W.w[a], K, W.s[SP][a], sel);
-  // the words (and scales) this step has freed, for the superblock they serve
-  if constexpr (t == 0) load_word(R, S, 3, W);
-  if constexpr (t >= 2) load_word(R, min(S + 1, nsb - 1), t - 2, W);
-  if constexpr (t == 2) load_scales<SP ^ 1>(R, min(S + 1, nsb - 1), g, W);
+  for (int a = 0; a < 4; ++a) {
+    const uint32_t w4[4] = {W.q[SP][a].x, W.q[SP][a].y, W.q[SP][a].z, W.q[SP][a].w};
+    A[a] = moe::quad_a_sel<t>(w4, K, W.s[SP][a], sel);
+  }
   if (!wact) return;  // wave-uniform: rows past the matrix
   // B operands one read ahead of their MFMAs: the next half is requested
   // before the current one's four MFMAs, so LDS latency overlaps them
@@ -336,9 +339,7 @@ __global__ void __launch_bounds__(kPThreads, 1) prefill_kernel(PrefillParams P) 
       for (int nt = 0; nt < kTT; ++nt) acc[a][nt] = (f4){0.f, 0.f, 0.f, 0.f};
     // prologue: superblock 0's weights; tiles of steps 0 (to LDS), 1 and 2
     WSb W;
-    load_word(R, 0, 0, W);
-    load_word(R, 0, 1, W);
-    load_word(R, 0, 2, W);
+    load_quads<0>(R, 0, W);
     load_scales<0>(R, 0, g, W);
     XStage<kHL> XS[2];
     load_x<kHL>(XR, 0, XS[0]);
