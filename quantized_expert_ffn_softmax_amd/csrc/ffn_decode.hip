@@ -21,6 +21,7 @@
 
 #include "moe_internal.h"
 #include "dequant.h"
+#include "lds_copy.h"
 #include "record.h"
 
 namespace {
@@ -175,30 +176,8 @@ __device__ inline void unit_setup(const DecodeParams &P, int u, int tpu, int til
   U.has_tok = col < U.m && entry_token(P, we, col, U.tok, U.rrow);
 }
 
-// One 16-byte-per-lane global-to-LDS copy: lane l's 16 bytes at `src` land at
-// LDS byte lds + 16 l.  Written as assembly so that the compiler's wait
-// insertion does not treat every later LDS read as possibly overlapping it
-// (it would wait for all loads in flight, the word loads included); the
-// kernel waits for these copies itself, before the barrier that publishes
-// them.  No register result, so nothing is left in flight in a register;
-// M0 (the LDS base of the copy, uniform across the wave) is saved and restored
-// around it.
-__device__ inline void lds_copy16(const void *src, uint32_t lds) {
-  uint32_t keep;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(keep)
-      : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(src)
-      : "memory");
-}
-
-__device__ inline uint32_t lds_addr(const void *p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)(p);
-}
+using moe::lds_addr;
+using moe::lds_copy16;
 
 __device__ inline h8 lds_h8(const uint8_t *p) { return *reinterpret_cast<const h8 *>(p); }
 

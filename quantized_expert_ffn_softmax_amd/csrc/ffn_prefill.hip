@@ -19,17 +19,21 @@
 // same 256 rows of up (the epilogue writes h for them); down: 512 rows.  Each
 // wave owns 4 16-row tiles (gate/up: 2 of gate and the same 2 of up) against
 // all 128 tokens: 4 x 8 16x16 output tiles, 128 fp32 accumulators per lane.
-//   A (16 rows x 32 K)  = weights, dequantised per wave in registers from the
-//                         packed words (no LDS round trip);
-//   B (32 K x 16 tokens) = activations (hi, then lo) from a double-buffered
-//                         LDS tile that all 8 waves share, one barrier per
-//                         32-K step.
-// Every global load is an ordinary register load the compiler tracks: word
-// quads and scales one superblock ahead, activations two steps ahead of
-// their LDS write.  v_mfma_f32_16x16x32_f16 only.
+//   A (16 rows x 32 K)  = weights: each wave's word quads and scale words are
+//                         copied to LDS a superblock ahead, read into
+//                         registers once per superblock and dequantised
+//                         there at every step;
+//   B (32 K x 16 tokens) = activations (hi, then lo) from a 4-slot LDS ring
+//                         of step tiles that all 8 waves share, filled 3
+//                         steps ahead, one barrier per 32-K step.
+// Every global load of the K loop is a direct global-to-LDS copy whose
+// completion the kernel waits for itself.  The gate/up epilogue stages h in
+// LDS in record order and stores whole 16-byte pieces of the h record.
+// v_mfma_f32_16x16x32_f16 only.
 #include <algorithm>
 
 #include "dequant.h"
+#include "lds_copy.h"
 #include "moe_internal.h"
 
 namespace {
@@ -125,15 +129,6 @@ __device__ __attribute__((always_inline)) inline bool entry_token(const PrefillP
 
 __device__ __attribute__((always_inline)) inline f4 mfma(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 
-// The lane's 4 weight rows: word quad g of each and the scale pairs, for the
-// current and the next superblock (indexed by superblock parity).  Each
-// quad is one 16-byte load per row, requested at step 0 of the superblock
-// before its use, five steps ahead.
-struct WSb {
-  u4 q[2][4];        // [superblock parity][tile]: words 4g .. 4g + 3
-  uint32_t s[2][4];  // [superblock parity][tile]: s_b | s_b+1 << 16
-};
-
 // Where the lane's 4 weight rows live: tile a's words at code + coff[a], its
 // scales at scale + soff[a] (the offsets are the same for the whole wave)
 struct WRows {
@@ -143,87 +138,145 @@ struct WRows {
   int nblk;
 };
 
-// every load is unconditional (callers clamp S), so the compiler's waits count
-// exactly the loads issued after the one they wait for
-template <int SP>
-__device__ __attribute__((always_inline)) inline void load_quads(const WRows &R, int S, WSb &o) {
-#pragma unroll
-  for (int a = 0; a < 4; ++a) o.q[SP][a] = *reinterpret_cast<const u4 *>(R.code + (R.coff[a] + S * 64));
+// K loop.  Every global load in it is a direct global-to-LDS copy that the
+// kernel waits for itself (lds_copy.h), so the only memory operations the
+// compiler sees are LDS reads, which it counts exactly:
+//   * the x (or h) record tile of step s + kXD goes to ring slot (s + kXD) & 3
+//     at step s (two 16-byte copies per thread);
+//   * at step 0 of superblock S, the next superblock's word quads (one 16-byte
+//     copy per tile: lane l's quad lands at 16 l) and, per tile, the three
+//     dwords of each of its 16 rows that hold scale blocks 5 S' .. 5 S' + 4
+//     (one 4-byte copy by 48 lanes) go to weight slot (S + 1) & 1 (8 copies
+//     per wave);
+//   * each step starts by waiting until its tile's copies have landed (loads
+//     complete in order, so everything issued before them has too), then one
+//     barrier publishes the tile to all waves.
+// Weights are read into registers at step 0 of their superblock (a quad and a
+// scale pair per tile), dequantised per step as before.
+constexpr int kXD = 3;                      // x tiles copied this many steps ahead
+constexpr int kXRing = 4;                   // slots of the x ring (> kXD)
+constexpr int kQuadB = 1024;                // one tile's quads of one wave: 64 lanes x 16 B
+constexpr int kScB = 256;                   // one tile's scale dwords: 16 rows x 3 (64 lane slots)
+constexpr int kTileWB = kQuadB + kScB;      // one tile's weights of one superblock
+constexpr int kWSlotB = kPWaves * 4 * kTileWB;  // one superblock's weights of the workgroup
+constexpr int kWCopies = 8;                 // copies per wave per superblock: 4 quads + 4 scale sets
+static_assert(kXRing > kXD && (kXRing & (kXRing - 1)) == 0, "x ring");
+
+// loads issued after a step's tile copies by the time that step waits for
+// them: the tiles of the kXD - 1 later steps (2 copies each) and kWCopies
+// weight copies per superblock start among the kXD steps since; in superblock
+// 0 the prologue's order (tiles 0..kXD-1, then superblock 0's weights)
+// applies
+constexpr int vm_after(int t, bool first) {
+  if (first) {
+    // step 0 waits for superblock 0's weights (the last prologue loads)
+    if (t == 0) return 0;
+    int n = 0;
+    // prologue: tiles t+1 .. kXD-1, superblock 0's weights
+    if (t < kXD) n += 2 * (kXD - 1 - t) + kWCopies;
+    // steps 0 .. t-1 of superblock 0 (for t <= kXD), or t-kXD .. t-1
+    const int u0 = t < kXD ? 0 : t - kXD;
+    for (int u = u0; u < t; ++u) n += 2 + (u == 0 ? kWCopies : 0);
+    return n - (t < kXD ? 0 : 2);  // the issuing step's own copies come first
+  }
+  int n = 2 * (kXD - 1);
+  for (int u = t - kXD; u < t; ++u) n += ((u % 5 + 5) % 5 == 0) ? kWCopies : 0;
+  return n;
 }
 
-template <int SP>
-__device__ __attribute__((always_inline)) inline void load_scales(const WRows &R, int S, int g, WSb &o) {
-  const int b0 = min(5 * S + g, R.nblk - 1), b1 = min(5 * S + g + 1, R.nblk - 1);
+template <int N>
+__device__ __attribute__((always_inline)) inline void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+struct XCopy {
+  const uint8_t *src[Geo::kCopies];  // this thread's granules of step 0 (row, piece)
+  uint32_t lds[Geo::kCopies];        // LDS byte of each granule inside a step tile
+};
+
+// the copies of step s's tile into ring slot s & 3 (s clamped: past the last
+// step the last tile is copied again into a slot nobody reads)
+__device__ __attribute__((always_inline)) inline void copy_x(const XCopy &X, uint32_t ring, int s, int nsteps) {
+  const int sc = min(s, nsteps - 1);
+  const uint32_t slot = ring + (uint32_t)(s & (kXRing - 1)) * Geo::kStepB;
+#pragma unroll
+  for (int i = 0; i < Geo::kCopies; ++i) moe::lds_copy16(X.src[i] + (size_t)sc * Geo::kRowB, slot + X.lds[i]);
+}
+
+// superblock S's weights (S clamped) into weight slot S & 1: per tile the
+// lane's quad, and the scale dwords d0 + k (k = 0..2, d0 = floor(5 S / 2),
+// each clamped to the row) of row lane / 3 copied by lanes 0..47 (lane
+// 3 r + k), which hold blocks 2 d0 .. 2 d0 + 5 -- every block 5 S + g and
+// 5 S + g + 1 the row's lanes read
+__device__ __attribute__((always_inline)) inline void copy_w(const WRows &R, uint32_t wbase, int S, int nsb, int r16,
+                                                             int lane, int w) {
+  const int Sc = min(S, nsb - 1);
+  const uint32_t slot = wbase + (uint32_t)(S & 1) * kWSlotB + (uint32_t)w * 4 * kTileWB;
+  const int crow = lane / 3, dk = min((5 * Sc) / 2 + (lane - 3 * crow), R.nblk / 2 - 1);
+  const int rdelta = (crow - r16) * R.nblk * 2;  // the copied row from the lane's own (rows are consecutive)
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
-    const uint32_t lo = *reinterpret_cast<const uint16_t *>(R.scale + (R.soff[a] + 2 * b0));
-    const uint32_t hi = *reinterpret_cast<const uint16_t *>(R.scale + (R.soff[a] + 2 * b1));
-    o.s[SP][a] = lo | (hi << 16);
+    const uint32_t t0 = slot + (uint32_t)a * kTileWB;
+    moe::lds_copy16(R.code + (R.coff[a] + (uint32_t)Sc * 64), t0);
+    if (lane < 48) moe::lds_copy4(R.scale + ((int)R.soff[a] + rdelta + 4 * dk), t0 + kQuadB);
   }
 }
 
-// activation staging of one step: this thread's granules of the tile
-template <int HL>
-struct XStage {
-  u4 v[RecGeom<HL>::kCopies];
+struct WReg {
+  uint32_t q[4][4];  // [tile][word]
+  uint32_t P[4];     // [tile]: s_b0 | s_b1 << 16
 };
 
-template <int HL>
-struct XRoles {
-  const uint8_t *base;                   // the record
-  uint32_t stride;                       // bytes per record row
-  uint32_t row[RecGeom<HL>::kCopies];    // record row (row 0 for columns without a token)
-  uint32_t piece[RecGeom<HL>::kCopies];  // byte offset of the granule inside a step
-  uint32_t lds[RecGeom<HL>::kCopies];    // byte offset inside a step tile
-};
-
-template <int HL>
-__device__ __attribute__((always_inline)) inline void load_x(const XRoles<HL> &X, int s, XStage<HL> &o) {
+// superblock S's weights from its LDS slot into registers: the quad, and the
+// scale pair b0 = min(5 S + g, nblk - 1), b1 = min(b0 + 1, nblk - 1) from the
+// row's three dwords (block b is half (b - 2 d0) of dword (b - 2 d0) / 2)
+__device__ __attribute__((always_inline)) inline void read_w(const uint8_t *wlds, int S, int g, int r16, int nblk,
+                                                             int w, int lane, WReg &o) {
+  const uint8_t *slot = wlds + (S & 1) * kWSlotB + w * 4 * kTileWB;
+  const int d0 = (5 * S) / 2;
+  const int b0 = min(5 * S + g, nblk - 1), b1 = min(b0 + 1, nblk - 1);
+  const int j0 = b0 - 2 * d0, j1 = b1 - 2 * d0;
 #pragma unroll
-  for (int i = 0; i < RecGeom<HL>::kCopies; ++i)
-    o.v[i] = *reinterpret_cast<const u4 *>(X.base + (size_t)X.row[i] * X.stride +
-                                           (X.piece[i] + (uint32_t)s * RecGeom<HL>::kRowB));
+  for (int a = 0; a < 4; ++a) {
+    const uint8_t *t0 = slot + a * kTileWB;
+    const u4 q = *reinterpret_cast<const u4 *>(t0 + 16 * lane);
+    o.q[a][0] = q.x;
+    o.q[a][1] = q.y;
+    o.q[a][2] = q.z;
+    o.q[a][3] = q.w;
+    const uint32_t e0 = *reinterpret_cast<const uint32_t *>(t0 + kQuadB + 4 * (3 * r16 + (j0 >> 1)));
+    const uint32_t e1 = *reinterpret_cast<const uint32_t *>(t0 + kQuadB + 4 * (3 * r16 + (j1 >> 1)));
+    const uint32_t s0 = (j0 & 1) ? e0 >> 16 : e0 & 0xffffu, s1 = (j1 & 1) ? e1 >> 16 : e1 & 0xffffu;
+    o.P[a] = s0 | (s1 << 16);
+  }
 }
 
-template <int HL>
-__device__ __attribute__((always_inline)) inline void store_x(const XRoles<HL> &X, const XStage<HL> &v, uint8_t *tile) {
-#pragma unroll
-  for (int i = 0; i < RecGeom<HL>::kCopies; ++i) *reinterpret_cast<u4 *>(tile + X.lds[i]) = v.v[i];
-}
-
-// One K step (t of superblock S, parity PAR of the step index; SP: parity
-// of S): after the barrier, stage the next step's tile into the free LDS
-// buffer and request the one after it, request the next superblock's word
-// (and scales) that this step frees, then the wave's 4 row tiles x the
-// entry's token tiles: every product twice, with the activations' hi and lo.
-template <int NMAT, int t, int PAR, int SP>
-__device__ __attribute__((always_inline)) inline void k_step(int S, int nsb, const WRows &R, int g, WSb &W,
-                                                             uint8_t (*xs)[Geo::kStepB],
-                                                             const XRoles<kHL> &XR, XStage<kHL> (&XS)[2],
+// One K step (t of superblock S; FIRST: superblock 0): wait for the step's
+// tile, publish it, issue the copies of later data, then the wave's 4 row
+// tiles x the entry's token tiles, every product twice (the activations' hi
+// and lo halves).
+template <int t, bool FIRST>
+__device__ __attribute__((always_inline)) inline void k_step(int S, int nsb, int nsteps, const WRows &R, int g, int r16,
+                                                             int w, int lane, WReg &W, const XCopy &X, uint32_t ring,
+                                                             const uint8_t *xring, uint32_t wbase, const uint8_t *wlds,
                                                              const uint32_t (&sel)[6], const moe::Consts &K, int ntt,
                                                              bool wact, int rl_hi, int rl_lo, f4 (&acc)[4][kTT]) {
   using G = Geo;
-  const int s = 5 * S + t, nsteps = 5 * nsb;
-  __syncthreads();  // step s's tile is complete; the other buffer is no longer read
-  // past the last step these restage the last tile: harmless, and no load is
-  // conditional
-  store_x<kHL>(XR, XS[PAR ^ 1], xs[PAR ^ 1]);
-  load_x<kHL>(XR, min(s + 3, nsteps - 1), XS[PAR ^ 1]);
-  // the next superblock's quads and scales, a superblock ahead of their use
+  const int s = 5 * S + t;
+  wait_vm<vm_after(t, FIRST)>();
+  __syncthreads();  // step s's tile is in LDS for every wave; slot (s - 1) & 3 is no longer read
+  copy_x(X, ring, s + kXD, nsteps);
   if constexpr (t == 0) {
-    load_quads<SP ^ 1>(R, min(S + 1, nsb - 1), W);
-    load_scales<SP ^ 1>(R, min(S + 1, nsb - 1), g, W);
-  }
-  h8 A[4];  // (a wave past the matrix dequantises its clamped rows and drops them)
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const uint32_t w4[4] = {W.q[SP][a].x, W.q[SP][a].y, W.q[SP][a].z, W.q[SP][a].w};
-    A[a] = moe::quad_a_sel<t>(w4, K, W.s[SP][a], sel);
+    copy_w(R, wbase, S + 1, nsb, r16, lane, w);
+    read_w(wlds, S, g, r16, R.nblk, w, lane, W);
   }
   if (!wact) return;  // wave-uniform: rows past the matrix
-  // B operands one read ahead of their MFMAs: the next half is requested
-  // before the current one's four MFMAs, so LDS latency overlaps them
-  const uint8_t *tile = xs[PAR];
+  h8 A[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) A[a] = moe::quad_a_sel<t>(W.q[a], K, W.P[a], sel);
+  // B operands one read ahead of their MFMAs
+  const uint8_t *tile = xring + (s & (kXRing - 1)) * G::kStepB;
   h8 cur = *reinterpret_cast<const h8 *>(tile + rl_hi);
 #pragma unroll
   for (int nt = 0; nt < kTT; ++nt) {
@@ -238,29 +291,39 @@ __device__ __attribute__((always_inline)) inline void k_step(int S, int nsb, con
   }
 }
 
-// One superblock (5 K steps).  PAR: parity of its first step index, SP: of
-// the superblock index (the two alternate together: 5 steps per superblock).
-template <int NMAT, int SP>
-__device__ __attribute__((always_inline)) inline void k_superblock(int S, int nsb, const WRows &R, int g, WSb &W,
-                                                                   uint8_t (*xs)[Geo::kStepB],
-                                                                   const XRoles<kHL> &XR, XStage<kHL> (&XS)[2],
-                                                                   const uint32_t (&sel)[6], const moe::Consts &K,
-                                                                   int ntt, bool wact, int rl_hi, int rl_lo,
-                                                                   f4 (&acc)[4][kTT]) {
-  constexpr int PAR = SP;
-  k_step<NMAT, 0, PAR, SP>(S, nsb, R, g, W, xs, XR, XS, sel, K, ntt, wact, rl_hi, rl_lo, acc);
-  k_step<NMAT, 1, PAR ^ 1, SP>(S, nsb, R, g, W, xs, XR, XS, sel, K, ntt, wact, rl_hi, rl_lo, acc);
-  k_step<NMAT, 2, PAR, SP>(S, nsb, R, g, W, xs, XR, XS, sel, K, ntt, wact, rl_hi, rl_lo, acc);
-  k_step<NMAT, 3, PAR ^ 1, SP>(S, nsb, R, g, W, xs, XR, XS, sel, K, ntt, wact, rl_hi, rl_lo, acc);
-  k_step<NMAT, 4, PAR, SP>(S, nsb, R, g, W, xs, XR, XS, sel, K, ntt, wact, rl_hi, rl_lo, acc);
+template <bool FIRST>
+__device__ __attribute__((always_inline)) inline void k_superblock(int S, int nsb, int nsteps, const WRows &R, int g,
+                                                                   int r16, int w, int lane, WReg &W, const XCopy &X,
+                                                                   uint32_t ring, const uint8_t *xring, uint32_t wbase,
+                                                                   const uint8_t *wlds, const uint32_t (&sel)[6],
+                                                                   const moe::Consts &K, int ntt, bool wact, int rl_hi,
+                                                                   int rl_lo, f4 (&acc)[4][kTT]) {
+  k_step<0, FIRST>(S, nsb, nsteps, R, g, r16, w, lane, W, X, ring, xring, wbase, wlds, sel, K, ntt, wact, rl_hi, rl_lo, acc);
+  k_step<1, FIRST>(S, nsb, nsteps, R, g, r16, w, lane, W, X, ring, xring, wbase, wlds, sel, K, ntt, wact, rl_hi, rl_lo, acc);
+  k_step<2, FIRST>(S, nsb, nsteps, R, g, r16, w, lane, W, X, ring, xring, wbase, wlds, sel, K, ntt, wact, rl_hi, rl_lo, acc);
+  k_step<3, FIRST>(S, nsb, nsteps, R, g, r16, w, lane, W, X, ring, xring, wbase, wlds, sel, K, ntt, wact, rl_hi, rl_lo, acc);
+  k_step<4, FIRST>(S, nsb, nsteps, R, g, r16, w, lane, W, X, ring, xring, wbase, wlds, sel, K, ntt, wact, rl_hi, rl_lo, acc);
 }
 
 // NMAT = 2: gate/up -> h record; NMAT = 1: down -> y.  One workgroup per CU
 // walks its accelerator die's share of the (entry, row block) items.
+// Gate/up epilogue staging: the h values of 64 tokens at a time, laid out in
+// LDS as the bytes of their h records over the record lines (step tiles of
+// 128 B) that the item's columns fall in -- at most 3 superblocks, 15 lines
+// -- one token every nl * 128 + 16 bytes; the item then writes every 16-byte
+// piece it owns whole, and 2-byte halves only in pieces it shares with the
+// neighbouring row block.
+constexpr int kImgTokens = 64;
+constexpr int kImgMaxLines = 15;
+constexpr int kSmemB = kXRing * Geo::kStepB + 2 * kWSlotB;
+static_assert(kImgTokens * (kImgMaxLines * 128 + 16) <= kSmemB, "staged h fits in the K loop's LDS");
+
 template <int NMAT>
 __global__ void __launch_bounds__(kPThreads, 1) prefill_kernel(PrefillParams P) {
   using G = Geo;
-  __shared__ __attribute__((aligned(16))) uint8_t xs[2][G::kStepB];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmemB];
+  uint8_t *const xring = smem;                          // K loop: x ring
+  uint8_t *const wlds = smem + kXRing * G::kStepB;      // K loop: weight slots
   __shared__ int row_sh[kPM], tok_sh[kPM];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
@@ -280,6 +343,7 @@ __global__ void __launch_bounds__(kPThreads, 1) prefill_kernel(PrefillParams P) 
   const moe::Consts K = moe::make_consts();
   uint32_t sel[6];
   moe::pattern_selectors(g, sel);
+  const uint32_t ring = moe::lds_addr(xring), wbase = moe::lds_addr(wlds);
   // this lane's B operand (token r16 of a 16-token tile, K group g) inside a
   // step tile: granule piece ^ swz(row), piece g (hi) or 4 + g (lo)
   const int sw = G::swz(r16);
@@ -290,7 +354,7 @@ __global__ void __launch_bounds__(kPThreads, 1) prefill_kernel(PrefillParams P) 
     if (!entry_ok(P, we)) continue;  // uniform over the workgroup
     const uint8_t *blob = entry_blob(P, we);
     if (!blob) continue;
-    __syncthreads();  // the previous item no longer reads the token lists or the tiles
+    __syncthreads();  // the previous item no longer reads the token lists or the LDS data
     if (tid < kPM) {
       int tok = -1, row = -1;
       if (tid < we.m && !entry_token(P, we, tid, tok, row)) tok = row = -1;
@@ -320,65 +384,110 @@ __global__ void __launch_bounds__(kPThreads, 1) prefill_kernel(PrefillParams P) 
         R.soff[a] = smat + (uint32_t)(16 * ta) * M.nblk * 2;
       }
     }
-    // activation copy roles: granule q = tid + 512 i of a step tile
-    XRoles<kHL> XR;
-    XR.base = NMAT == 2 ? P.xrec : P.hrec;
-    XR.stride = (uint32_t)(NMAT == 2 ? P.xrec_b : P.hrec_b);
+    // activation copy roles: granule q = tid + 512 i of a step tile, row n =
+    // q / 8 of the tile (its record row, row 0 for columns without a token),
+    // its piece swizzled by the row; lands at LDS byte 16 q of the tile
+    XCopy X;
+    {
+      const uint8_t *base = NMAT == 2 ? P.xrec : P.hrec;
+      const size_t stride = (size_t)(NMAT == 2 ? P.xrec_b : P.hrec_b);
 #pragma unroll
-    for (int i = 0; i < G::kCopies; ++i) {
-      const int q = tid + kPThreads * i, n = q / G::kGran, pos = q - n * G::kGran;
-      const int rr = n < m ? (NMAT == 2 ? tok_sh[n] : row_sh[n]) : -1;
-      XR.row[i] = (uint32_t)(rr < 0 ? 0 : rr);
-      XR.piece[i] = (uint32_t)(pos ^ G::swz(n)) * 16u;
-      XR.lds[i] = (uint32_t)q * 16u;
+      for (int i = 0; i < G::kCopies; ++i) {
+        const int q = tid + kPThreads * i, n = q / G::kGran, pos = q - n * G::kGran;
+        const int rr = n < m ? (NMAT == 2 ? tok_sh[n] : row_sh[n]) : -1;
+        X.src[i] = base + (size_t)(rr < 0 ? 0 : rr) * stride + (uint32_t)(pos ^ G::swz(n)) * 16u;
+        X.lds[i] = (uint32_t)q * 16u;
+      }
     }
     f4 acc[4][kTT];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
       for (int nt = 0; nt < kTT; ++nt) acc[a][nt] = (f4){0.f, 0.f, 0.f, 0.f};
-    // prologue: superblock 0's weights; tiles of steps 0 (to LDS), 1 and 2
-    WSb W;
-    load_quads<0>(R, 0, W);
-    load_scales<0>(R, 0, g, W);
-    XStage<kHL> XS[2];
-    load_x<kHL>(XR, 0, XS[0]);
-    load_x<kHL>(XR, min(1, nsteps - 1), XS[1]);
-    store_x<kHL>(XR, XS[0], xs[0]);
-    load_x<kHL>(XR, min(2, nsteps - 1), XS[0]);
-    int S = 0;
-    for (; S + 1 < nsb; S += 2) {
-      k_superblock<NMAT, 0>(S, nsb, R, g, W, xs, XR, XS, sel, K, ntt, wact, rl_hi, rl_lo, acc);
-      k_superblock<NMAT, 1>(S + 1, nsb, R, g, W, xs, XR, XS, sel, K, ntt, wact, rl_hi, rl_lo, acc);
-    }
-    if (S < nsb) k_superblock<NMAT, 0>(S, nsb, R, g, W, xs, XR, XS, sel, K, ntt, wact, rl_hi, rl_lo, acc);
-    if (!wact) continue;
+    // prologue: the tiles of steps 0 .. kXD-1, then superblock 0's weights
+#pragma unroll
+    for (int s0 = 0; s0 < kXD; ++s0) copy_x(X, ring, s0, nsteps);
+    copy_w(R, wbase, 0, nsb, r16, lane, w);
+    WReg W;
+    k_superblock<true>(0, nsb, nsteps, R, g, r16, w, lane, W, X, ring, xring, wbase, wlds, sel, K, ntt, wact, rl_hi,
+                       rl_lo, acc);
+    for (int S = 1; S < nsb; ++S)
+      k_superblock<false>(S, nsb, nsteps, R, g, r16, w, lane, W, X, ring, xring, wbase, wlds, sel, K, ntt, wact,
+                          rl_hi, rl_lo, acc);
+    // every copy of this item (the ones past the last step included) has
+    // landed before the next item's prologue reuses the slots
+    wait_vm<0>();
     // D layout: lane (r16, g) holds rows 4 g + i of each row tile for token
     // r16 of each token tile
     if constexpr (NMAT == 2) {
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
+      // the item owns h columns [c0, c1); they lie in record lines L0 .. L0 + nl - 1
+      const int c0 = rt * kGRows, c1 = min(c0 + kGRows, P.d_ff);
+      const int L0 = 5 * (c0 / moe::kSbCols), nl = 5 * ((c1 - 1) / moe::kSbCols) + 5 - L0;
+      const int istride = nl * 128 + 16;
+      // write-out roles: thread (tq, wi) stores piece wi (line L0 + wi / 8,
+      // piece wi % 8) of the record for tokens tq, tq + 4, ... of each half,
+      // so neighbouring threads store neighbouring bytes of one record; which
+      // of the piece's 8 halves the item owns is the same for every token
+      const int wi = tid & 127, tq = tid >> 7;
+      uint32_t own = 0;
+      if (wi < 8 * nl) {
+        const int L = L0 + (wi >> 3), gq = wi & 3, S = L / 5, t = L - 5 * S;
+        // halves 2 i + e of the piece: column 160 S + pair_col(20 gq + 4 t + i) + 5 e
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float inv_f;
-          const int off = rec_byte(wrow0 + 16 * a + 4 * g + i, inv_f);
+          const int c = S * moe::kSbCols + moe::pair_col(20 * gq + 4 * t + i);
+          own |= (c >= c0 && c < c1 ? 1u : 0u) << (2 * i);
+          own |= (c + 5 >= c0 && c + 5 < c1 ? 1u : 0u) << (2 * i + 1);
+        }
+      }
+      const size_t dst_off = (size_t)L0 * 128 + (size_t)wi * 16;
+      __syncthreads();  // every wave is done with the x ring and the weight slots
 #pragma unroll
-          for (int nt = 0; nt < kTT; ++nt) {
-            const int n = 16 * nt + r16;
-            if (nt < ntt && n < m) {
-              const int row = row_sh[n];
-              if (row >= 0) {
-                const float gv = acc[a][nt][i], uv = acc[a + 2][nt][i];
-                const float h = gv / (1.0f + __expf(-gv)) * uv * inv_f;
-                const _Float16 hh = (_Float16)h, hl = (_Float16)(h - (float)hh);
-                uint8_t *o = P.hrec + (size_t)row * P.hrec_b + off;
-                *reinterpret_cast<_Float16 *>(o) = hh;
-                *reinterpret_cast<_Float16 *>(o + 64) = hl;
+      for (int half = 0; half < kTT / 4; ++half) {
+        if (16 * 4 * half >= m) break;  // uniform: no token in this half
+        if (wact) {
+#pragma unroll
+          for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float inv_f;
+              const int off = rec_byte(wrow0 + 16 * a + 4 * g + i, inv_f) - L0 * 128;
+#pragma unroll
+              for (int q4 = 0; q4 < 4; ++q4) {
+                const int nt = 4 * half + q4, n = 16 * nt + r16;
+                if (nt < ntt && n < m) {
+                  const float gv = acc[a][nt][i], uv = acc[a + 2][nt][i];
+                  const float h = gv / (1.0f + __expf(-gv)) * uv * inv_f;
+                  const _Float16 hh = (_Float16)h, hl = (_Float16)(h - (float)hh);
+                  uint8_t *o = smem + (16 * q4 + r16) * istride + off;
+                  *reinterpret_cast<_Float16 *>(o) = hh;
+                  *reinterpret_cast<_Float16 *>(o + 64) = hl;
+                }
               }
+            }
+        }
+        __syncthreads();  // the half's image is complete
+        const int n_tok = min(kImgTokens, m - kImgTokens * half);
+        if (own) {
+          for (int nloc = tq; nloc < n_tok; nloc += kPThreads / 128) {
+            const int row = row_sh[kImgTokens * half + nloc];
+            if (row < 0) continue;
+            const uint8_t *src = smem + nloc * istride + wi * 16;
+            uint8_t *dst = P.hrec + (size_t)row * P.hrec_b + dst_off;
+            if (own == 0xffu) {
+              *reinterpret_cast<u4 *>(dst) = *reinterpret_cast<const u4 *>(src);
+            } else {
+#pragma unroll
+              for (int j = 0; j < 8; ++j)
+                if (own >> j & 1u)
+                  *reinterpret_cast<uint16_t *>(dst + 2 * j) = *reinterpret_cast<const uint16_t *>(src + 2 * j);
             }
           }
         }
+        __syncthreads();  // the image is read out before the next half or item reuses it
+      }
     } else {
+      if (!wact) continue;
 #pragma unroll
       for (int nt = 0; nt < kTT; ++nt) {
         const int n = 16 * nt + r16;
