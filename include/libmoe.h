@@ -157,8 +157,12 @@ moe_status moe_cache_resolve_async(moe_ctx *ctx, int32_t layer, const int32_t *i
  * columns), MOE_ERR_INVALID above; MOE_PATH_PREFILL -- the same precision
  * (dequantised weights rounded once to fp16, x and h carried as two fp16
  * halves, fp32 accumulation) as a grouped GEMM, needs d_model and d_ff to be
- * multiples of 64; MOE_PATH_AUTO -- decode for T <= 64 when the dims allow
- * it, prefill otherwise.  Expert ids outside [0, n_experts) are ignored
+ * multiples of 64 and the call's activation records to stay under 4 GiB --
+ * T * 5 * ceil(d_model / 160) * 128 bytes for x and (T * top_k + T) * 5 *
+ * ceil(d_ff / 160) * 128 bytes for h (MOE_ERR_INVALID otherwise; d_ff =
+ * 8192 reaches it near T = 12,000); MOE_PATH_AUTO -- decode for T <= 64 when
+ * the dims allow it, prefill otherwise when it can take the call, else
+ * decode.  Expert ids outside [0, n_experts) are ignored
  * (their y_pairs rows are not written).  Uses the context's workspace: calls
  * on one context must not overlap.  Asynchronous; deterministic (no
  * floating-point atomics). */

@@ -292,11 +292,16 @@ extern "C" moe_status moe_expert_ffn(moe_ctx *c, int32_t layer, const float *x, 
   if (st != MOE_OK) return st;
   MOE_CHECK(path == MOE_PATH_AUTO || path == MOE_PATH_DECODE || path == MOE_PATH_PREFILL, MOE_ERR_INVALID,
             "moe_expert_ffn: unknown path");
-  const bool prefill_ok = c->cfg.d_model % 64 == 0 && c->cfg.d_ff % 64 == 0;
+  // the prefill kernels address the x and h records with 32-bit byte offsets
+  const uint64_t xrec_bytes = (uint64_t)T * 5 * c->L.gate.nsb * 128;
+  const uint64_t hrec_bytes = ((uint64_t)T * c->cfg.top_k + T) * 5 * c->L.down.nsb * 128;
+  const bool prefill_ok = c->cfg.d_model % 64 == 0 && c->cfg.d_ff % 64 == 0 && xrec_bytes <= UINT32_MAX &&
+                          hrec_bytes <= UINT32_MAX;
   const bool decode_ok = c->L.gate.nsb <= moe::kDecodeMaxNsb && c->L.down.nsb <= moe::kDecodeMaxNsb;
   if (path == MOE_PATH_AUTO) path = ((T <= 64 && decode_ok) || !prefill_ok) ? MOE_PATH_DECODE : MOE_PATH_PREFILL;
   MOE_CHECK(path != MOE_PATH_PREFILL || prefill_ok, MOE_ERR_INVALID,
-            "moe_expert_ffn: the prefill path needs d_model and d_ff to be multiples of 64");
+            "moe_expert_ffn: the prefill path needs d_model and d_ff to be multiples of 64 and the call's x and h "
+            "records under 4 GiB");
   MOE_CHECK(path != MOE_PATH_DECODE || decode_ok, MOE_ERR_INVALID,
             "moe_expert_ffn: the decode path takes d_model and d_ff up to 2048 (13 superblocks of 160 columns)");
   hipStream_t s = as_stream(stream);

@@ -129,11 +129,13 @@ __device__ __attribute__((always_inline)) inline bool entry_token(const PrefillP
 
 __device__ __attribute__((always_inline)) inline f4 mfma(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 
-// Where the lane's 4 weight rows live: tile a's words at code + coff[a], its
-// scales at scale + soff[a] (the offsets are the same for the whole wave)
+// Where the lane's 4 weight rows live, as byte offsets into the entry's blob:
+// tile a's words at code + coff[a], its scales at scale + soff[a] (coff and
+// soff are the same for the whole wave)
 struct WRows {
-  const uint8_t *code;   // word quad g of superblock 0 of tile 0's row
-  const uint8_t *scale;  // tile 0's row of scales
+  uint64_t blob;    // the entry's blob (wave-uniform)
+  uint32_t code;    // word quad g of superblock 0 of tile 0's row
+  uint32_t scale;   // tile 0's row of scales
   uint32_t coff[4], soff[4];
   int nblk;
 };
@@ -151,8 +153,9 @@ struct WRows {
 //   * each step starts by waiting until its tile's copies have landed (loads
 //     complete in order, so everything issued before them has too), then one
 //     barrier publishes the tile to all waves.
-// Weights are read into registers at step 0 of their superblock (a quad and a
-// scale pair per tile), dequantised per step as before.
+// Weights stay in their LDS slot for the superblock: each step reads the one
+// or two words of the lane's quad it needs, and the scale pairs are read once
+// per superblock; fragments are dequantised a step ahead of their MFMAs.
 constexpr int kXD = 3;                      // x tiles copied this many steps ahead
 constexpr int kXRing = 4;                   // slots of the x ring (> kXD)
 constexpr int kQuadB = 1024;                // one tile's quads of one wave: 64 lanes x 16 B
@@ -191,17 +194,20 @@ __device__ __attribute__((always_inline)) inline void wait_vm() {
 }
 
 struct XCopy {
-  const uint8_t *src[Geo::kCopies];  // this thread's granules of step 0 (row, piece)
-  uint32_t lds[Geo::kCopies];        // LDS byte of each granule inside a step tile
+  uint64_t base;                // the record (wave-uniform)
+  uint32_t src[Geo::kCopies];   // byte offset of this thread's granules of step 0 (row, piece)
+  uint32_t lds;                 // LDS byte of the wave's first granule inside a step tile
 };
 
 // the copies of step s's tile into ring slot s & 3 (s clamped: past the last
-// step the last tile is copied again into a slot nobody reads)
+// step the last tile is copied again into a slot nobody reads); copy i of the
+// wave fills granules 64 (w + 8 i) .. + 63
 __device__ __attribute__((always_inline)) inline void copy_x(const XCopy &X, uint32_t ring, int s, int nsteps) {
   const int sc = min(s, nsteps - 1);
   const uint32_t slot = ring + (uint32_t)(s & (kXRing - 1)) * Geo::kStepB;
 #pragma unroll
-  for (int i = 0; i < Geo::kCopies; ++i) moe::lds_copy16(X.src[i] + (size_t)sc * Geo::kRowB, slot + X.lds[i]);
+  for (int i = 0; i < Geo::kCopies; ++i)
+    moe::lds_copy16_off(X.base, X.src[i] + (uint32_t)sc * Geo::kRowB, slot + X.lds + (uint32_t)(i * kPThreads * 16));
 }
 
 // superblock S's weights (S clamped) into weight slot S & 1: per tile the
@@ -214,25 +220,21 @@ __device__ __attribute__((always_inline)) inline void copy_w(const WRows &R, uin
   const int Sc = min(S, nsb - 1);
   const uint32_t slot = wbase + (uint32_t)(S & 1) * kWSlotB + (uint32_t)w * 4 * kTileWB;
   const int crow = lane / 3, dk = min((5 * Sc) / 2 + (lane - 3 * crow), R.nblk / 2 - 1);
-  const int rdelta = (crow - r16) * R.nblk * 2;  // the copied row from the lane's own (rows are consecutive)
+  // scale dword dk of row crow (rows are consecutive, crow - r16 rows from the lane's own)
+  const uint32_t sco = (uint32_t)((int)R.scale + (crow - r16) * R.nblk * 2 + 4 * dk);
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
     const uint32_t t0 = slot + (uint32_t)a * kTileWB;
-    moe::lds_copy16(R.code + (R.coff[a] + (uint32_t)Sc * 64), t0);
-    if (lane < 48) moe::lds_copy4(R.scale + ((int)R.soff[a] + rdelta + 4 * dk), t0 + kQuadB);
+    moe::lds_copy16_off(R.blob, R.code + R.coff[a] + (uint32_t)Sc * 64, t0);
+    if (lane < 48) moe::lds_copy4_off(R.blob, sco + R.soff[a], t0 + kQuadB);
   }
 }
 
-struct WReg {
-  uint32_t q[4][4];  // [tile][word]
-  uint32_t P[4];     // [tile]: s_b0 | s_b1 << 16
-};
-
-// superblock S's weights from its LDS slot into registers: the quad, and the
-// scale pair b0 = min(5 S + g, nblk - 1), b1 = min(b0 + 1, nblk - 1) from the
-// row's three dwords (block b is half (b - 2 d0) of dword (b - 2 d0) / 2)
-__device__ __attribute__((always_inline)) inline void read_w(const uint8_t *wlds, int S, int g, int r16, int nblk,
-                                                             int w, int lane, WReg &o) {
+// superblock S's scale pairs from its LDS slot, one per tile: b0 = min(5 S +
+// g, nblk - 1), b1 = min(b0 + 1, nblk - 1) from the row's three dwords (block
+// b is half (b - 2 d0) of dword (b - 2 d0) / 2)
+__device__ __attribute__((always_inline)) inline void read_p(const uint8_t *wlds, int S, int g, int r16, int nblk,
+                                                             int w, uint32_t (&P)[4]) {
   const uint8_t *slot = wlds + (S & 1) * kWSlotB + w * 4 * kTileWB;
   const int d0 = (5 * S) / 2;
   const int b0 = min(5 * S + g, nblk - 1), b1 = min(b0 + 1, nblk - 1);
@@ -240,69 +242,103 @@ __device__ __attribute__((always_inline)) inline void read_w(const uint8_t *wlds
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
     const uint8_t *t0 = slot + a * kTileWB;
-    const u4 q = *reinterpret_cast<const u4 *>(t0 + 16 * lane);
-    o.q[a][0] = q.x;
-    o.q[a][1] = q.y;
-    o.q[a][2] = q.z;
-    o.q[a][3] = q.w;
     const uint32_t e0 = *reinterpret_cast<const uint32_t *>(t0 + kQuadB + 4 * (3 * r16 + (j0 >> 1)));
     const uint32_t e1 = *reinterpret_cast<const uint32_t *>(t0 + kQuadB + 4 * (3 * r16 + (j1 >> 1)));
     const uint32_t s0 = (j0 & 1) ? e0 >> 16 : e0 & 0xffffu, s1 = (j1 & 1) ? e1 >> 16 : e1 & 0xffffu;
-    o.P[a] = s0 | (s1 << 16);
+    P[a] = s0 | (s1 << 16);
   }
+}
+
+// A fragment of step t of one tile from the lane's word quad in LDS (`quad`):
+// only the words holding pairs 4t .. 4t+3 are read
+template <int t>
+__device__ __attribute__((always_inline)) inline h8 deq_step(const uint8_t *quad, uint32_t P, const moe::Consts &K,
+                                                             const uint32_t (&sel)[6]) {
+  constexpr int k0 = (4 * t) / 5, k1 = (4 * t + 3) / 5;
+  uint32_t q[4] = {0u, 0u, 0u, 0u};
+  q[k0] = *reinterpret_cast<const uint32_t *>(quad + 4 * k0);
+  if constexpr (k1 != k0) q[k1] = *reinterpret_cast<const uint32_t *>(quad + 4 * k1);
+  return moe::quad_a_sel<t>(q, K, P, sel);
 }
 
 // One K step (t of superblock S; FIRST: superblock 0): wait for the step's
 // tile, publish it, issue the copies of later data, then the wave's 4 row
 // tiles x the entry's token tiles, every product twice (the activations' hi
-// and lo halves).
-template <int t, bool FIRST>
+// and lo halves).  The A fragments of the step were dequantised during the
+// previous one; this step's MFMAs run beside the dequantisation of the next
+// step's (so VALU work fills the matrix pipe's shadow).  At step 4 the next
+// superblock's scale pairs replace the registers, whose last use was step 3's
+// dequantisation of step 4.  FULL (an entry of kPM tokens): no token tile
+// is skipped, so the step is one block the scheduler interleaves as one
+// MFMA beside one VALU instruction.
+template <int t, bool FIRST, bool FULL>
 __device__ __attribute__((always_inline)) inline void k_step(int S, int nsb, int nsteps, const WRows &R, int g, int r16,
-                                                             int w, int lane, WReg &W, const XCopy &X, uint32_t ring,
-                                                             const uint8_t *xring, uint32_t wbase, const uint8_t *wlds,
-                                                             const uint32_t (&sel)[6], const moe::Consts &K, int ntt,
-                                                             bool wact, int rl_hi, int rl_lo, f4 (&acc)[4][kTT]) {
+                                                             int w, int lane, uint32_t (&P)[4], h8 (&A)[4], const XCopy &X,
+                                                             uint32_t ring, const uint8_t *xring, uint32_t wbase,
+                                                             const uint8_t *wlds, const uint32_t (&sel)[6],
+                                                             const moe::Consts &K, int ntt, bool wact, int rl_hi,
+                                                             int rl_lo, f4 (&acc)[4][kTT]) {
   using G = Geo;
   const int s = 5 * S + t;
   wait_vm<vm_after(t, FIRST)>();
   __syncthreads();  // step s's tile is in LDS for every wave; slot (s - 1) & 3 is no longer read
   copy_x(X, ring, s + kXD, nsteps);
-  if constexpr (t == 0) {
-    copy_w(R, wbase, S + 1, nsb, r16, lane, w);
-    read_w(wlds, S, g, r16, R.nblk, w, lane, W);
-  }
+  if constexpr (t == 0) copy_w(R, wbase, S + 1, nsb, r16, lane, w);
   if (!wact) return;  // wave-uniform: rows past the matrix
-  h8 A[4];
+  const uint8_t *quads = wlds + w * 4 * kTileWB + 16 * lane;  // tile 0's quad of the lane in slot 0
+  if constexpr (FIRST && t == 0) {
+    // the very first step has no previous one to dequantise its fragments
+    read_p(wlds, 0, g, r16, R.nblk, w, P);
 #pragma unroll
-  for (int a = 0; a < 4; ++a) A[a] = moe::quad_a_sel<t>(W.q[a], K, W.P[a], sel);
+    for (int a = 0; a < 4; ++a) A[a] = deq_step<0>(quads + a * kTileWB, P[a], K, sel);
+  }
+  // superblock S + 1's words landed with step 5 S + 4's tile (copied after them)
+  if constexpr (t == 4) read_p(wlds, S + 1, g, r16, R.nblk, w, P);
+  constexpr int tn = t == 4 ? 0 : t + 1;
+  const uint8_t *qn = quads + ((t == 4 ? S + 1 : S) & 1) * kWSlotB;  // the next step's superblock slot
+  h8 An[4];
   // B operands one read ahead of their MFMAs
   const uint8_t *tile = xring + (s & (kXRing - 1)) * G::kStepB;
   h8 cur = *reinterpret_cast<const h8 *>(tile + rl_hi);
 #pragma unroll
   for (int nt = 0; nt < kTT; ++nt) {
-    if (nt < ntt) {  // wave-uniform: token tiles holding tokens
+    if (FULL || nt < ntt) {  // wave-uniform: token tiles holding tokens
       const h8 bl = *reinterpret_cast<const h8 *>(tile + nt * 16 * G::kRowB + rl_lo);
 #pragma unroll
       for (int a = 0; a < 4; ++a) acc[a][nt] = mfma(A[a], cur, acc[a][nt]);
-      if (nt + 1 < ntt) cur = *reinterpret_cast<const h8 *>(tile + (nt + 1) * 16 * G::kRowB + rl_hi);
+      if (nt + 1 < kTT && (FULL || nt + 1 < ntt)) cur = *reinterpret_cast<const h8 *>(tile + (nt + 1) * 16 * G::kRowB + rl_hi);
 #pragma unroll
       for (int a = 0; a < 4; ++a) acc[a][nt] = mfma(A[a], bl, acc[a][nt]);
     }
+    if (nt < 4) An[nt] = deq_step<tn>(qn + nt * kTileWB, P[nt], K, sel);
   }
+  if constexpr (FULL) {
+#pragma unroll
+    for (int i = 0; i < 8 * kTT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);  // one VALU instruction
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a) A[a] = An[a];
 }
 
-template <bool FIRST>
+template <bool FIRST, bool FULL>
 __device__ __attribute__((always_inline)) inline void k_superblock(int S, int nsb, int nsteps, const WRows &R, int g,
-                                                                   int r16, int w, int lane, WReg &W, const XCopy &X,
-                                                                   uint32_t ring, const uint8_t *xring, uint32_t wbase,
-                                                                   const uint8_t *wlds, const uint32_t (&sel)[6],
-                                                                   const moe::Consts &K, int ntt, bool wact, int rl_hi,
-                                                                   int rl_lo, f4 (&acc)[4][kTT]) {
-  k_step<0, FIRST>(S, nsb, nsteps, R, g, r16, w, lane, W, X, ring, xring, wbase, wlds, sel, K, ntt, wact, rl_hi, rl_lo, acc);
-  k_step<1, FIRST>(S, nsb, nsteps, R, g, r16, w, lane, W, X, ring, xring, wbase, wlds, sel, K, ntt, wact, rl_hi, rl_lo, acc);
-  k_step<2, FIRST>(S, nsb, nsteps, R, g, r16, w, lane, W, X, ring, xring, wbase, wlds, sel, K, ntt, wact, rl_hi, rl_lo, acc);
-  k_step<3, FIRST>(S, nsb, nsteps, R, g, r16, w, lane, W, X, ring, xring, wbase, wlds, sel, K, ntt, wact, rl_hi, rl_lo, acc);
-  k_step<4, FIRST>(S, nsb, nsteps, R, g, r16, w, lane, W, X, ring, xring, wbase, wlds, sel, K, ntt, wact, rl_hi, rl_lo, acc);
+                                                                   int r16, int w, int lane, uint32_t (&P)[4], h8 (&A)[4],
+                                                                   const XCopy &X, uint32_t ring, const uint8_t *xring,
+                                                                   uint32_t wbase, const uint8_t *wlds,
+                                                                   const uint32_t (&sel)[6], const moe::Consts &K,
+                                                                   int ntt, bool wact, int rl_hi, int rl_lo,
+                                                                   f4 (&acc)[4][kTT]) {
+#define MOE_K_STEP(t) \
+  k_step<t, FIRST, FULL>(S, nsb, nsteps, R, g, r16, w, lane, P, A, X, ring, xring, wbase, wlds, sel, K, ntt, wact, rl_hi, rl_lo, acc)
+  MOE_K_STEP(0);
+  MOE_K_STEP(1);
+  MOE_K_STEP(2);
+  MOE_K_STEP(3);
+  MOE_K_STEP(4);
+#undef MOE_K_STEP
 }
 
 // NMAT = 2: gate/up -> h record; NMAT = 1: down -> y.  One workgroup per CU
@@ -373,8 +409,9 @@ __global__ void __launch_bounds__(kPThreads, 1) prefill_kernel(PrefillParams P) 
       const moe::MatLayout &M = NMAT == 2 ? P.gate : P.down;
       const int rbase = wact ? wrow0 : rows_out - kWRows;  // rows_out >= 64 >= kWRows
       R.nblk = M.nblk;
-      R.code = blob + M.code_off + (size_t)(rbase + r16) * M.wpr * 4 + g * 16;
-      R.scale = blob + M.scale_off + (size_t)(rbase + r16) * M.nblk * 2;
+      R.blob = moe::uniform_base(blob);
+      R.code = M.code_off + (uint32_t)(rbase + r16) * M.wpr * 4 + g * 16;
+      R.scale = M.scale_off + (uint32_t)(rbase + r16) * M.nblk * 2;
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int ta = NMAT == 2 ? (a & 1) : a;  // 16-row tile within the wave's rows
@@ -389,14 +426,14 @@ __global__ void __launch_bounds__(kPThreads, 1) prefill_kernel(PrefillParams P) 
     // its piece swizzled by the row; lands at LDS byte 16 q of the tile
     XCopy X;
     {
-      const uint8_t *base = NMAT == 2 ? P.xrec : P.hrec;
-      const size_t stride = (size_t)(NMAT == 2 ? P.xrec_b : P.hrec_b);
+      const uint32_t stride = (uint32_t)(NMAT == 2 ? P.xrec_b : P.hrec_b);
+      X.base = moe::uniform_base(NMAT == 2 ? P.xrec : P.hrec);
+      X.lds = (uint32_t)(64 * w) * 16u;
 #pragma unroll
       for (int i = 0; i < G::kCopies; ++i) {
         const int q = tid + kPThreads * i, n = q / G::kGran, pos = q - n * G::kGran;
         const int rr = n < m ? (NMAT == 2 ? tok_sh[n] : row_sh[n]) : -1;
-        X.src[i] = base + (size_t)(rr < 0 ? 0 : rr) * stride + (uint32_t)(pos ^ G::swz(n)) * 16u;
-        X.lds[i] = (uint32_t)q * 16u;
+        X.src[i] = (uint32_t)(rr < 0 ? 0 : rr) * stride + (uint32_t)(pos ^ G::swz(n)) * 16u;
       }
     }
     f4 acc[4][kTT];
@@ -408,12 +445,21 @@ __global__ void __launch_bounds__(kPThreads, 1) prefill_kernel(PrefillParams P) 
 #pragma unroll
     for (int s0 = 0; s0 < kXD; ++s0) copy_x(X, ring, s0, nsteps);
     copy_w(R, wbase, 0, nsb, r16, lane, w);
-    WReg W;
-    k_superblock<true>(0, nsb, nsteps, R, g, r16, w, lane, W, X, ring, xring, wbase, wlds, sel, K, ntt, wact, rl_hi,
-                       rl_lo, acc);
-    for (int S = 1; S < nsb; ++S)
-      k_superblock<false>(S, nsb, nsteps, R, g, r16, w, lane, W, X, ring, xring, wbase, wlds, sel, K, ntt, wact,
-                          rl_hi, rl_lo, acc);
+    uint32_t Pw[4];
+    h8 A[4];
+    if (ntt == kTT) {  // uniform
+      k_superblock<true, true>(0, nsb, nsteps, R, g, r16, w, lane, Pw, A, X, ring, xring, wbase, wlds, sel, K, ntt, wact,
+                               rl_hi, rl_lo, acc);
+      for (int S = 1; S < nsb; ++S)
+        k_superblock<false, true>(S, nsb, nsteps, R, g, r16, w, lane, Pw, A, X, ring, xring, wbase, wlds, sel, K, ntt,
+                                  wact, rl_hi, rl_lo, acc);
+    } else {
+      k_superblock<true, false>(0, nsb, nsteps, R, g, r16, w, lane, Pw, A, X, ring, xring, wbase, wlds, sel, K, ntt,
+                                wact, rl_hi, rl_lo, acc);
+      for (int S = 1; S < nsb; ++S)
+        k_superblock<false, false>(S, nsb, nsteps, R, g, r16, w, lane, Pw, A, X, ring, xring, wbase, wlds, sel, K, ntt,
+                                   wact, rl_hi, rl_lo, acc);
+    }
     // every copy of this item (the ones past the last step included) has
     // landed before the next item's prologue reuses the slots
     wait_vm<0>();
@@ -441,6 +487,13 @@ __global__ void __launch_bounds__(kPThreads, 1) prefill_kernel(PrefillParams P) 
         }
       }
       const size_t dst_off = (size_t)L0 * 128 + (size_t)wi * 16;
+      // image offset and 1 / f of the lane's 8 columns
+      int off[8];
+      float inv_f[8];
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) off[4 * a + i] = rec_byte(wrow0 + 16 * a + 4 * g + i, inv_f[4 * a + i]) - L0 * 128;
       __syncthreads();  // every wave is done with the x ring and the weight slots
 #pragma unroll
       for (int half = 0; half < kTT / 4; ++half) {
@@ -450,16 +503,14 @@ __global__ void __launch_bounds__(kPThreads, 1) prefill_kernel(PrefillParams P) 
           for (int a = 0; a < 2; ++a)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              float inv_f;
-              const int off = rec_byte(wrow0 + 16 * a + 4 * g + i, inv_f) - L0 * 128;
 #pragma unroll
               for (int q4 = 0; q4 < 4; ++q4) {
                 const int nt = 4 * half + q4, n = 16 * nt + r16;
                 if (nt < ntt && n < m) {
                   const float gv = acc[a][nt][i], uv = acc[a + 2][nt][i];
-                  const float h = gv / (1.0f + __expf(-gv)) * uv * inv_f;
+                  const float h = gv / (1.0f + __expf(-gv)) * uv * inv_f[4 * a + i];
                   const _Float16 hh = (_Float16)h, hl = (_Float16)(h - (float)hh);
-                  uint8_t *o = smem + (16 * q4 + r16) * istride + off;
+                  uint8_t *o = smem + (16 * q4 + r16) * istride + off[4 * a + i];
                   *reinterpret_cast<_Float16 *>(o) = hh;
                   *reinterpret_cast<_Float16 *>(o + 64) = hl;
                 }
@@ -468,20 +519,33 @@ __global__ void __launch_bounds__(kPThreads, 1) prefill_kernel(PrefillParams P) 
         }
         __syncthreads();  // the half's image is complete
         const int n_tok = min(kImgTokens, m - kImgTokens * half);
-        if (own) {
-          for (int nloc = tq; nloc < n_tok; nloc += kPThreads / 128) {
+        constexpr int kTq = kPThreads / 128;  // token stride of a thread
+        if (own == 0xffu) {
+          // 4 tokens at a time: every LDS read before the stores
+#pragma unroll
+          for (int j0 = 0; j0 < kImgTokens / kTq; j0 += 4) {
+            u4 v[4];
+            int rw[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int nloc = tq + kTq * (j0 + j);  // < kImgTokens: the image read stays in it
+              rw[j] = nloc < n_tok ? row_sh[kImgTokens * half + nloc] : -1;
+              v[j] = *reinterpret_cast<const u4 *>(smem + nloc * istride + wi * 16);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (rw[j] >= 0) *reinterpret_cast<u4 *>(P.hrec + (size_t)rw[j] * P.hrec_b + dst_off) = v[j];
+          }
+        } else if (own) {
+          for (int nloc = tq; nloc < n_tok; nloc += kTq) {
             const int row = row_sh[kImgTokens * half + nloc];
             if (row < 0) continue;
             const uint8_t *src = smem + nloc * istride + wi * 16;
             uint8_t *dst = P.hrec + (size_t)row * P.hrec_b + dst_off;
-            if (own == 0xffu) {
-              *reinterpret_cast<u4 *>(dst) = *reinterpret_cast<const u4 *>(src);
-            } else {
 #pragma unroll
-              for (int j = 0; j < 8; ++j)
-                if (own >> j & 1u)
-                  *reinterpret_cast<uint16_t *>(dst + 2 * j) = *reinterpret_cast<const uint16_t *>(src + 2 * j);
-            }
+            for (int j = 0; j < 8; ++j)
+              if (own >> j & 1u)
+                *reinterpret_cast<uint16_t *>(dst + 2 * j) = *reinterpret_cast<const uint16_t *>(src + 2 * j);
           }
         }
         __syncthreads();  // the image is read out before the next half or item reuses it

@@ -43,4 +43,41 @@ __device__ inline void lds_copy4(const void *src, uint32_t lds) {
       : "memory");
 }
 
+// The same with a wave-uniform 64-bit base and a per-lane 32-bit byte offset
+// (the address is base + off): one VGPR per copy address instead of two.
+// (readfirstlane returns int: each half goes through uint32_t so that the low
+// half is zero-extended, never sign-extended into the high one)
+__device__ inline uint64_t uniform_base(const void *base) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  return (uint64_t)lo | ((uint64_t)hi << 32);
+}
+
+__device__ inline void lds_copy16_off(uint64_t base, uint32_t off, uint32_t lds) {
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(base)
+      : "memory");
+}
+
+__device__ inline void lds_copy4_off(uint64_t base, uint32_t off, uint32_t lds) {
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(base)
+      : "memory");
+}
+
 }  // namespace moe
