@@ -99,9 +99,18 @@ struct PrefillParams {
   int d_model, d_ff;
 };
 
+// A wave-uniform read of data that no kernel of this launch writes (the work
+// list, the bucketing and the slot map): through the constant address space,
+// so it is a scalar load rather than a vector load, whose wait would also
+// wait for every copy in flight.
+template <class T>
+__device__ __attribute__((always_inline)) inline T ld_uniform(const T *p) {
+  return *(const __attribute__((address_space(4))) T *)p;
+}
+
 __device__ __attribute__((always_inline)) inline const uint8_t *entry_blob(const PrefillParams &P, const moe::WorkEntry &we) {
   if (we.expert < 0) return P.shared_pool + (size_t)P.layer * P.stride;
-  const int slot = P.slot_of_pair ? P.slot_of_pair[P.perm[we.first]] : P.layer * P.E + we.expert;
+  const int slot = P.slot_of_pair ? ld_uniform(P.slot_of_pair + ld_uniform(P.perm + we.first)) : P.layer * P.E + we.expert;
   if (slot < 0 || slot >= P.n_slots) return nullptr;  // never read outside the pool
   return P.slot_pool + (size_t)slot * P.stride;
 }
@@ -112,19 +121,56 @@ __device__ __attribute__((always_inline)) inline bool entry_ok(const PrefillPara
   return we.expert >= 0 ? (we.expert < P.E && we.first + we.m <= P.T * P.k) : (we.first + we.m <= P.T);
 }
 
-// token and record row (pair id, or T*k + token for the shared expert) of
-// entry column n
-__device__ __attribute__((always_inline)) inline bool entry_token(const PrefillParams &P, const moe::WorkEntry &we, int n, int &tok, int &row) {
-  if (we.expert >= 0) {
-    const int pair = P.perm[we.first + n];
-    if (pair < 0 || pair >= P.T * P.k) return false;
-    tok = pair / P.k;
-    row = pair;
-  } else {
-    tok = we.first + n;
-    row = P.T * P.k + tok;
+// a work entry's fields, one scalar load each (a struct read can be narrowed
+// to three dwords, for which there is no scalar load)
+__device__ __attribute__((always_inline)) inline moe::WorkEntry ld_entry(const moe::WorkEntry *p) {
+  moe::WorkEntry we;
+  we.expert = ld_uniform(&p->expert);
+  we.first = ld_uniform(&p->first);
+  we.m = ld_uniform(&p->m);
+  we.pad = 0;
+  return we;
+}
+
+// The first item at or after `it` (stepping by istep) whose entry has work
+// and whose blob exists, with that entry and blob; i_end when none is left.
+// Wave-uniform (scalar loads).
+__device__ __attribute__((always_inline)) inline int fetch_item(const PrefillParams &P, int it, int istep, int i_end,
+                                                                int nrt, moe::WorkEntry &we, const uint8_t *&blob) {
+  for (; it < i_end; it += istep) {
+    we = ld_entry(P.work + it / nrt);
+    if (!entry_ok(P, we)) continue;
+    blob = entry_blob(P, we);
+    if (blob) break;
   }
-  return true;
+  return it;
+}
+
+// A routed entry's pair ids into LDS `pairs` (kPM ints) by waves 0 and 1
+// with direct copies (column n reads perm[first + min(n, m - 1)], inside the
+// entry), which no compiler-inserted wait covers: the K loop's own waits
+// (and the drain at its end) cover them.  Nothing for the shared expert.
+__device__ __attribute__((always_inline)) inline void copy_pairs(const PrefillParams &P, const moe::WorkEntry &we,
+                                                                 int *pairs, int w, int lane) {
+  if (we.expert < 0 || w >= kPM / 64) return;  // wave-uniform
+  const int n = 64 * w + lane;
+  moe::lds_copy4_off(moe::uniform_base(P.perm), 4u * (uint32_t)(we.first + min(n, we.m - 1)),
+                     moe::lds_addr(pairs + 64 * w));
+}
+
+// record row of entry column n (the pair id, or T*k + token for the shared
+// expert), -1 for a column without a token or an out-of-range pair
+__device__ __attribute__((always_inline)) inline int entry_row(const PrefillParams &P, const moe::WorkEntry &we, int n,
+                                                               const int *pairs) {
+  if (n >= we.m) return -1;
+  if (we.expert < 0) return P.T * P.k + we.first + n;
+  const int pair = pairs[n];
+  return pair >= 0 && pair < P.T * P.k ? pair : -1;
+}
+
+// token of a record row from entry_row (>= 0)
+__device__ __attribute__((always_inline)) inline int row_token(const PrefillParams &P, int row) {
+  return row < P.T * P.k ? row / P.k : row - P.T * P.k;
 }
 
 __device__ __attribute__((always_inline)) inline f4 mfma(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
@@ -269,8 +315,7 @@ __device__ __attribute__((always_inline)) inline h8 deq_step(const uint8_t *quad
 // step's (so VALU work fills the matrix pipe's shadow).  At step 4 the next
 // superblock's scale pairs replace the registers, whose last use was step 3's
 // dequantisation of step 4.  FULL (an entry of kPM tokens): no token tile
-// is skipped, so the step is one block the scheduler interleaves as one
-// MFMA beside one VALU instruction.
+// is skipped, so the step is one branch-free block for the scheduler.
 template <int t, bool FIRST, bool FULL>
 __device__ __attribute__((always_inline)) inline void k_step(int S, int nsb, int nsteps, const WRows &R, int g, int r16,
                                                              int w, int lane, uint32_t (&P)[4], h8 (&A)[4], const XCopy &X,
@@ -311,13 +356,6 @@ __device__ __attribute__((always_inline)) inline void k_step(int S, int nsb, int
       for (int a = 0; a < 4; ++a) acc[a][nt] = mfma(A[a], bl, acc[a][nt]);
     }
     if (nt < 4) An[nt] = deq_step<tn>(qn + nt * kTileWB, P[nt], K, sel);
-  }
-  if constexpr (FULL) {
-#pragma unroll
-    for (int i = 0; i < 8 * kTT; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);  // one VALU instruction
-    }
   }
 #pragma unroll
   for (int a = 0; a < 4; ++a) A[a] = An[a];
@@ -360,7 +398,10 @@ __global__ void __launch_bounds__(kPThreads, 1) prefill_kernel(PrefillParams P) 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmemB];
   uint8_t *const xring = smem;                          // K loop: x ring
   uint8_t *const wlds = smem + kXRing * G::kStepB;      // K loop: weight slots
-  __shared__ int row_sh[kPM], tok_sh[kPM];
+  // pair ids of the current item's entry and of the next one's (copied in
+  // during the current item, before its stores, so that no load waits for
+  // those stores)
+  __shared__ int pair_sh[2][kPM];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
   const moe::MatLayout &M0 = NMAT == 2 ? P.gate : P.down;
@@ -369,7 +410,7 @@ __global__ void __launch_bounds__(kPThreads, 1) prefill_kernel(PrefillParams P) 
   constexpr int kWRows = NMAT == 2 ? 32 : 64;  // output rows per wave (gate/up: h rows)
   constexpr int kGRows = kPWaves * kWRows;
   const int nrt = (rows_out + kGRows - 1) / kGRows;
-  const int n_items = min(P.n_work[0], P.max_work) * nrt;
+  const int n_items = min(ld_uniform(P.n_work), P.max_work) * nrt;
   // Workgroup b runs on die b % 8 (round-robin dispatch); each die takes a
   // contiguous range of items, so the row blocks of one entry and the entries
   // of one expert share that die's L2 (activations and weights re-read there).
@@ -384,20 +425,19 @@ __global__ void __launch_bounds__(kPThreads, 1) prefill_kernel(PrefillParams P) 
   // step tile: granule piece ^ swz(row), piece g (hi) or 4 + g (lo)
   const int sw = G::swz(r16);
   const int rl_hi = r16 * G::kRowB + ((g ^ sw) << 4), rl_lo = r16 * G::kRowB + (((4 + g) ^ sw) << 4);
-  for (int it = xcd * per + blockIdx.x / kXcds; it < i_end; it += istep) {
+  moe::WorkEntry we_n;
+  const uint8_t *blob_n = nullptr;
+  int it_n = fetch_item(P, xcd * per + blockIdx.x / kXcds, istep, i_end, nrt, we_n, blob_n);
+  if (it_n < i_end) copy_pairs(P, we_n, pair_sh[0], w, lane);
+  wait_vm<0>();
+  int lb = 0;  // pair buffer of the current item
+  while (it_n < i_end) {
+    const int it = it_n;
+    const moe::WorkEntry we = we_n;
+    const uint8_t *const blob = blob_n;
     const int ei = it / nrt, rt = it - ei * nrt;
-    const moe::WorkEntry we = P.work[ei];
-    if (!entry_ok(P, we)) continue;  // uniform over the workgroup
-    const uint8_t *blob = entry_blob(P, we);
-    if (!blob) continue;
-    __syncthreads();  // the previous item no longer reads the token lists or the LDS data
-    if (tid < kPM) {
-      int tok = -1, row = -1;
-      if (tid < we.m && !entry_token(P, we, tid, tok, row)) tok = row = -1;
-      tok_sh[tid] = tok;
-      row_sh[tid] = row;
-    }
-    __syncthreads();
+    const int *const pairs = pair_sh[lb];
+    __syncthreads();  // the item's pair ids are published; the previous item no longer reads the LDS data
     const int m = we.m, ntt = (m + 15) >> 4;
     const int wrow0 = rt * kGRows + w * kWRows;
     const bool wact = wrow0 < rows_out;  // whole wave: d_ff, d_model are multiples of 64
@@ -432,7 +472,8 @@ __global__ void __launch_bounds__(kPThreads, 1) prefill_kernel(PrefillParams P) 
 #pragma unroll
       for (int i = 0; i < G::kCopies; ++i) {
         const int q = tid + kPThreads * i, n = q / G::kGran, pos = q - n * G::kGran;
-        const int rr = n < m ? (NMAT == 2 ? tok_sh[n] : row_sh[n]) : -1;
+        const int row = entry_row(P, we, n, pairs);
+        const int rr = NMAT == 2 && row >= 0 ? row_token(P, row) : row;
         X.src[i] = (uint32_t)(rr < 0 ? 0 : rr) * stride + (uint32_t)(pos ^ G::swz(n)) * 16u;
       }
     }
@@ -447,21 +488,35 @@ __global__ void __launch_bounds__(kPThreads, 1) prefill_kernel(PrefillParams P) 
     copy_w(R, wbase, 0, nsb, r16, lane, w);
     uint32_t Pw[4];
     h8 A[4];
+    // the next item's entry, and its pair ids copied into the other buffer,
+    // as the last superblock starts: younger than the copies in flight (so
+    // every counted wait only gets stronger) and landed by the end of the K
+    // loop; the next item's start barrier publishes them
+    auto fetch_next = [&]() {
+      it_n = fetch_item(P, it + istep, istep, i_end, nrt, we_n, blob_n);
+      if (it_n < i_end) copy_pairs(P, we_n, pair_sh[lb ^ 1], w, lane);
+    };
+    if (nsb == 1) fetch_next();
     if (ntt == kTT) {  // uniform
       k_superblock<true, true>(0, nsb, nsteps, R, g, r16, w, lane, Pw, A, X, ring, xring, wbase, wlds, sel, K, ntt, wact,
                                rl_hi, rl_lo, acc);
-      for (int S = 1; S < nsb; ++S)
+      for (int S = 1; S < nsb; ++S) {
+        if (S == nsb - 1) fetch_next();
         k_superblock<false, true>(S, nsb, nsteps, R, g, r16, w, lane, Pw, A, X, ring, xring, wbase, wlds, sel, K, ntt,
                                   wact, rl_hi, rl_lo, acc);
+      }
     } else {
       k_superblock<true, false>(0, nsb, nsteps, R, g, r16, w, lane, Pw, A, X, ring, xring, wbase, wlds, sel, K, ntt,
                                 wact, rl_hi, rl_lo, acc);
-      for (int S = 1; S < nsb; ++S)
+      for (int S = 1; S < nsb; ++S) {
+        if (S == nsb - 1) fetch_next();
         k_superblock<false, false>(S, nsb, nsteps, R, g, r16, w, lane, Pw, A, X, ring, xring, wbase, wlds, sel, K, ntt,
                                    wact, rl_hi, rl_lo, acc);
+      }
     }
-    // every copy of this item (the ones past the last step included) has
-    // landed before the next item's prologue reuses the slots
+    // every copy of this item (the ones past the last step included, and the
+    // next item's pair ids) has landed before the next item's prologue reuses
+    // the slots
     wait_vm<0>();
     // D layout: lane (r16, g) holds rows 4 g + i of each row tile for token
     // r16 of each token tile
@@ -473,8 +528,12 @@ __global__ void __launch_bounds__(kPThreads, 1) prefill_kernel(PrefillParams P) 
       // write-out roles: thread (tq, wi) stores piece wi (line L0 + wi / 8,
       // piece wi % 8) of the record for tokens tq, tq + 4, ... of each half,
       // so neighbouring threads store neighbouring bytes of one record; which
-      // of the piece's 8 halves the item owns is the same for every token
-      const int wi = tid & 127, tq = tid >> 7;
+      // of the piece's 8 halves the item owns is the same for every token.
+      // (The thread index is made opaque here so that none of this is
+      // computed ahead of the item loop and kept live through the K loop.)
+      int tid_e = tid;
+      asm volatile("" : "+v"(tid_e));
+      const int wi = tid_e & 127, tq = tid_e >> 7;
       uint32_t own = 0;
       if (wi < 8 * nl) {
         const int L = L0 + (wi >> 3), gq = wi & 3, S = L / 5, t = L - 5 * S;
@@ -487,33 +546,64 @@ __global__ void __launch_bounds__(kPThreads, 1) prefill_kernel(PrefillParams P) 
         }
       }
       const size_t dst_off = (size_t)L0 * 128 + (size_t)wi * 16;
-      // image offset and 1 / f of the lane's 8 columns
+      // Pieces the item owns only in part lie in the quad (40 columns) of a
+      // row-block boundary that is not quad-aligned -- c0, or c1 (the next
+      // block, or the padding past d_ff): 5 lines x (hi, lo) = 10 candidate
+      // pieces each.  Thread (tb, pp, jh) stores half jh of candidate piece pp
+      // for tokens tb, tb + 3, ... if the item owns that half and not the
+      // whole piece (whole pieces go out as 16-byte stores above).
+      const int pq = tid_e % 160, tb = tid_e / 160;  // tb == 3: idle
+      const int pp = pq >> 3, jh = pq & 7;
+      const int bcol = pp < 10 ? c0 : c1, tt = (pp % 10) >> 1, hl = pp & 1;
+      const int Sb = bcol / moe::kSbCols, gb = (bcol % moe::kSbCols) / 40;
+      const int Lb = 5 * Sb + tt;
+      bool mine = false;
+      if (tb < 3 && bcol % 40 != 0) {
+        uint32_t ownb = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c = Sb * moe::kSbCols + moe::pair_col(20 * gb + 4 * tt + i);
+          ownb |= (c >= c0 && c < c1 ? 1u : 0u) << (2 * i);
+          ownb |= (c + 5 >= c0 && c + 5 < c1 ? 1u : 0u) << (2 * i + 1);
+        }
+        mine = ownb != 0xffu && (ownb >> jh & 1u);
+      }
+      const int b_img = ((Lb - L0) * 8 + 4 * hl + gb) * 16 + 2 * jh;  // byte in a token's image
+      const size_t b_dst = (size_t)Lb * 128 + (4 * hl + gb) * 16 + 2 * jh;
+      // h = silu(gate) up / f of the lane's 8 columns for all token tiles, as
+      // packed (hi, lo) fp16 halves (the accumulators die here), and each
+      // column's offset in the image
+      uint32_t hp[8][kTT];
       int off[8];
-      float inv_f[8];
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) off[4 * a + i] = rec_byte(wrow0 + 16 * a + 4 * g + i, inv_f[4 * a + i]) - L0 * 128;
+        for (int i = 0; i < 4; ++i) {
+          float inv_f;
+          off[4 * a + i] = rec_byte(wrow0 + 16 * a + 4 * ((tid_e & 63) >> 4) + i, inv_f) - L0 * 128;
+#pragma unroll
+          for (int nt = 0; nt < kTT; ++nt) {
+            const float gv = acc[a][nt][i], uv = acc[a + 2][nt][i];
+            const float h = gv / (1.0f + __expf(-gv)) * uv * inv_f;
+            const _Float16 hh = (_Float16)h, hl = (_Float16)(h - (float)hh);
+            hp[4 * a + i][nt] = (uint32_t)__builtin_bit_cast(uint16_t, hh) |
+                                ((uint32_t)__builtin_bit_cast(uint16_t, hl) << 16);
+          }
+        }
       __syncthreads();  // every wave is done with the x ring and the weight slots
 #pragma unroll
       for (int half = 0; half < kTT / 4; ++half) {
         if (16 * 4 * half >= m) break;  // uniform: no token in this half
         if (wact) {
 #pragma unroll
-          for (int a = 0; a < 2; ++a)
+          for (int c8 = 0; c8 < 8; ++c8)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-#pragma unroll
-              for (int q4 = 0; q4 < 4; ++q4) {
-                const int nt = 4 * half + q4, n = 16 * nt + r16;
-                if (nt < ntt && n < m) {
-                  const float gv = acc[a][nt][i], uv = acc[a + 2][nt][i];
-                  const float h = gv / (1.0f + __expf(-gv)) * uv * inv_f[4 * a + i];
-                  const _Float16 hh = (_Float16)h, hl = (_Float16)(h - (float)hh);
-                  uint8_t *o = smem + (16 * q4 + r16) * istride + off[4 * a + i];
-                  *reinterpret_cast<_Float16 *>(o) = hh;
-                  *reinterpret_cast<_Float16 *>(o + 64) = hl;
-                }
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const int nt = 4 * half + q4, n = 16 * nt + r16;
+              if (nt < ntt && n < m) {
+                uint8_t *o = smem + (16 * q4 + r16) * istride + off[c8];
+                *reinterpret_cast<uint16_t *>(o) = (uint16_t)hp[c8][nt];
+                *reinterpret_cast<uint16_t *>(o + 64) = (uint16_t)(hp[c8][nt] >> 16);
               }
             }
         }
@@ -529,37 +619,33 @@ __global__ void __launch_bounds__(kPThreads, 1) prefill_kernel(PrefillParams P) 
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const int nloc = tq + kTq * (j0 + j);  // < kImgTokens: the image read stays in it
-              rw[j] = nloc < n_tok ? row_sh[kImgTokens * half + nloc] : -1;
+              rw[j] = nloc < n_tok ? entry_row(P, we, kImgTokens * half + nloc, pairs) : -1;
               v[j] = *reinterpret_cast<const u4 *>(smem + nloc * istride + wi * 16);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j)
               if (rw[j] >= 0) *reinterpret_cast<u4 *>(P.hrec + (size_t)rw[j] * P.hrec_b + dst_off) = v[j];
           }
-        } else if (own) {
-          for (int nloc = tq; nloc < n_tok; nloc += kTq) {
-            const int row = row_sh[kImgTokens * half + nloc];
-            if (row < 0) continue;
-            const uint8_t *src = smem + nloc * istride + wi * 16;
-            uint8_t *dst = P.hrec + (size_t)row * P.hrec_b + dst_off;
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-              if (own >> j & 1u)
-                *reinterpret_cast<uint16_t *>(dst + 2 * j) = *reinterpret_cast<const uint16_t *>(src + 2 * j);
+        }
+        if (mine) {
+          for (int nloc = tb; nloc < n_tok; nloc += 3) {
+            const int row = entry_row(P, we, kImgTokens * half + nloc, pairs);
+            if (row >= 0)
+              *reinterpret_cast<uint16_t *>(P.hrec + (size_t)row * P.hrec_b + b_dst) =
+                  *reinterpret_cast<const uint16_t *>(smem + nloc * istride + b_img);
           }
         }
         __syncthreads();  // the image is read out before the next half or item reuses it
       }
-    } else {
-      if (!wact) continue;
+    } else if (wact) {
 #pragma unroll
       for (int nt = 0; nt < kTT; ++nt) {
         const int n = 16 * nt + r16;
         if (nt < ntt && n < m) {
-          const int row = row_sh[n];
+          const int row = entry_row(P, we, n, pairs);
           if (row >= 0) {
             float *y = we.expert >= 0 ? P.y_pairs + (size_t)row * P.d_model
-                                      : P.y_shared + (size_t)tok_sh[n] * P.d_model;
+                                      : P.y_shared + (size_t)(row - P.T * P.k) * P.d_model;
 #pragma unroll
             for (int a = 0; a < 4; ++a)
               *reinterpret_cast<float4 *>(y + wrow0 + 16 * a + 4 * g) =
@@ -568,6 +654,7 @@ __global__ void __launch_bounds__(kPThreads, 1) prefill_kernel(PrefillParams P) 
         }
       }
     }
+    lb ^= 1;
   }
 }
 
