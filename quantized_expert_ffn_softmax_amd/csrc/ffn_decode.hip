@@ -406,8 +406,16 @@ __device__ inline void compute_all(std::integer_sequence<int, Ps...>, uint4 (&W)
 // [h H, min((h + 1) H, NSB)) with H = ceil(NSB / 2) -- and the halves' sums
 // added through LDS before the epilogue.  Twice the waves in flight and half
 // the chain per wave, for batches whose units leave CUs idle.
+// workgroups per CU the kernel is built for: gate/up 3; down 4 up to 6
+// superblocks (the model's d_ff = 768 is 5), then what its registers allow
+// on entries of 8 tokens (3 up to 9 superblocks, 2 beyond)
+template <int NSB, int NMAT>
+constexpr int decode_min_blocks() {
+  return NMAT == 2 ? 3 : (NSB <= 6 ? 4 : (NSB <= 9 ? 3 : 2));
+}
+
 template <int NSB, int NMAT, int KS, int COLS>
-__global__ void __launch_bounds__(64 * kWaves, NMAT == 2 ? 3 : 4) ffn_decode_kernel(DecodeParams P) {
+__global__ void __launch_bounds__(64 * kWaves, (decode_min_blocks<NSB, NMAT>())) ffn_decode_kernel(DecodeParams P) {
   static_assert(KS == 1 || (NMAT == 2 && ((NSB + 1) / 2) % 2 == 1), "K split: gate/up, an odd half length");
   static_assert(COLS == 4 || COLS == 8, "entries of 4 or 8 tokens");
   constexpr int NS = KS == 2 ? (NSB + 1) / 2 : NSB;  // superblocks of a wave's range
