@@ -67,7 +67,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--prefill-reps", type=int, default=5)
+    ap.add_argument("--prefill-reps", type=int, default=10)
     ap.add_argument("--cpu-sample-layers", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
@@ -280,6 +280,8 @@ def bench_stack(ctx, routers, biases, seed, d, f, L, T, W, K, use_graph, peaks):
     # fixed-shape decode step), replayed on fresh inputs copied in beforehand:
     # first as the seven launches per layer of the separate calls, then as the
     # six of moe_decode_layer (the headline)
+    spread = {}
+
     def graph_time(fn):
         xin = torch.empty((T, d), dtype=torch.float32, device="cuda")
         side = torch.cuda.Stream()
@@ -305,13 +307,17 @@ def bench_stack(ctx, routers, biases, seed, d, f, L, T, W, K, use_graph, peaks):
             gev[s_][1].record()
         torch.cuda.synchronize()
         del graph
-        return float(np.mean([a.elapsed_time(b) for a, b in gev]))
+        ts = [a.elapsed_time(b) for a, b in gev]
+        spread["graph_ms"] = {"median": round(float(np.median(ts)), 4), "min": round(float(np.min(ts)), 4),
+                              "max": round(float(np.max(ts)), 4)}
+        return float(np.mean(ts))
 
     graph_ms = sep_graph_ms = None
     if use_graph:
         sep_graph_ms = graph_time(step)
         log(f"[bench] decode stack (graph, separate calls, 7 launches/layer): {sep_graph_ms:.3f} ms/step, "
             f"{T / (sep_graph_ms * 1e-3):.0f} tok/s")
+        sep_spread = dict(spread)
         graph_ms = graph_time(step_fused)
         log(f"[bench] decode stack (graph, moe_decode_layer, 6 launches/layer): {graph_ms:.3f} ms/step, "
             f"{T / (graph_ms * 1e-3):.0f} tok/s")
@@ -332,8 +338,11 @@ def bench_stack(ctx, routers, biases, seed, d, f, L, T, W, K, use_graph, peaks):
            "eager_ms_per_step": round(eager_ms, 4),
            "step_mode": "hip_graph, moe_decode_layer (6 launches per layer)" if graph_ms is not None
            else "eager, separate calls (7 launches per layer)"}
+    if graph_ms is not None:
+        res["ms_per_step_spread"] = spread["graph_ms"]
     if sep_graph_ms is not None:
         res["separate_calls_graph_ms_per_step"] = round(sep_graph_ms, 4)
+        res["separate_calls_ms_per_step_spread"] = sep_spread["graph_ms"]
         res["separate_calls_tok_per_s"] = round(T / (sep_graph_ms * 1e-3), 1)
     return res
 
@@ -350,8 +359,9 @@ def bench_prefill(ctx, router, bias, seed, d, f, k, T, reps, peaks):
     c = ctx.ctx
     xp = torch.from_numpy(moe_synth.gen_x(seed, 100000, T, d)).cuda()
     pbuf = ctx.buffers(T)
-    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps + 1)]
-    for r in range(reps + 1):
+    warm = 3
+    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps + warm)]
+    for r in range(reps + warm):
         e = pev[r]
         e[0].record()
         B.moe_route(c, 0, xp, T, router, bias, None, pbuf["idx"], pbuf["w"])
@@ -362,8 +372,9 @@ def bench_prefill(ctx, router, bias, seed, d, f, k, T, reps, peaks):
         B.moe_combine(c, pbuf["y_pairs"], pbuf["w"], pbuf["y_shared"], T, pbuf["out"])
         e[3].record()
     torch.cuda.synchronize()
-    layer_ms = float(np.median([pev[r][0].elapsed_time(pev[r][3]) for r in range(1, reps + 1)]))
-    ffn_p_ms = float(np.median([pev[r][1].elapsed_time(pev[r][2]) for r in range(1, reps + 1)]))
+    layer_t = [pev[r][0].elapsed_time(pev[r][3]) for r in range(warm, reps + warm)]
+    ffn_t = [pev[r][1].elapsed_time(pev[r][2]) for r in range(warm, reps + warm)]
+    layer_ms, ffn_p_ms = float(np.median(layer_t)), float(np.median(ffn_t))
     flops = 6.0 * d * f * (T * k + T)
     tflops = flops / (ffn_p_ms * 1e-3) / 1e12
     roof = {"bound": "mfma", "kernel": "moe_expert_ffn (prefill path)",
@@ -376,7 +387,10 @@ def bench_prefill(ctx, router, bias, seed, d, f, k, T, reps, peaks):
     log(f"[bench] prefill chunk: layer {layer_ms:.2f} ms ({T / (layer_ms * 1e-3):.0f} tok/s), "
         f"FFN {ffn_p_ms:.2f} ms = {tflops:.1f} TFLOP/s")
     return {"workload": "prefill_chunk", "tokens": T, "tok_per_s": round(T / (layer_ms * 1e-3), 1),
-            "layer_ms": round(layer_ms, 4), "ffn_ms": round(ffn_p_ms, 4), "roofline": roof}
+            "layer_ms": round(layer_ms, 4), "ffn_ms": round(ffn_p_ms, 4), "warmup": warm, "reps": reps,
+            "layer_ms_min_max": [round(min(layer_t), 4), round(max(layer_t), 4)],
+            "ffn_ms_min_max": [round(min(ffn_t), 4), round(max(ffn_t), 4)],
+            "timing": "HIP events; medians over the timed reps", "roofline": roof}
 
 
 def bench_decode_layer(ctx, router, seed, d, f, E, k, reps=200):
@@ -413,14 +427,17 @@ def bench_decode_layer(ctx, router, seed, d, f, E, k, reps=200):
         B.moe_combine(c, buf["y_pairs"], buf["w"], buf["y_shared"], T, buf["out"])
     torch.cuda.synchronize()
     st1 = B.moe_get_stats(c)
-    layer_us = float(np.mean([ev[r][0].elapsed_time(ev[r][2]) for r in range(10, reps + 10)])) * 1e3
-    ffn_us = float(np.mean([ev[r][1].elapsed_time(ev[r][2]) for r in range(10, reps + 10)])) * 1e3
+    layer_t = [ev[r][0].elapsed_time(ev[r][2]) * 1e3 for r in range(10, reps + 10)]
+    ffn_t = [ev[r][1].elapsed_time(ev[r][2]) * 1e3 for r in range(10, reps + 10)]
+    layer_us, ffn_us = float(np.mean(layer_t)), float(np.mean(ffn_t))
     uniq = (st1["lookups"] - st0["lookups"]) / reps
     gbs = (uniq + 1) * algo_blob_bytes(d, f) / (ffn_us * 1e-6) / 1e9
     log(f"[bench] decode layer T={T}: route+resolve+ffn {layer_us:.1f} us, ffn {ffn_us:.1f} us for "
         f"{uniq:.1f} + 1 experts -> {gbs:.0f} GB/s")
     return {"workload": "decode_layer", "tokens": T, "reps": reps, "route_resolve_ffn_us": round(layer_us, 2),
-            "ffn_us": round(ffn_us, 2), "distinct_experts": round(uniq, 2), "ffn_hbm_gbs": round(gbs, 1),
+            "ffn_us": round(ffn_us, 2),
+            "ffn_us_median_min_max": [round(float(np.median(ffn_t)), 2), round(min(ffn_t), 2), round(max(ffn_t), 2)],
+            "distinct_experts": round(uniq, 2), "ffn_hbm_gbs": round(gbs, 1),
             "ffn_hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
@@ -844,7 +861,25 @@ def cpu_baseline(seed, d, f, E, k, T, alpha, n_layers, step, prefill_T, prefill_
                                 f"({t_route:.1f} s), shared expert on every token ({t_shared:.1f} s), expert FFNs "
                                 f"of {pick.size} of the {used.size} experts with tokens (seeded pick, {rows} pairs, "
                                 f"{t_ffn:.1f} s) scaled by {used.size}/{pick.size}; estimated {est:.1f} s per chunk"}
-    log(f"[bench] cpu oracle: decode {out['value']} tok/s, prefill {out['prefill']['value']} tok/s on {cores} cores")
+    # the two small configurations, each timed whole: the tiny layer (T = 8,
+    # 16 experts of 256 x 128) and one real layer at T = 5 (no router bias)
+    for name in ("tiny", "decode_layer"):
+        wl = moe_synth.WORKLOADS[name]
+        dd, ff, EE, kk, TT = wl["d_model"], wl["d_ff"], wl["n_experts"], wl["top_k"], wl["n_tokens"]
+        xw = moe_synth.gen_x(seed, 200000, TT, dd)
+        wrw = moe_synth.gen_router(seed, 0, EE, dd)
+        bw = moe_synth.gen_bias(seed, 0, EE, wl["alpha"])
+        _, idw, _ = oracle.route(xw, wrw, bw, kk)
+        blobs_w = {int(e): moe_synth.gen_blob(seed, 0, int(e), dd, ff) for e in np.unique(idw)}
+        shared_w = moe_synth.gen_blob(seed, 0, EE, dd, ff)
+        t = time.time()
+        oracle.moe_layer(xw, wrw, bw, kk, lambda e: blobs_w[e], shared_w, dd, ff, precision="exact")
+        tw = time.time() - t
+        out[name] = {"value": round(TT / tw, 3), "unit": "tok/s", "cores": cores, "kind": "oracle",
+                     "sample": f"the whole layer: {TT} tokens, {EE} experts of {dd} x {ff}, top-{kk} "
+                               f"(route, {len(blobs_w)} + 1 expert FFNs, combine), {tw:.2f} s"}
+    log(f"[bench] cpu oracle: decode {out['value']} tok/s, prefill {out['prefill']['value']} tok/s, tiny layer "
+        f"{out['tiny']['value']} tok/s, one real layer at T=5 {out['decode_layer']['value']} tok/s on {cores} cores")
     return out
 
 
