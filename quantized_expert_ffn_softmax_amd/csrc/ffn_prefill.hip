@@ -35,6 +35,7 @@
 #include "dequant.h"
 #include "lds_copy.h"
 #include "moe_internal.h"
+#include "prefill_plan.h"
 
 namespace {
 
@@ -66,19 +67,9 @@ struct RecGeom {
 };
 constexpr int kHL = 2;  // halves per value: hi and lo
 using Geo = RecGeom<kHL>;
-static_assert(Geo::kCopies == 2 && Geo::kGran == 8, "copy roles and swizzle width");
-
-// byte offset of column c's hi half inside one row of a record (its lo half
-// sits 64 bytes further); `inv_f` gets the 1 / f the value is stored with
-__host__ __device__ inline int rec_byte(int c, float &inv_f) {
-  const int S = c / moe::kSbCols, lc = c - S * moe::kSbCols;
-  const int w = lc / 10, j = lc - 10 * w;
-  const int p = 5 * w + j % 5, e = j / 5;  // pair of the superblock, half
-  const int g = p / 20, t = (p % 20) / 4, i = p % 4;
-  const int jj = (j % 5) % 3;
-  inv_f = jj == 0 ? 1.0f : (jj == 1 ? 0.125f : 0.015625f);
-  return (S * 5 + t) * Geo::kRowB + g * 16 + (2 * i + e) * 2;
-}
+static_assert(Geo::kCopies == moe::pf::kXCopies && Geo::kGran == 8 && Geo::kRowB == moe::pf::kRecRowB,
+              "copy roles, swizzle width and record row as the plan has them");
+using moe::pf::rec_byte;
 
 struct PrefillParams {
   const moe::WorkEntry *work;
@@ -202,36 +193,16 @@ struct WRows {
 // Weights stay in their LDS slot for the superblock: each step reads the one
 // or two words of the lane's quad it needs, and the scale pairs are read once
 // per superblock; fragments are dequantised a step ahead of their MFMAs.
-constexpr int kXD = 3;                      // x tiles copied this many steps ahead
-constexpr int kXRing = 4;                   // slots of the x ring (> kXD)
+using moe::pf::kXD;      // x tiles copied this many steps ahead
+using moe::pf::kXRing;   // slots of the x ring (> kXD)
+using moe::pf::kWCopies; // copies per wave per superblock: 4 quads + 4 scale sets
+using moe::pf::vm_after; // the wait count of each step (prefill_plan.h)
 constexpr int kQuadB = 1024;                // one tile's quads of one wave: 64 lanes x 16 B
 constexpr int kScB = 256;                   // one tile's scale dwords: 16 rows x 3 (64 lane slots)
 constexpr int kTileWB = kQuadB + kScB;      // one tile's weights of one superblock
 constexpr int kWSlotB = kPWaves * 4 * kTileWB;  // one superblock's weights of the workgroup
-constexpr int kWCopies = 8;                 // copies per wave per superblock: 4 quads + 4 scale sets
 static_assert(kXRing > kXD && (kXRing & (kXRing - 1)) == 0, "x ring");
-
-// loads issued after a step's tile copies by the time that step waits for
-// them: the tiles of the kXD - 1 later steps (2 copies each) and kWCopies
-// weight copies per superblock start among the kXD steps since; in superblock
-// 0 the prologue's order (tiles 0..kXD-1, then superblock 0's weights)
-// applies
-constexpr int vm_after(int t, bool first) {
-  if (first) {
-    // step 0 waits for superblock 0's weights (the last prologue loads)
-    if (t == 0) return 0;
-    int n = 0;
-    // prologue: tiles t+1 .. kXD-1, superblock 0's weights
-    if (t < kXD) n += 2 * (kXD - 1 - t) + kWCopies;
-    // steps 0 .. t-1 of superblock 0 (for t <= kXD), or t-kXD .. t-1
-    const int u0 = t < kXD ? 0 : t - kXD;
-    for (int u = u0; u < t; ++u) n += 2 + (u == 0 ? kWCopies : 0);
-    return n - (t < kXD ? 0 : 2);  // the issuing step's own copies come first
-  }
-  int n = 2 * (kXD - 1);
-  for (int u = t - kXD; u < t; ++u) n += ((u % 5 + 5) % 5 == 0) ? kWCopies : 0;
-  return n;
-}
+static_assert(kWCopies == 2 * 4, "a quad copy and a scale copy per tile");
 
 template <int N>
 __device__ __attribute__((always_inline)) inline void wait_vm() {
@@ -523,7 +494,7 @@ __global__ void __launch_bounds__(kPThreads, 1) prefill_kernel(PrefillParams P) 
     if constexpr (NMAT == 2) {
       // the item owns h columns [c0, c1); they lie in record lines L0 .. L0 + nl - 1
       const int c0 = rt * kGRows, c1 = min(c0 + kGRows, P.d_ff);
-      const int L0 = 5 * (c0 / moe::kSbCols), nl = 5 * ((c1 - 1) / moe::kSbCols) + 5 - L0;
+      const int L0 = moe::pf::item_L0(c0), nl = moe::pf::item_nl(c0, c1);
       const int istride = nl * 128 + 16;
       // write-out roles: thread (tq, wi) stores piece wi (line L0 + wi / 8,
       // piece wi % 8) of the record for tokens tq, tq + 4, ... of each half,
@@ -534,42 +505,16 @@ __global__ void __launch_bounds__(kPThreads, 1) prefill_kernel(PrefillParams P) 
       int tid_e = tid;
       asm volatile("" : "+v"(tid_e));
       const int wi = tid_e & 127, tq = tid_e >> 7;
-      uint32_t own = 0;
-      if (wi < 8 * nl) {
-        const int L = L0 + (wi >> 3), gq = wi & 3, S = L / 5, t = L - 5 * S;
-        // halves 2 i + e of the piece: column 160 S + pair_col(20 gq + 4 t + i) + 5 e
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int c = S * moe::kSbCols + moe::pair_col(20 * gq + 4 * t + i);
-          own |= (c >= c0 && c < c1 ? 1u : 0u) << (2 * i);
-          own |= (c + 5 >= c0 && c + 5 < c1 ? 1u : 0u) << (2 * i + 1);
-        }
-      }
+      const uint32_t own = moe::pf::full_piece_own(wi, c0, c1);
       const size_t dst_off = (size_t)L0 * 128 + (size_t)wi * 16;
-      // Pieces the item owns only in part lie in the quad (40 columns) of a
-      // row-block boundary that is not quad-aligned -- c0, or c1 (the next
-      // block, or the padding past d_ff): 5 lines x (hi, lo) = 10 candidate
-      // pieces each.  Thread (tb, pp, jh) stores half jh of candidate piece pp
-      // for tokens tb, tb + 3, ... if the item owns that half and not the
-      // whole piece (whole pieces go out as 16-byte stores above).
+      // Pieces the item owns only in part (moe::pf::boundary_role): thread
+      // (tb, pq) stores one half of one of them for tokens tb, tb + 3, ...
+      // (whole pieces go out as 16-byte stores above)
       const int pq = tid_e % 160, tb = tid_e / 160;  // tb == 3: idle
-      const int pp = pq >> 3, jh = pq & 7;
-      const int bcol = pp < 10 ? c0 : c1, tt = (pp % 10) >> 1, hl = pp & 1;
-      const int Sb = bcol / moe::kSbCols, gb = (bcol % moe::kSbCols) / 40;
-      const int Lb = 5 * Sb + tt;
-      bool mine = false;
-      if (tb < 3 && bcol % 40 != 0) {
-        uint32_t ownb = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int c = Sb * moe::kSbCols + moe::pair_col(20 * gb + 4 * tt + i);
-          ownb |= (c >= c0 && c < c1 ? 1u : 0u) << (2 * i);
-          ownb |= (c + 5 >= c0 && c + 5 < c1 ? 1u : 0u) << (2 * i + 1);
-        }
-        mine = ownb != 0xffu && (ownb >> jh & 1u);
-      }
-      const int b_img = ((Lb - L0) * 8 + 4 * hl + gb) * 16 + 2 * jh;  // byte in a token's image
-      const size_t b_dst = (size_t)Lb * 128 + (4 * hl + gb) * 16 + 2 * jh;
+      const moe::pf::BoundaryRole br = moe::pf::boundary_role(pq, c0, c1);
+      const bool mine = tb < 3 && br.mine;
+      const int b_img = ((br.line - L0) * 8 + br.piece) * 16 + 2 * br.half;  // byte in a token's image
+      const size_t b_dst = (size_t)br.line * 128 + br.piece * 16 + 2 * br.half;
       // h = silu(gate) up / f of the lane's 8 columns for all token tiles, as
       // packed (hi, lo) fp16 halves (the accumulators die here), and each
       // column's offset in the image
