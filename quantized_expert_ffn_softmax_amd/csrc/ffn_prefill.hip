@@ -1,8 +1,8 @@
 // Prefill path of the expert FFN: many tokens per expert, a real dense
 // contraction, so it runs as a grouped GEMM on MFMA.
 //
-// The pages' engine runs prefill in chunks of 12,288 tokens ("一张 RTX 4090
-// 跑千亿模型，Strata 实测 155 tok/s", the PREFILL=12288 finding); every token
+// The pages' engine runs prefill in chunks of 12,288 tokens on one card ("一张
+// RTX 4090 跑千亿模型，Strata 实测 155 tok/s", section 加个草稿层); every token
 // of a chunk is routed to 10 of 512 experts, so one chunk is 122,880
 // (token, expert) pairs grouped per expert, plus the shared expert's 12,288.
 //
@@ -20,15 +20,17 @@
 // wave owns 4 16-row tiles (gate/up: 2 of gate and the same 2 of up) against
 // all 128 tokens: 4 x 8 16x16 output tiles, 128 fp32 accumulators per lane.
 //   A (16 rows x 32 K)  = weights: each wave's word quads and scale words are
-//                         copied to LDS a superblock ahead, read into
-//                         registers once per superblock and dequantised
-//                         there at every step;
+//                         copied to LDS a superblock ahead; each step reads
+//                         the one or two words it needs (the scale pairs
+//                         once per superblock) and dequantises the next
+//                         step's fragments while its own MFMAs run;
 //   B (32 K x 16 tokens) = activations (hi, then lo) from a 4-slot LDS ring
 //                         of step tiles that all 8 waves share, filled 3
 //                         steps ahead, one barrier per 32-K step.
 // Every global load of the K loop is a direct global-to-LDS copy whose
-// completion the kernel waits for itself.  The gate/up epilogue stages h in
-// LDS in record order and stores whole 16-byte pieces of the h record.
+// completion the kernel waits for itself (the counts: prefill_plan.h).  The
+// gate/up epilogue stages h in LDS in record order and stores whole 16-byte
+// pieces of the h record.
 // v_mfma_f32_16x16x32_f16 only.
 #include <algorithm>
 
@@ -249,7 +251,10 @@ __device__ __attribute__((always_inline)) inline void copy_w(const WRows &R, uin
 
 // superblock S's scale pairs from its LDS slot, one per tile: b0 = min(5 S +
 // g, nblk - 1), b1 = min(b0 + 1, nblk - 1) from the row's three dwords (block
-// b is half (b - 2 d0) of dword (b - 2 d0) / 2)
+// b is half (b - 2 d0) of dword (b - 2 d0) / 2).  Step 4 of the last
+// superblock reads for S = nsb, which has no blocks: the clamp can put the
+// dword index up to 3 below the row's first, still inside the slot (its quad
+// region), and nothing uses those values.
 __device__ __attribute__((always_inline)) inline void read_p(const uint8_t *wlds, int S, int g, int r16, int nblk,
                                                              int w, uint32_t (&P)[4]) {
   const uint8_t *slot = wlds + (S & 1) * kWSlotB + w * 4 * kTileWB;
