@@ -509,9 +509,15 @@ def bench_lru(seed, d, f, E, k, L, routers, biases, shared_pool, warmup, steps):
     log(f"[bench] lru: miss fill through moe_cache_resolve_async: " +
         ", ".join(f"{r['misses_per_call']} blob(s) in {r['call_us']} us = {r['gbs']} GB/s" for r in fill_link))
 
-    def step(x0, zero_copy, bl=biases):
+    def step(x0, zero_copy, bl=biases, layer_call=False):
         x = x0
         for l in range(L):
+            if layer_call:  # moe_decode_layer: the FFN kernels stream the misses and fill their slots
+                xn = xa if (l % 2 == 0) else xb
+                B.moe_decode_layer(c, l, x, T, routers[l], bl[l], None, buf["idx"], buf["w"], buf["y_pairs"],
+                                   buf["y_shared"], buf["out"], xn)
+                x = xn
+                continue
             B.moe_route(c, l, x, T, routers[l], bl[l], None, buf["idx"], buf["w"])
             if zero_copy:
                 B.moe_cache_resolve_async(c, l, buf["idx"], T, buf["slot"])
@@ -533,13 +539,13 @@ def bench_lru(seed, d, f, E, k, L, routers, biases, shared_pool, warmup, steps):
         the 48-layer step captured once in a HIP graph and replayed."""
         B.moe_cache_reset(c)
         torch.cuda.synchronize()
-        if mode == "zero_copy_graph":
+        if mode in ("zero_copy_graph", "layer_graph"):
             x_static = torch.empty((T, d), dtype=torch.float32, device="cuda")
             graph = torch.cuda.CUDAGraph()
             cs = torch.cuda.Stream()
             cs.wait_stream(torch.cuda.current_stream())
             with torch.cuda.graph(graph, stream=cs):
-                step(x_static, True, bl)
+                step(x_static, True, bl, layer_call=(mode == "layer_graph"))
             torch.cuda.synchronize()
 
             def one(x0):
@@ -561,22 +567,28 @@ def bench_lru(seed, d, f, E, k, L, routers, biases, shared_pool, warmup, steps):
         st2 = B.moe_get_stats(c)
         return wall, st0, st1, st2
 
-    runs = {m: run(m) for m in ("copy", "zero_copy_graph")}
-    wall, st0, st1, st2 = runs["zero_copy_graph"]
-    same = all(runs["copy"][i][key] == runs["zero_copy_graph"][i][key] for i in (1, 2, 3)
-               for key in ("lookups", "hits", "misses"))
+    runs = {m: run(m) for m in ("copy", "zero_copy_graph", "layer_graph")}
+    wall, st0, st1, st2 = runs["layer_graph"]
+    same = all(runs[m][i][key] == runs["layer_graph"][i][key] for m in ("copy", "zero_copy_graph")
+               for i in (1, 2, 3) for key in ("lookups", "hits", "misses"))
     cold = (st1["hits"] - st0["hits"]) / max(1, st1["lookups"] - st0["lookups"])
     lookups, hits = st2["lookups"] - st1["lookups"], st2["hits"] - st1["hits"]
     h2d = st2["bytes_h2d"] - st1["bytes_h2d"]
     hit_bytes = (lookups + L * steps) * algo_blob_bytes(d, f)
-    cw = runs["copy"][0]
+    cw, fw = runs["copy"][0], runs["zero_copy_graph"][0]
     out = {"workload": "decode_stack_lru", "tokens_per_step": T, "layers": L, "slots": S, "steps": steps,
-           "warmup": warmup, "miss_path": "zero-copy fill kernel, 48-layer step in a HIP graph",
+           "warmup": warmup,
+           "miss_path": "moe_decode_layer: the FFN kernels stream missed experts from pinned host memory and fill "
+                        "their slots (no fill kernel), 48-layer step in a HIP graph",
            "tok_per_s": round(T * steps / wall, 2), "ms_per_step": round(wall / steps * 1e3, 3),
            "hit_rate": round(hits / max(1, lookups), 4), "cold_start_hit_rate": round(cold, 4),
            "misses_per_token": round((lookups - hits) / (T * steps), 2),
            "h2d_gbs": round(h2d / wall / 1e9, 2), "h2d_peak_gbs": round(h2d_peak, 2),
            "hit_path_hbm_gbs": round(hit_bytes / wall / 1e9, 1),
+           "fill_kernel_path": {"miss_path": "separate calls, moe_cache_resolve_async (a fill kernel copies each "
+                                             "missed blob before the FFN), HIP graph",
+                                "tok_per_s": round(T * steps / fw, 2), "ms_per_step": round(fw / steps * 1e3, 3),
+                                "h2d_gbs": round(h2d / fw / 1e9, 2)},
            "copy_path": {"miss_path": "host reads the miss list, hipMemcpyAsync per missed blob",
                          "tok_per_s": round(T * steps / cw, 2), "ms_per_step": round(cw / steps * 1e3, 3),
                          "h2d_gbs": round(h2d / cw / 1e9, 2)},
@@ -589,7 +601,7 @@ def bench_lru(seed, d, f, E, k, L, routers, biases, shared_pool, warmup, steps):
     for alpha in (0.5, 1.0):
         bl = [torch.from_numpy(moe_synth.gen_bias(seed, l, E, alpha)).cuda() for l in range(L)]
         n_sw = max(1, steps // 2)
-        w_, _s0, s1_, s2_ = run("zero_copy_graph", bl, n_sw)
+        w_, _s0, s1_, s2_ = run("layer_graph", bl, n_sw)
         lk, ht = s2_["lookups"] - s1_["lookups"], s2_["hits"] - s1_["hits"]
         sweep.append({"zipf_alpha": alpha, "hit_rate": round(ht / max(1, lk), 4),
                       "misses_per_token": round((lk - ht) / (T * n_sw), 2), "tok_per_s": round(T * n_sw / w_, 2),
@@ -600,10 +612,11 @@ def bench_lru(seed, d, f, E, k, L, routers, biases, shared_pool, warmup, steps):
     out["hit_rate_sweep"] = sweep
     log("[bench] lru: tok/s against hit rate: " +
         ", ".join(f"alpha {r['zipf_alpha']}: hit {r['hit_rate']:.4f} -> {r['tok_per_s']} tok/s" for r in sweep))
-    log(f"[bench] lru: zero-copy+graph {out['tok_per_s']} tok/s ({out['ms_per_step']} ms/step), copy path "
+    log(f"[bench] lru: moe_decode_layer+graph {out['tok_per_s']} tok/s ({out['ms_per_step']} ms/step), fill kernel "
+        f"{out['fill_kernel_path']['tok_per_s']} tok/s, copy path "
         f"{out['copy_path']['tok_per_s']} tok/s; hit rate {out['hit_rate']:.4f} (cold start {cold:.4f}), "
         f"{out['misses_per_token']} misses/token, H2D {out['h2d_gbs']} GB/s (peak {h2d_peak:.1f}); "
-        f"identical cache traffic in both modes: {same}")
+        f"identical cache traffic in all three modes: {same}")
     ctx.close()
     del host, slot_pool
     return out

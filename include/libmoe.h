@@ -183,7 +183,7 @@ moe_status moe_expert_ffn(moe_ctx *ctx, int32_t layer, const float *x, int32_t T
 moe_status moe_combine(moe_ctx *ctx, const float *y_pairs, const float *w,
                        const float *y_shared, int32_t T, float *out, void *stream);
 
-/* One whole decode layer on a resident cache in six launches instead of the
+/* One whole decode layer; on a resident cache in six launches instead of the
  * seven of the separate calls (the pages' engine has a fused-kernel mode,
  * "融合核": "从一张到四张 RTX 4090 ...", section 调参：前后 40 多次重启):
  * the router's two launches; one launch for the resident lookup count, the
@@ -196,9 +196,28 @@ moe_status moe_combine(moe_ctx *ctx, const float *y_pairs, const float *w,
  *   x_next ? moe_combine_norm(ctx, y_pairs, w, y_shared, T, out, x_next)
  *          : moe_combine(ctx, y_pairs, w, y_shared, T, out).
  * Arguments as there; logits and x_next may be NULL; x_next must differ from
- * x and out.  Needs a resident cache (n_slots == n_layers * n_experts),
- * T * top_k <= 1,024 and d_model, d_ff <= 2048; MOE_ERR_INVALID otherwise,
- * nothing enqueued.  Asynchronous; uses the context's workspace. */
+ * x and out.  Needs T * top_k <= 1,024 and d_model, d_ff <= 2048.
+ *
+ * On a capped cache (its host_store mapped into the device address space,
+ * i.e. from hipHostMalloc) the layer resolves through the LRU table in the
+ * context's own slot array.  Results, table, stamps and counters are those of
+ * the separate calls with moe_cache_resolve_async in place of
+ * moe_cache_resolve; the misses' slots end up holding their blobs' bytes up
+ * to the end of the down-projection scales (the padding of the 256-byte
+ * stride is not written).  The pages put the cost of a miss in the host link
+ * ("一张 RTX 4090 跑千亿模型 ...", section 如何做到：三层存储); for T <= 4
+ * (every expert then one unit row of each FFN kernel) no fill kernel runs:
+ * the FFN units of a missed expert stream its weights from the host store
+ * themselves and write every byte they read into its slot, so the transfer
+ * overlaps the hit experts' work and one launch fewer is made (seven).  For
+ * larger T the fill kernel runs first, as in moe_cache_resolve_async.  A call
+ * that cannot pin its working set changes nothing in the table, counts one
+ * failed call and leaves its pairs' y_pairs rows unwritten (out is then not
+ * meaningful).
+ *
+ * MOE_ERR_INVALID otherwise (a capped cache whose host_store is not mapped,
+ * shapes out of range), nothing enqueued.  Asynchronous; uses the context's
+ * workspace. */
 moe_status moe_decode_layer(moe_ctx *ctx, int32_t layer, const float *x, int32_t T,
                             const float *w_router, const float *bias, float *logits,
                             int32_t *idx, float *w, float *y_pairs, float *y_shared,

@@ -21,6 +21,10 @@
 // pinned host store (mapped into the device address space; the reads cross
 // the host link) into its slot.  The pages name the link as the bottleneck
 // of a miss; the zero-copy fill removes the per-layer host synchronisation.
+// A third way (small decode batches, moe_decode_layer on a capped cache):
+// no fill kernel at all -- the decode FFN kernels stream a missed expert's
+// weights from the mapped host store themselves and write each byte they
+// read into its slot, so the link transfer overlaps the hit experts' work.
 #include "device_util.h"
 #include "moe_internal.h"
 
@@ -56,13 +60,17 @@ __device__ inline void add_stat(int64_t *p, int64_t v) {
 }
 
 // stats: [0] unique identities, [1] hits, [2] misses, [3] calls, [4] calls that
-// could not pin their working set, [5] the clock
+// could not pin their working set, [5] the clock.
+// With fill_of_pair (capped cache, misses filled by the decode FFN kernels
+// themselves) every pair p < n also gets the identity to stream from the host
+// store when its expert missed in this call, else -1.
 __global__ void __launch_bounds__(kThreads) resolve_kernel(const int32_t *__restrict__ idx, int n, int layer, int E,
                                                            int S, int resident, int clear_on_fail,
                                                            int32_t *__restrict__ slot_of, int32_t *__restrict__ id_of,
                                                            uint32_t *__restrict__ stamp,
                                                            int32_t *__restrict__ slot_of_pair,
-                                                           int32_t *__restrict__ dmiss, int64_t *__restrict__ stats) {
+                                                           int32_t *__restrict__ dmiss, int64_t *__restrict__ stats,
+                                                           int32_t *__restrict__ fill_of_pair) {
   __shared__ int mark[1024];
   __shared__ int miss_e[1024];
   __shared__ int victim[1024];
@@ -107,7 +115,10 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(const int32_t *__rest
   if (is_miss) miss_e[mpos] = tid;
   if (nuniq > S) {  // cannot pin this call's working set: change nothing
     if (clear_on_fail)  // no host reads the error: the call's pairs get no slot (no output)
-      for (int p = tid; p < n; p += kThreads) slot_of_pair[p] = -1;
+      for (int p = tid; p < n; p += kThreads) {
+        slot_of_pair[p] = -1;
+        if (fill_of_pair) fill_of_pair[p] = -1;
+      }
     if (tid == 0) {
       dmiss[0] = nuniq;
       dmiss[1] = 0;
@@ -138,7 +149,10 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(const int32_t *__rest
     best = block_min_u64(best, shred);
     if (best == kNone) {  // cannot happen on a consistent table; never write out of range
       if (clear_on_fail)
-        for (int p = tid; p < n; p += kThreads) slot_of_pair[p] = -1;
+        for (int p = tid; p < n; p += kThreads) {
+          slot_of_pair[p] = -1;
+          if (fill_of_pair) fill_of_pair[p] = -1;
+        }
       if (tid == 0) {
         dmiss[0] = nuniq;
         dmiss[1] = 0;
@@ -163,12 +177,15 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(const int32_t *__rest
     stamp[v] = clock;
     dmiss[3 + 2 * tid] = id;
     dmiss[4 + 2 * tid] = v;
+    mark[miss_e[tid]] = 2;  // this call's misses (mark is not read as a set any more)
   }
   __threadfence_block();
   __syncthreads();
   for (int p = tid; p < n; p += kThreads) {
     const int e = idx[p];
-    slot_of_pair[p] = (e >= 0 && e < E) ? slot_of[base + e] : -1;
+    const bool ok = e >= 0 && e < E;
+    slot_of_pair[p] = ok ? slot_of[base + e] : -1;
+    if (fill_of_pair) fill_of_pair[p] = ok && mark[e] == 2 ? base + e : -1;
   }
   if (tid == 0) {
     dmiss[0] = nuniq;
@@ -218,13 +235,15 @@ __global__ void __launch_bounds__(kFillThreads) fill_kernel(const int32_t *__res
 namespace moe {
 
 hipError_t launch_resolve(moe_ctx *c, int layer, const int32_t *idx, int T, int32_t *slot_of_pair, bool fill,
-                          hipStream_t s) {
+                          hipStream_t s, int32_t *fill_of_pair) {
   const int n = T * c->cfg.top_k;
+  if (fill_of_pair && (c->resident || !fill)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(resolve_kernel, dim3(1), dim3(kThreads), 0, s, idx, n, layer, c->cfg.n_experts, c->cfg.n_slots,
                      c->resident ? 1 : 0, fill ? 1 : 0, c->slot_of, c->id_of, c->stamp, slot_of_pair, c->dmiss,
-                     c->dstats);
+                     c->dstats, fill_of_pair);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || c->resident || !fill) return e;
+  // with fill_of_pair the decode FFN kernels fill the missed slots
+  if (e != hipSuccess || c->resident || !fill || fill_of_pair) return e;
   // at most min(pairs, experts) misses per call
   const int n_miss = n < c->cfg.n_experts ? n : c->cfg.n_experts;
   hipLaunchKernelGGL(fill_kernel, dim3(n_miss * kFillChunks), dim3(kFillThreads), 0, s, c->dmiss, c->host_dev,

@@ -204,6 +204,9 @@ int run_resolve(char **a) {
   }
   int32_t *idx = exact<int32_t>(n, 0);
   int32_t *sop = exact<int32_t>(n, 0xa5);
+  // fill == 2: the slots are left to the decode FFN kernels; the resolve
+  // writes, per pair, the identity to stream from the host store
+  int32_t *fop = fill == 2 ? exact<int32_t>(n, 0xa5) : nullptr;
   Out o(out);
   for (int call = 0; call < calls; ++call) {
     const int32_t *rec = iv.data() + (size_t)call * (1 + n);
@@ -211,10 +214,12 @@ int run_resolve(char **a) {
     if (layer < 0 || layer >= L) die("layer out of range");
     std::memcpy(idx, rec + 1, (size_t)n * 4);
     std::memset(sop, 0xa5, (size_t)n * 4);
-    if (moe::launch_resolve(&c, layer, idx, T, sop, fill != 0, (hipStream_t) nullptr) != hipSuccess)
+    if (fop) std::memset(fop, 0xa5, (size_t)n * 4);
+    if (moe::launch_resolve(&c, layer, idx, T, sop, fill != 0, (hipStream_t) nullptr, fop) != hipSuccess)
       die("launch_resolve failed");
     o.put(c.dmiss, 3);
     o.put(sop, n);
+    if (fop) o.put(fop, n);
   }
   o.put(c.dstats, 6);
   if (!resident) {
@@ -224,7 +229,7 @@ int run_resolve(char **a) {
     // every occupied slot holds its identity's blob (the fill path copies it
     // from the host store; without fill the host copies it, not modelled here)
     int32_t bad = 0;
-    if (fill)
+    if (fill == 1)
       for (int s = 0; s < S; ++s)
         if (c.id_of[s] >= 0 && std::memcmp(pool + (size_t)s * stride, host + (size_t)c.id_of[s] * stride, stride) != 0)
           ++bad;
@@ -239,6 +244,7 @@ int run_resolve(char **a) {
   std::free(pool);
   std::free(idx);
   std::free(sop);
+  std::free(fop);
   return 0;
 }
 

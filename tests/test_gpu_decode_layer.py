@@ -1,5 +1,6 @@
 """moe_decode_layer -- a whole decode layer on a resident cache in six
-launches -- against the seven-launch sequence of separate calls it replaces
+launches (the capped cache: test_gpu_decode_layer_capped.py) -- against the
+seven-launch sequence of separate calls it replaces
 (moe_route -> moe_cache_resolve -> moe_expert_ffn on the decode path ->
 moe_combine_norm / moe_combine), through the C ABI: every output bit for bit,
 the cumulative counters equal, at the real shape (T = 1 .. 64) and small ones
@@ -177,9 +178,10 @@ def test_fused_layer_refusals():
         B.moe_decode_layer(res.ctx, 0, x, 8, wr[0], bias[0], None, buf["idx"], buf["w"], buf["y_pairs"],
                            buf["y_shared"], buf["out"], buf["out"])
     assert ei.value.status == B.MOE_ERR_INVALID
-    cap = MoeContext(d, f, E, k, 1, 8, 8)
+    # a capped cache whose host store is pageable (not mapped into the device address space)
+    cap = MoeContext(d, f, E, k, 1, 8, 8, host_store=torch.zeros((E, res.stride), dtype=torch.uint8))
     cbuf = cap.buffers(8)
-    with pytest.raises(B.MoeError) as ei:  # a capped cache
+    with pytest.raises(B.MoeError) as ei:
         B.moe_decode_layer(cap.ctx, 0, x, 8, wr[0], bias[0], None, cbuf["idx"], cbuf["w"], cbuf["y_pairs"],
                            cbuf["y_shared"], cbuf["out"], None)
     assert ei.value.status == B.MOE_ERR_INVALID
