@@ -202,17 +202,14 @@ moe_status moe_combine(moe_ctx *ctx, const float *y_pairs, const float *w,
  * i.e. from hipHostMalloc) the layer resolves through the LRU table in the
  * context's own slot array.  Results, table, stamps and counters are those of
  * the separate calls with moe_cache_resolve_async in place of
- * moe_cache_resolve; the misses' slots end up holding their blobs' bytes up
- * to the end of the down-projection scales (the padding of the 256-byte
- * stride is not written).  The pages put the cost of a miss in the host link
- * ("一张 RTX 4090 跑千亿模型 ...", section 如何做到：三层存储); for T <= 4
- * (every expert then one unit row of each FFN kernel) no fill kernel runs:
- * the FFN units of a missed expert stream its weights from the host store
- * themselves and write every byte they read into its slot, so the transfer
- * overlaps the hit experts' work and one launch fewer is made (seven).  For
- * larger T the fill kernel runs first, as in moe_cache_resolve_async.  A call
- * that cannot pin its working set changes nothing in the table, counts one
- * failed call and leaves its pairs' y_pairs rows unwritten (out is then not
+ * moe_cache_resolve, the slots' contents included.  The pages put the cost
+ * of a miss in the host link ("一张 RTX 4090 跑千亿模型 ...", section
+ * 如何做到：三层存储); the missed blobs are copied from the mapped host store
+ * as moe_cache_resolve_async's fill kernel copies them, but by spare
+ * workgroups of the bucketing launch, which does not depend on the resolve:
+ * seven launches instead of the separate calls' eight.  A call that cannot
+ * pin its working set changes nothing in the table, counts one failed call
+ * and leaves its pairs' y_pairs rows unwritten (out is then not
  * meaningful).
  *
  * MOE_ERR_INVALID otherwise (a capped cache whose host_store is not mapped,

@@ -51,7 +51,7 @@ static void free_ctx(moe_ctx *c) {
   if (!c) return;
   void *dev[] = {c->slot_of, c->id_of, c->stamp, c->dstats, c->logits_ws, c->offsets_ws, c->perm_ws,
                  c->chunk_ws, c->work, c->work8, c->n_work, c->xrec, c->hrec, c->h16,
-                 c->slot_ws, c->fill_ws, c->dmiss, c->route_part};
+                 c->slot_ws, c->dmiss, c->route_part};
   for (void *p : dev)
     if (p) (void)hipFree(p);
   if (c->hmiss) (void)hipHostFree(c->hmiss);
@@ -127,7 +127,6 @@ extern "C" moe_status moe_create(const moe_config *cfg, moe_ctx **out) {
   // record shares xrec)
   TRY(dalloc(&c->h16, (size_t)hrows * dsb * moe::kSbCols * 2));
   TRY(dalloc(&c->slot_ws, c->max_pairs));
-  TRY(dalloc(&c->fill_ws, c->max_pairs));
   // decode-size router: about 256 workgroups in all, at least one 16-column
   // chunk per wave (8 waves per workgroup)
   c->route_ks = 256 / ((k.n_experts + 15) / 16);
@@ -427,16 +426,12 @@ extern "C" moe_status moe_decode_layer(moe_ctx *c, int32_t layer, const float *x
     if (e == hipSuccess) e = moe::launch_bucket_lookup(c, idx, T, moe::kEntryTokens, x, c->xrec, xh, s);
     if (e == hipSuccess) e = moe::launch_ffn_decode_kernels(c, layer, T, nullptr, y_pairs, y_shared, s);
   } else {
-    // capped: up to kEntryTokens tokens every expert is one unit row of each
-    // FFN kernel, which then streams a missed expert from the host store and
-    // fills its slot (no fill kernel; the link transfer overlaps the hit
-    // experts' work); larger batches fill with the fill kernel first
-    int32_t *fill = T <= moe::kEntryTokens ? c->fill_ws : nullptr;
-    if (e == hipSuccess) e = moe::launch_resolve(c, layer, idx, T, c->slot_ws, true, s, fill);
-    if (e == hipSuccess)
-      e = moe::launch_bucket_ex(c, idx, T, c->offsets_ws, c->perm_ws, true, moe::kEntryTokens, x, c->xrec, xh, s,
-                                c->work8);
-    if (e == hipSuccess) e = moe::launch_ffn_decode_kernels(c, layer, T, c->slot_ws, y_pairs, y_shared, s, fill);
+    // capped: the resolve, then one launch for the bucketing, the x record
+    // and the zero-copy fill of the resolve's misses (no fill launch of its
+    // own), then the FFN on the filled slots
+    if (e == hipSuccess) e = moe::launch_resolve(c, layer, idx, T, c->slot_ws, true, s, false);
+    if (e == hipSuccess) e = moe::launch_bucket_fill(c, idx, T, moe::kEntryTokens, x, c->xrec, xh, s);
+    if (e == hipSuccess) e = moe::launch_ffn_decode_kernels(c, layer, T, c->slot_ws, y_pairs, y_shared, s);
   }
   if (e == hipSuccess)
     e = x_next ? moe::launch_combine_norm(y_pairs, w, y_shared, T, c->cfg.top_k, c->cfg.d_model, out, x_next, s)

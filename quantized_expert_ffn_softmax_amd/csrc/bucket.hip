@@ -170,22 +170,29 @@ __device__ void bucket_block(const int32_t *idx, int n, int E, int T, int32_t *_
   }
 }
 
-// Workgroup 0 buckets (bucket_block); the other workgroups of the launch
-// build the record of x (decode path).  With stats (a resident cache, whose
-// slots are the identities), workgroup 0 also records what the resolve
-// kernel records for a resident call: the number of distinct experts touched
-// as this call's lookups and hits, and one call -- so the lookup needs no
-// launch of its own.
+// Workgroup 0 buckets (bucket_block); the next xrec_blocks workgroups build
+// the record of x (decode path); any further ones fill a capped cache's
+// misses, fill.chunks workgroups per miss of the resolve's list (the bucketing
+// does not depend on the resolve, so the two need no order beyond the resolve
+// launch before this one).  With stats (a resident cache, whose slots are the
+// identities), workgroup 0 also records what the resolve kernel records for a
+// resident call: the number of distinct experts touched as this call's
+// lookups and hits, and one call -- so the lookup needs no launch of its own.
 __global__ void __launch_bounds__(kBucketThreads) bucket_small(const int32_t *__restrict__ idx, int n, int E, int T,
                                                        int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
                                                        int build, int entry_m, moe::WorkEntry *work,
                                                        int32_t *n_work, const float *__restrict__ x, int d, int nsb,
-                                                       uint16_t *__restrict__ xrec, int xrec_h,
+                                                       uint16_t *__restrict__ xrec, int xrec_h, int xrec_blocks,
                                                        int32_t *__restrict__ dmiss, int64_t *__restrict__ stats,
-                                                       moe::WorkEntry *work8) {
+                                                       moe::WorkEntry *work8, moe::FillArgs fill) {
   if (blockIdx.x > 0) {
-    moe::build_xrec_range(x, T, d, nsb, xrec, xrec_h, (blockIdx.x - 1) * blockDim.x + threadIdx.x,
-                          (gridDim.x - 1) * blockDim.x);
+    const int b = blockIdx.x - 1;
+    if (b < xrec_blocks) {
+      moe::build_xrec_range(x, T, d, nsb, xrec, xrec_h, b * blockDim.x + threadIdx.x, xrec_blocks * blockDim.x);
+    } else if (fill.chunks > 0) {
+      const int fb = b - xrec_blocks;
+      moe::fill_chunk(fill, fb / fill.chunks, fb % fill.chunks, threadIdx.x, blockDim.x);
+    }
     return;
   }
   __shared__ int nuniq_sh;
@@ -285,14 +292,10 @@ hipError_t launch_bucket_ex(const moe_ctx *c, const int32_t *idx, int T, int32_t
     // build its record, one value per thread (so all its loads are in flight
     // at once: at 8 per thread the record took ~6 us of dependent loads)
     const int nt = ((n > E ? n : E) + 63) / 64 * 64;
-    int blocks = 1;
-    if (x) {
-      const int vals = T * c->L.gate.nsb * moe::kSteps * 8;
-      blocks += (vals + nt - 1) / nt;
-    }
-    hipLaunchKernelGGL(bucket_small, dim3(blocks), dim3(nt), 0, s, idx, n, E, T, offsets, perm,
-                       build ? 1 : 0, entry_m, c->work, c->n_work, x, c->cfg.d_model, c->L.gate.nsb, xrec, xrec_h,
-                       (int32_t *)nullptr, (int64_t *)nullptr, work8);
+    const int xb = x ? (T * c->L.gate.nsb * moe::kSteps * 8 + nt - 1) / nt : 0;
+    hipLaunchKernelGGL(bucket_small, dim3(1 + xb), dim3(nt), 0, s, idx, n, E, T, offsets, perm,
+                       build ? 1 : 0, entry_m, c->work, c->n_work, x, c->cfg.d_model, c->L.gate.nsb, xrec, xrec_h, xb,
+                       (int32_t *)nullptr, (int64_t *)nullptr, work8, moe::FillArgs{});
     return hipGetLastError();
   }
   const int nch = (n + kChunk - 1) / kChunk;
@@ -313,11 +316,25 @@ hipError_t launch_bucket_lookup(const moe_ctx *c, const int32_t *idx, int T, int
   const int E = c->cfg.n_experts, n = T * c->cfg.top_k;
   if (n > kSmallMax || E > 1024 || !c->resident) return hipErrorInvalidValue;
   const int nt = ((n > E ? n : E) + 63) / 64 * 64;
-  const int vals = T * c->L.gate.nsb * moe::kSteps * 8;
-  const int blocks = 1 + (vals + nt - 1) / nt;
-  hipLaunchKernelGGL(bucket_small, dim3(blocks), dim3(nt), 0, s, idx, n, E, T, c->offsets_ws, c->perm_ws, 1, entry_m,
-                     c->work, c->n_work, x, c->cfg.d_model, c->L.gate.nsb, xrec, xrec_h, c->dmiss, c->dstats,
-                     c->work8);
+  const int xb = (T * c->L.gate.nsb * moe::kSteps * 8 + nt - 1) / nt;
+  hipLaunchKernelGGL(bucket_small, dim3(1 + xb), dim3(nt), 0, s, idx, n, E, T, c->offsets_ws, c->perm_ws, 1, entry_m,
+                     c->work, c->n_work, x, c->cfg.d_model, c->L.gate.nsb, xrec, xrec_h, xb, c->dmiss, c->dstats,
+                     c->work8, moe::FillArgs{});
+  return hipGetLastError();
+}
+
+hipError_t launch_bucket_fill(const moe_ctx *c, const int32_t *idx, int T, int entry_m, const float *x,
+                              uint16_t *xrec, int xrec_h, hipStream_t s) {
+  const int E = c->cfg.n_experts, n = T * c->cfg.top_k;
+  if (n > kSmallMax || E > 1024 || c->resident || !c->host_dev) return hipErrorInvalidValue;
+  const int nt = ((n > E ? n : E) + 63) / 64 * 64;
+  const int xb = x ? (T * c->L.gate.nsb * moe::kSteps * 8 + nt - 1) / nt : 0;
+  // as many threads per blob as the fill kernel's 64 x 256; at most
+  // min(pairs, experts) misses per call
+  const int chunks = (16384 + nt - 1) / nt, n_miss = n < E ? n : E;
+  hipLaunchKernelGGL(bucket_small, dim3(1 + xb + n_miss * chunks), dim3(nt), 0, s, idx, n, E, T, c->offsets_ws,
+                     c->perm_ws, 1, entry_m, c->work, c->n_work, x, c->cfg.d_model, c->L.gate.nsb, xrec, xrec_h, xb,
+                     (int32_t *)nullptr, (int64_t *)nullptr, c->work8, fill_args(c, chunks));
   return hipGetLastError();
 }
 
@@ -377,7 +394,8 @@ extern "C" moe_status moe_bucket_noalloc(const int32_t *idx, int32_t T, int32_t 
     const int nt = ((n > E ? n : E) + 63) / 64 * 64;
     hipLaunchKernelGGL(bucket_small, dim3(1), dim3(nt), 0, s, idx, n, E, T, offsets, perm, 0, 1,
                        (moe::WorkEntry *)nullptr, (int32_t *)nullptr, (const float *)nullptr, 0, 0,
-                       (uint16_t *)nullptr, 0, (int32_t *)nullptr, (int64_t *)nullptr, (moe::WorkEntry *)nullptr);
+                       (uint16_t *)nullptr, 0, 0, (int32_t *)nullptr, (int64_t *)nullptr, (moe::WorkEntry *)nullptr,
+                       moe::FillArgs{});
     MOE_HIP(hipGetLastError());
     return MOE_OK;
   }

@@ -21,11 +21,10 @@
 // pinned host store (mapped into the device address space; the reads cross
 // the host link) into its slot.  The pages name the link as the bottleneck
 // of a miss; the zero-copy fill removes the per-layer host synchronisation.
-// A third way (small decode batches, moe_decode_layer on a capped cache):
-// no fill kernel at all -- the decode FFN kernels stream a missed expert's
-// weights from the mapped host store themselves and write each byte they
-// read into its slot, so the link transfer overlaps the hit experts' work.
+// (A capped decode layer runs the same copy in spare workgroups of its
+// bucketing launch instead of a launch of its own: fill.h.)
 #include "device_util.h"
+#include "fill.h"
 #include "moe_internal.h"
 
 namespace {
@@ -60,17 +59,13 @@ __device__ inline void add_stat(int64_t *p, int64_t v) {
 }
 
 // stats: [0] unique identities, [1] hits, [2] misses, [3] calls, [4] calls that
-// could not pin their working set, [5] the clock.
-// With fill_of_pair (capped cache, misses filled by the decode FFN kernels
-// themselves) every pair p < n also gets the identity to stream from the host
-// store when its expert missed in this call, else -1.
+// could not pin their working set, [5] the clock
 __global__ void __launch_bounds__(kThreads) resolve_kernel(const int32_t *__restrict__ idx, int n, int layer, int E,
                                                            int S, int resident, int clear_on_fail,
                                                            int32_t *__restrict__ slot_of, int32_t *__restrict__ id_of,
                                                            uint32_t *__restrict__ stamp,
                                                            int32_t *__restrict__ slot_of_pair,
-                                                           int32_t *__restrict__ dmiss, int64_t *__restrict__ stats,
-                                                           int32_t *__restrict__ fill_of_pair) {
+                                                           int32_t *__restrict__ dmiss, int64_t *__restrict__ stats) {
   __shared__ int mark[1024];
   __shared__ int miss_e[1024];
   __shared__ int victim[1024];
@@ -115,10 +110,7 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(const int32_t *__rest
   if (is_miss) miss_e[mpos] = tid;
   if (nuniq > S) {  // cannot pin this call's working set: change nothing
     if (clear_on_fail)  // no host reads the error: the call's pairs get no slot (no output)
-      for (int p = tid; p < n; p += kThreads) {
-        slot_of_pair[p] = -1;
-        if (fill_of_pair) fill_of_pair[p] = -1;
-      }
+      for (int p = tid; p < n; p += kThreads) slot_of_pair[p] = -1;
     if (tid == 0) {
       dmiss[0] = nuniq;
       dmiss[1] = 0;
@@ -149,10 +141,7 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(const int32_t *__rest
     best = block_min_u64(best, shred);
     if (best == kNone) {  // cannot happen on a consistent table; never write out of range
       if (clear_on_fail)
-        for (int p = tid; p < n; p += kThreads) {
-          slot_of_pair[p] = -1;
-          if (fill_of_pair) fill_of_pair[p] = -1;
-        }
+        for (int p = tid; p < n; p += kThreads) slot_of_pair[p] = -1;
       if (tid == 0) {
         dmiss[0] = nuniq;
         dmiss[1] = 0;
@@ -177,15 +166,12 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(const int32_t *__rest
     stamp[v] = clock;
     dmiss[3 + 2 * tid] = id;
     dmiss[4 + 2 * tid] = v;
-    mark[miss_e[tid]] = 2;  // this call's misses (mark is not read as a set any more)
   }
   __threadfence_block();
   __syncthreads();
   for (int p = tid; p < n; p += kThreads) {
     const int e = idx[p];
-    const bool ok = e >= 0 && e < E;
-    slot_of_pair[p] = ok ? slot_of[base + e] : -1;
-    if (fill_of_pair) fill_of_pair[p] = ok && mark[e] == 2 ? base + e : -1;
+    slot_of_pair[p] = (e >= 0 && e < E) ? slot_of[base + e] : -1;
   }
   if (tid == 0) {
     dmiss[0] = nuniq;
@@ -200,55 +186,41 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(const int32_t *__rest
 }
 
 // Zero-copy miss fill: workgroup b copies chunk b % kFillChunks of miss
-// b / kFillChunks (if that miss exists) from the mapped host store into its
-// slot.  16-byte loads and stores; the blob stride is a multiple of 256.
+// b / kFillChunks (if that miss exists) into its slot.
 constexpr int kFillChunks = 64;
 constexpr int kFillThreads = 256;
 
-__global__ void __launch_bounds__(kFillThreads) fill_kernel(const int32_t *__restrict__ dmiss,
-                                                            const uint8_t *__restrict__ host_store,
-                                                            uint8_t *__restrict__ slot_pool, uint64_t stride,
-                                                            int64_t n_ids, int n_slots) {
-  const int i = blockIdx.x / kFillChunks, chunk = blockIdx.x % kFillChunks;
-  if (i >= dmiss[1]) return;
-  const int64_t id = dmiss[3 + 2 * i];
-  const int slot = dmiss[4 + 2 * i];
-  if (id < 0 || id >= n_ids || slot < 0 || slot >= n_slots) return;  // never copy out of range
-  const uint64_t n16 = stride / 16, per = (n16 + kFillChunks - 1) / kFillChunks;
-  const uint64_t b0 = chunk * per, b1 = b0 + per < n16 ? b0 + per : n16;
-  const uint4 *src = reinterpret_cast<const uint4 *>(host_store + (uint64_t)id * stride);
-  uint4 *dst = reinterpret_cast<uint4 *>(slot_pool + (uint64_t)slot * stride);
-  // four loads in flight per thread before the stores
-  uint64_t q = b0 + threadIdx.x;
-  for (; q + 3 * kFillThreads < b1; q += 4 * kFillThreads) {
-    const uint4 a0 = src[q], a1 = src[q + kFillThreads], a2 = src[q + 2 * kFillThreads], a3 = src[q + 3 * kFillThreads];
-    dst[q] = a0;
-    dst[q + kFillThreads] = a1;
-    dst[q + 2 * kFillThreads] = a2;
-    dst[q + 3 * kFillThreads] = a3;
-  }
-  for (; q < b1; q += kFillThreads) dst[q] = src[q];
+__global__ void __launch_bounds__(kFillThreads) fill_kernel(moe::FillArgs F) {
+  moe::fill_chunk(F, blockIdx.x / kFillChunks, blockIdx.x % kFillChunks, threadIdx.x, kFillThreads);
 }
 
 }  // namespace
 
 namespace moe {
 
+FillArgs fill_args(const moe_ctx *c, int chunks) {
+  FillArgs F;
+  F.dmiss = c->dmiss;
+  F.host = c->host_dev;
+  F.pool = (uint8_t *)c->cfg.slot_pool;
+  F.stride = c->L.stride;
+  F.n_ids = (int64_t)c->cfg.n_layers * c->cfg.n_experts;
+  F.n_slots = c->cfg.n_slots;
+  F.chunks = chunks;
+  return F;
+}
+
 hipError_t launch_resolve(moe_ctx *c, int layer, const int32_t *idx, int T, int32_t *slot_of_pair, bool fill,
-                          hipStream_t s, int32_t *fill_of_pair) {
+                          hipStream_t s, bool launch_fill) {
   const int n = T * c->cfg.top_k;
-  if (fill_of_pair && (c->resident || !fill)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(resolve_kernel, dim3(1), dim3(kThreads), 0, s, idx, n, layer, c->cfg.n_experts, c->cfg.n_slots,
                      c->resident ? 1 : 0, fill ? 1 : 0, c->slot_of, c->id_of, c->stamp, slot_of_pair, c->dmiss,
-                     c->dstats, fill_of_pair);
+                     c->dstats);
   hipError_t e = hipGetLastError();
-  // with fill_of_pair the decode FFN kernels fill the missed slots
-  if (e != hipSuccess || c->resident || !fill || fill_of_pair) return e;
+  if (e != hipSuccess || c->resident || !fill || !launch_fill) return e;
   // at most min(pairs, experts) misses per call
   const int n_miss = n < c->cfg.n_experts ? n : c->cfg.n_experts;
-  hipLaunchKernelGGL(fill_kernel, dim3(n_miss * kFillChunks), dim3(kFillThreads), 0, s, c->dmiss, c->host_dev,
-                     (uint8_t *)c->cfg.slot_pool, (uint64_t)c->L.stride,
-                     (int64_t)c->cfg.n_layers * c->cfg.n_experts, c->cfg.n_slots);
+  hipLaunchKernelGGL(fill_kernel, dim3(n_miss * kFillChunks), dim3(kFillThreads), 0, s, fill_args(c, kFillChunks));
   return hipGetLastError();
 }
 

@@ -29,19 +29,6 @@ namespace {
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
-// 16-byte global (not flat) loads, whatever the compiler can prove of the pointer
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-__device__ inline uint4 ld_global16(const uint8_t *p) {
-  return __builtin_bit_cast(uint4, *(const __attribute__((address_space(1))) u32x4 *)p);
-}
-// 16-byte store at byte `off` of a slot through a buffer resource over the
-// slot's `bytes` (scalar base, 32-bit lane offset; the hardware drops a store
-// past `bytes`, so a slot write cannot leave its slot).  0x00020000 is the
-// resource's fourth word for raw 32-bit accesses on this architecture.
-__device__ inline void st_slot16(uint8_t *slot, uint32_t bytes, uint32_t off, uint4 v) {
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(slot, 0, (int)bytes, 0x00020000);
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, 0);
-}
 
 // pair p (0..79) of a superblock: word p/5, slot p%5 (low half) and p%5+5
 // (high half); columns 10 (p/5) + p%5 and +5.
@@ -67,11 +54,6 @@ struct DecodeParams {
   const uint16_t *xrec_zero, *hrec_zero;  // the all-zero rows
   float *y_pairs, *y_shared;
   int d_model, d_ff;
-  // capped cache, misses filled here: per pair the identity to stream from
-  // the mapped host store (-1: none); null when the slots are all filled
-  const int32_t *fill_of_pair;
-  const uint8_t *host_store;
-  int64_t n_ids;
 };
 
 __device__ inline const uint8_t *entry_blob(const DecodeParams &P, const moe::WorkEntry &we) {
@@ -150,7 +132,6 @@ struct Cols {
 
 struct Unit {
   const uint8_t *blob;  // the expert's blob (a readable stand-in when the entry is unusable)
-  uint8_t *dst;         // the expert's slot when blob is its copy in the host store (a miss), else null
   int tile0;            // first 16-row tile of the unit
   int m;                // entry columns in use (0 for an unusable entry)
   int routed;
@@ -182,14 +163,7 @@ __device__ inline Mats<NMAT> mats_of(const DecodeParams &P) {
   return Mt;
 }
 
-// A miss filled by the FFN kernels: the unit reads the expert from the host
-// store and writes every 16 bytes it read at the same offset of the slot.  A
-// unit reads only inside the blob, and the units of one entry (the expert's
-// only one: the caller keeps every expert to one entry per list) together
-// read all of its matrices' code and scale bytes, so the slot then holds the
-// blob's bytes up to the end of its last section.  No other unit of the call
-// reads this slot (every unit of the expert streams from the host).
-template <int COLS, bool FILL>
+template <int COLS>
 __device__ inline void unit_setup(const DecodeParams &P, int u, int tpu, int tiles, int col, Unit &U) {
   const moe::WorkEntry we = (COLS == 8 ? P.work8 : P.work)[u / tpu];
   U.tile0 = (u % tpu) * tiles;
@@ -197,16 +171,6 @@ __device__ inline void unit_setup(const DecodeParams &P, int u, int tpu, int til
   const uint8_t *blob = entry_ok(P, we, COLS) ? entry_blob(P, we) : nullptr;
   U.m = blob ? we.m : 0;
   U.blob = blob ? blob : P.shared_pool + (size_t)P.layer * P.stride;
-  U.dst = nullptr;
-  if constexpr (FILL) {
-    if (blob && U.routed) {
-      const int fid = P.fill_of_pair[P.perm[we.first]];
-      if (fid >= 0 && fid < P.n_ids) {
-        U.dst = reinterpret_cast<uint8_t *>(moe::uniform_base(blob));  // one address for the workgroup
-        U.blob = P.host_store + (size_t)fid * P.stride;
-      }
-    }
-  }
   U.tok = 0;
   U.rrow = 0;
   U.has_tok = col < U.m && entry_token(P, we, col, U.tok, U.rrow);
@@ -233,22 +197,11 @@ struct CopyCounts {
   static constexpr int sc = (64 * sc_pitch(5 * NSB + 8) + 16 * 64 * kWaves - 1) / (16 * 64 * kWaves);
 };
 
-// 16 bytes of scales of a missed expert: read from the host store with an
-// ordinary load (no direct-to-LDS copy from host memory), written to LDS and
-// to the expert's slot at the offset they were read from
-__device__ inline void fill_granule(const uint8_t *src_blob, uint8_t *slot, uint32_t bytes, uint32_t off,
-                                    uint8_t *lds) {
-  const uint4 v = ld_global16(src_blob + off);
-  *reinterpret_cast<uint4 *>(lds) = v;
-  st_slot16(slot, bytes, off, v);
-}
-
 // activation slot p = (superblock * 20 + step) * 2 COLS + half * COLS + col
-// holds the 8 halves of that record step for entry column col.  With FILL
-// and a missed expert (U.dst) the scales take the ordinary-load path above.
-template <int NSB, int NMAT, int COLS, bool FILL>
-__device__ inline void copy_unit_lds(const Mats<NMAT> &Mt, const Unit &U, uint32_t bytes, int tid, uint32_t row_off,
-                                     int unit_rows, int sc_mat_bytes, uint8_t *lact, uint8_t *lsc) {
+// holds the 8 halves of that record step for entry column col
+template <int NSB, int NMAT, int COLS>
+__device__ inline void copy_unit_lds(const Mats<NMAT> &Mt, const Unit &U, int tid, uint32_t row_off, int unit_rows,
+                                     int sc_mat_bytes, uint8_t *lact, uint8_t *lsc) {
   const uint8_t *rec = reinterpret_cast<const uint8_t *>(Mt.rec);
   const int half = (tid / COLS) & 1, w = tid >> 6;
   const uint32_t a0 = lds_addr(lact) + 1024u * w;
@@ -267,26 +220,6 @@ __device__ inline void copy_unit_lds(const Mats<NMAT> &Mt, const Unit &U, uint32
   // lane's source, so padding a row costs only the extra granule
   const uint32_t s0 = lds_addr(lsc) + 1024u * w;
   const int rb = Mt.m[0].nblk * 2, pitch = sc_pitch(Mt.m[0].nblk), gpr = pitch / 16;
-  if constexpr (FILL) {
-    if (U.dst) {
-#pragma unroll
-      for (int mat = 0; mat < NMAT; ++mat) {
-        const uint32_t o = Mt.m[mat].scale_off + (uint32_t)U.tile0 * 16 * rb;
-        uint8_t *l = lsc + mat * sc_mat_bytes;
-#pragma unroll
-        for (int i = 0; i < CopyCounts<NSB, NMAT, COLS>::sc; ++i) {
-          const int k = tid + 64 * kWaves * i;  // granule k lands at LDS byte 16 k of the matrix's region
-          if (pitch == rb) {
-            if (16 * k < unit_rows * rb) fill_granule(U.blob, U.dst, bytes, o + 16 * k, l + 16 * k);
-          } else if (k < unit_rows * gpr) {
-            const int row = k / gpr, c = min(k - row * gpr, rb / 16 - 1);
-            fill_granule(U.blob, U.dst, bytes, o + (uint32_t)(row * rb + 16 * c), l + 16 * k);
-          }
-        }
-      }
-      return;
-    }
-  }
 #pragma unroll
   for (int mat = 0; mat < NMAT; ++mat) {
     const uint8_t *src = U.blob + Mt.m[mat].scale_off + (uint32_t)U.tile0 * 16 * rb;
@@ -391,26 +324,16 @@ constexpr int words_depth() {
 template <int NSB, int NMAT>
 struct WordSrc {
   const uint8_t *blob;
-  uint8_t *dst;        // a miss: the slot the words are written to as they arrive (else null)
-  uint32_t bytes;      // the slot's size
   uint32_t off[NMAT];  // this lane's quad of the range's first superblock in each matrix
   int nvalid;
 };
-
-// a miss: the word quads of superblock S into the slot, at the offsets they were read from
-template <int NSB, int NMAT, int S>
-__device__ inline void fill_words(const WordSrc<NSB, NMAT> &Src, const uint4 (&W)[NSB][NMAT]) {
-  const uint32_t so = S + 1 < NSB ? (uint32_t)S * 64 : (uint32_t)min(S, Src.nvalid - 1) * 64;
-#pragma unroll
-  for (int mat = 0; mat < NMAT; ++mat) st_slot16(Src.dst, Src.bytes, Src.off[mat] + so, W[S][mat]);
-}
 
 template <int NSB, int NMAT, int S>
 __device__ inline void load_words(const WordSrc<NSB, NMAT> &Src, uint4 (&W)[NSB][NMAT]) {
   // only a range's last superblock can lie past the row (a shorter second half)
   const uint32_t so = S + 1 < NSB ? (uint32_t)S * 64 : (uint32_t)min(S, Src.nvalid - 1) * 64;
 #pragma unroll
-  for (int mat = 0; mat < NMAT; ++mat) W[S][mat] = ld_global16(Src.blob + (Src.off[mat] + so));
+  for (int mat = 0; mat < NMAT; ++mat) W[S][mat] = *reinterpret_cast<const uint4 *>(Src.blob + (Src.off[mat] + so));
 }
 
 template <int NSB, int NMAT, int... Ss>
@@ -431,7 +354,7 @@ __device__ inline void refill(uint4 (&W)[NSB][NMAT], const WordSrc<NSB, NMAT> &S
 // superblocks S and S + 1 together, their steps interleaved (twice the
 // independent dequantise-and-MFMA chains per wave); a last odd superblock
 // alone
-template <int NSB, int NMAT, int COLS, bool FILL, int S>
+template <int NSB, int NMAT, int COLS, int S>
 __device__ inline void compute_pair(uint4 (&W)[NSB][NMAT], const WordSrc<NSB, NMAT> &Src,
                                     const uint8_t *(&srow)[NMAT], int g, int nblk, const uint32_t (&sel)[6],
                                     const Consts &K, const uint8_t *xb, f4 &acc0, f4 &acc1, f4 &acc2, f4 &acc3) {
@@ -442,9 +365,6 @@ __device__ inline void compute_pair(uint4 (&W)[NSB][NMAT], const WordSrc<NSB, NM
   MatSb M[NMAT];
 #pragma unroll
   for (int mat = 0; mat < NMAT; ++mat) M[mat] = mat_sb<S + 2 >= NSB>(W[S][mat], srow[mat], 5 * S + g, nblk, sel);
-  if constexpr (FILL) {
-    if (Src.dst) fill_words<NSB, NMAT, S>(Src, W);
-  }
   refill<NSB, NMAT, S>(W, Src);
   const uint8_t *xs = xb + S * Cols<COLS>::kSbBytes;
   if constexpr (S + 1 < NSB) {
@@ -452,9 +372,6 @@ __device__ inline void compute_pair(uint4 (&W)[NSB][NMAT], const WordSrc<NSB, NM
 #pragma unroll
     for (int mat = 0; mat < NMAT; ++mat)
       M2[mat] = mat_sb<S + 3 >= NSB>(W[S + 1][mat], srow[mat], 5 * (S + 1) + g, nblk, sel);
-    if constexpr (FILL) {
-      if (Src.dst) fill_words<NSB, NMAT, S + 1>(Src, W);
-    }
     refill<NSB, NMAT, S + 1>(W, Src);
     const uint8_t *xs2 = xs + Cols<COLS>::kSbBytes;
     sb_step<NMAT, 0, COLS>(M, K, xs, acc0, acc1);
@@ -476,12 +393,12 @@ __device__ inline void compute_pair(uint4 (&W)[NSB][NMAT], const WordSrc<NSB, NM
   }
 }
 
-template <int NSB, int NMAT, int COLS, bool FILL, int... Ps>
+template <int NSB, int NMAT, int COLS, int... Ps>
 __device__ inline void compute_all(std::integer_sequence<int, Ps...>, uint4 (&W)[NSB][NMAT],
                                    const WordSrc<NSB, NMAT> &Src, const uint8_t *(&srow)[NMAT], int g, int nblk,
                                    const uint32_t (&sel)[6], const Consts &K, const uint8_t *xb, f4 &acc0, f4 &acc1,
                                    f4 &acc2, f4 &acc3) {
-  (compute_pair<NSB, NMAT, COLS, FILL, 2 * Ps>(W, Src, srow, g, nblk, sel, K, xb, acc0, acc1, acc2, acc3), ...);
+  (compute_pair<NSB, NMAT, COLS, 2 * Ps>(W, Src, srow, g, nblk, sel, K, xb, acc0, acc1, acc2, acc3), ...);
 }
 
 // KS = 2 (gate/up of small batches): K split in two halves over the waves of a
@@ -497,7 +414,7 @@ constexpr int decode_min_blocks() {
   return NMAT == 2 ? 3 : (NSB <= 6 ? 4 : (NSB <= 9 ? 3 : 2));
 }
 
-template <int NSB, int NMAT, int KS, int COLS, bool FILL>
+template <int NSB, int NMAT, int KS, int COLS>
 __global__ void __launch_bounds__(64 * kWaves, (decode_min_blocks<NSB, NMAT>())) ffn_decode_kernel(DecodeParams P) {
   static_assert(KS == 1 || (NMAT == 2 && ((NSB + 1) / 2) % 2 == 1), "K split: gate/up, an odd half length");
   static_assert(COLS == 4 || COLS == 8, "entries of 4 or 8 tokens");
@@ -540,15 +457,13 @@ __global__ void __launch_bounds__(64 * kWaves, (decode_min_blocks<NSB, NMAT>()))
     if (!first) __syncthreads();  // every wave is done with the previous unit's LDS data
     first = false;
     Unit U;
-    unit_setup<COLS, FILL>(P, u, tpu, kTiles, tid & (COLS - 1), U);
+    unit_setup<COLS>(P, u, tpu, kTiles, tid & (COLS - 1), U);
     const uint32_t row_off = (uint32_t)(NMAT == 2 ? U.tok : U.rrow) * (uint32_t)Mt.rec_h * 2u;
-    copy_unit_lds<NSB, NMAT, COLS, FILL>(Mt, U, P.stride, tid, row_off, 16 * kTiles, kScMat, lact, lsc);
+    copy_unit_lds<NSB, NMAT, COLS>(Mt, U, tid, row_off, 16 * kTiles, kScMat, lact, lsc);
     // the word quads of this wave's rows, as many superblocks as fit
     const int row = min((U.tile0 + ltile) * 16 + r16, Mt.m[0].rows - 1);
     WordSrc<NS, NMAT> Src;
     Src.blob = U.blob;
-    Src.dst = U.dst;
-    Src.bytes = P.stride;
     Src.nvalid = min(NS, NSB - sb0);
 #pragma unroll
     for (int mat = 0; mat < NMAT; ++mat)
@@ -565,7 +480,7 @@ __global__ void __launch_bounds__(64 * kWaves, (decode_min_blocks<NSB, NMAT>()))
     for (int mat = 0; mat < NMAT; ++mat)
       srow[mat] = lsc + mat * kScMat + (ltile * 16 + r16) * sc_pitch(nblk);
     f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f}, acc2 = acc0, acc3 = acc0;
-    compute_all<NS, NMAT, COLS, FILL>(std::make_integer_sequence<int, (NS + 1) / 2>{}, W, Src, srow, 5 * sb0 + g, nblk,
+    compute_all<NS, NMAT, COLS>(std::make_integer_sequence<int, (NS + 1) / 2>{}, W, Src, srow, 5 * sb0 + g, nblk,
                                 sel, K, xb, acc0, acc1, acc2, acc3);
     acc0 += acc2;
     acc1 += acc3;
@@ -613,20 +528,13 @@ template <int NSB, int NMAT, int KS = 1>
 hipError_t launch_decode_nsb(const DecodeParams &P, int units, int per_cu, int n_cu, hipStream_t s) {
   const int cap = (per_cu > 0 ? per_cu : 1) * (n_cu > 0 ? n_cu : 1);
   const int grid = (std::min(units, cap) + kXcds - 1) / kXcds * kXcds;
-  if (P.fill_of_pair)
-    hipLaunchKernelGGL((ffn_decode_kernel<NSB, NMAT, KS, cols_of<NMAT>(), true>), dim3(grid), dim3(64 * kWaves), 0, s,
-                       P);
-  else
-    hipLaunchKernelGGL((ffn_decode_kernel<NSB, NMAT, KS, cols_of<NMAT>(), false>), dim3(grid), dim3(64 * kWaves), 0,
-                       s, P);
+  hipLaunchKernelGGL((ffn_decode_kernel<NSB, NMAT, KS, cols_of<NMAT>()>), dim3(grid), dim3(64 * kWaves), 0, s, P);
   return hipGetLastError();
 }
 
-// the filling kernels are built for the same occupancy (their extra stores
-// reuse the loads' registers)
 template <int NSB, int NMAT, int KS = 1>
 hipError_t occupancy_nsb(int *occ) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, ffn_decode_kernel<NSB, NMAT, KS, cols_of<NMAT>(), false>,
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, ffn_decode_kernel<NSB, NMAT, KS, cols_of<NMAT>()>,
                                                       64 * kWaves, 0);
 }
 
@@ -701,7 +609,7 @@ hipError_t launch_ffn_decode(const moe_ctx *c, int layer, const float *x, int T,
 }
 
 hipError_t launch_ffn_decode_kernels(const moe_ctx *c, int layer, int T, const int32_t *slot_of_pair, float *y_pairs,
-                                     float *y_shared, hipStream_t s, const int32_t *fill_of_pair) {
+                                     float *y_shared, hipStream_t s) {
   const moe_config &k = c->cfg;
   const int xh = xrec_halves(c->L.gate.nsb);
   hipError_t e = hipSuccess;
@@ -734,12 +642,6 @@ hipError_t launch_ffn_decode_kernels(const moe_ctx *c, int layer, int T, const i
   P.y_shared = y_shared;
   P.d_model = k.d_model;
   P.d_ff = k.d_ff;
-  // a unit that fills a slot must be the expert's only one: at most
-  // kEntryTokens tokens, so at most one entry per expert in either list
-  if (fill_of_pair && (T > kEntryTokens || c->resident || !c->host_dev || !slot_of_pair)) return hipErrorInvalidValue;
-  P.fill_of_pair = fill_of_pair;
-  P.host_store = c->host_dev;
-  P.n_ids = (int64_t)k.n_layers * k.n_experts;
   const int ents = max_entries(T, k.top_k, k.n_experts, cols_of<2>());
   const int ents_d = max_entries(T, k.top_k, k.n_experts, cols_of<1>());
   const int u1 = ents * ((k.d_ff / 16 + kWaves - 1) / kWaves), u2 = ents_d * ((k.d_model / 16 + kWaves - 1) / kWaves);

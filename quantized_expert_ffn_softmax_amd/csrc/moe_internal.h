@@ -7,6 +7,7 @@
 
 #include <string>
 
+#include "fill.h"
 #include "libmoe.h"
 
 namespace moe {
@@ -117,7 +118,6 @@ struct moe_ctx {
   uint16_t *hrec;        // decode h record: [max_pairs + max_tokens + 1][xrec_halves(down.nsb)]
   uint16_t *h16;         // prefill h record: [max_pairs + max_tokens][down.nsb * 160 * 2] fp16 (hi, lo), pads zero
   int32_t *slot_ws;      // [max_pairs] slots when the caller passes none
-  int32_t *fill_ws;      // [max_pairs] per pair, the identity its decode FFN units stream from the host store (-1: none)
   float *route_part;     // [route_ks][route_small_t][n_experts] partial logits (decode-size router)
   int32_t route_ks;      // column slices of the decode-size router
   int32_t route_small_t; // largest T routed by the decode-size router (<= 64)
@@ -159,30 +159,32 @@ hipError_t launch_bucket(const moe_ctx *c, const int32_t *idx, int T, int32_t *o
 hipError_t launch_bucket_ex(const moe_ctx *c, const int32_t *idx, int T, int32_t *offsets, int32_t *perm, bool build,
                             int entry_m, const float *x, uint16_t *xrec, int xrec_h, hipStream_t s,
                             moe::WorkEntry *work8);
-// fill: misses are filled without a host round trip (a call that cannot pin
-// its working set then gives every pair slot -1).  With fill_of_pair (capped
-// cache, fill) no fill kernel is launched: the resolve writes each pair's
-// identity to stream from the host store (-1: none) and the decode FFN
-// kernels, given the same array, fill the slots.
+// fill: misses are filled with no host round trip, and a call that cannot
+// pin its working set gives every pair slot -1; the fill kernel is launched
+// unless launch_fill is false (the caller then runs launch_bucket_fill)
 hipError_t launch_resolve(moe_ctx *c, int layer, const int32_t *idx, int T, int32_t *slot_of_pair, bool fill,
-                          hipStream_t s, int32_t *fill_of_pair = nullptr);
+                          hipStream_t s, bool launch_fill = true);
 hipError_t decode_occupancy(moe_ctx *c);  // fills c->decode_occ for c's superblock counts
 hipError_t launch_ffn_decode(const moe_ctx *c, int layer, const float *x, int T, const int32_t *idx,
                              const int32_t *slot_of_pair, float *y_pairs, float *y_shared, hipStream_t s);
 // the decode FFN kernels alone, on the work list, perm and x record already
 // in the context's workspace (from launch_ffn_decode's bucketing or from
 // launch_route_bucket)
-// With fill_of_pair (from launch_resolve; every expert with at most one
-// entry per list, i.e. T <= kEntryTokens) a unit whose pairs name an identity
-// there reads the expert from the mapped host store and writes what it read
-// into the expert's slot.
 hipError_t launch_ffn_decode_kernels(const moe_ctx *c, int layer, int T, const int32_t *slot_of_pair, float *y_pairs,
-                                     float *y_shared, hipStream_t s, const int32_t *fill_of_pair = nullptr);
+                                     float *y_shared, hipStream_t s);
 // resident cache: the lookup count (as launch_resolve records it) + the
 // bucketing with its work list (entry_m) + the x record, in one launch;
 // T * top_k <= 1024, n_experts <= 1024
 hipError_t launch_bucket_lookup(const moe_ctx *c, const int32_t *idx, int T, int entry_m, const float *x,
                                 uint16_t *xrec, int xrec_h, hipStream_t s);
+// the zero-copy fill's arguments for c's cache, `chunks` workgroups per blob
+FillArgs fill_args(const moe_ctx *c, int chunks);
+// capped cache: the bucketing with its work lists, the x record (with x) and,
+// in further workgroups of the same launch, the zero-copy fill of the misses
+// that launch_resolve (launch_fill = false) listed; T * top_k <= 1024,
+// n_experts <= 1024
+hipError_t launch_bucket_fill(const moe_ctx *c, const int32_t *idx, int T, int entry_m, const float *x,
+                              uint16_t *xrec, int xrec_h, hipStream_t s);
 hipError_t launch_ffn_prefill(const moe_ctx *c, int layer, const float *x, int T, const int32_t *idx,
                               const int32_t *slot_of_pair, float *y_pairs, float *y_shared, hipStream_t s);
 hipError_t launch_combine(const float *y_pairs, const float *w, const float *y_shared, int T, int k, int d,

@@ -204,9 +204,17 @@ int run_resolve(char **a) {
   }
   int32_t *idx = exact<int32_t>(n, 0);
   int32_t *sop = exact<int32_t>(n, 0xa5);
-  // fill == 2: the slots are left to the decode FFN kernels; the resolve
-  // writes, per pair, the identity to stream from the host store
-  int32_t *fop = fill == 2 ? exact<int32_t>(n, 0xa5) : nullptr;
+  // fill == 2: no fill kernel; the fill runs in the bucketing launch of a
+  // capped decode layer (launch_bucket_fill), which needs the bucketing workspace
+  if (fill == 2) {
+    c.max_work = z.max_work;
+    c.max_work8 = z.max_work8;
+    c.offsets_ws = exact<int32_t>(E + 1, 0xa5);
+    c.perm_ws = exact<int32_t>(z.max_pairs, 0xa5);
+    c.work = exact<moe::WorkEntry>(z.max_work, 0xa5);
+    c.work8 = exact<moe::WorkEntry>(z.max_work8, 0xa5);
+    c.n_work = exact<int32_t>(4, 0xa5);
+  }
   Out o(out);
   for (int call = 0; call < calls; ++call) {
     const int32_t *rec = iv.data() + (size_t)call * (1 + n);
@@ -214,12 +222,14 @@ int run_resolve(char **a) {
     if (layer < 0 || layer >= L) die("layer out of range");
     std::memcpy(idx, rec + 1, (size_t)n * 4);
     std::memset(sop, 0xa5, (size_t)n * 4);
-    if (fop) std::memset(fop, 0xa5, (size_t)n * 4);
-    if (moe::launch_resolve(&c, layer, idx, T, sop, fill != 0, (hipStream_t) nullptr, fop) != hipSuccess)
+    if (moe::launch_resolve(&c, layer, idx, T, sop, fill != 0, (hipStream_t) nullptr, fill != 2) != hipSuccess)
       die("launch_resolve failed");
+    if (fill == 2 &&
+        moe::launch_bucket_fill(&c, idx, T, moe::kEntryTokens, nullptr, nullptr, 0, (hipStream_t) nullptr) !=
+            hipSuccess)
+      die("launch_bucket_fill refused the shape");
     o.put(c.dmiss, 3);
     o.put(sop, n);
-    if (fop) o.put(fop, n);
   }
   o.put(c.dstats, 6);
   if (!resident) {
@@ -229,7 +239,7 @@ int run_resolve(char **a) {
     // every occupied slot holds its identity's blob (the fill path copies it
     // from the host store; without fill the host copies it, not modelled here)
     int32_t bad = 0;
-    if (fill == 1)
+    if (fill)
       for (int s = 0; s < S; ++s)
         if (c.id_of[s] >= 0 && std::memcmp(pool + (size_t)s * stride, host + (size_t)c.id_of[s] * stride, stride) != 0)
           ++bad;
@@ -244,7 +254,11 @@ int run_resolve(char **a) {
   std::free(pool);
   std::free(idx);
   std::free(sop);
-  std::free(fop);
+  std::free(c.offsets_ws);
+  std::free(c.perm_ws);
+  std::free(c.work);
+  std::free(c.work8);
+  std::free(c.n_work);
   return 0;
 }
 

@@ -5,11 +5,10 @@ store:
 
 * every output bit for bit, call after call, with misses, hits and
   evictions; the same table, stamps and counters after every call;
-* up to 4 tokens no fill kernel runs and the FFN kernels fill the missed
-  slots themselves: every slot in use then holds its identity's blob, byte
-  for byte up to the end of the last section, and later calls that hit those
-  slots still match the twin;
-* from 5 tokens the fill kernel runs first (same checks);
+* no fill kernel runs (the bucketing launch copies the misses in spare
+  workgroups): every slot in use then holds its identity's blob, byte for byte
+  up to the end of the last section, and later calls that hit those slots
+  still match the twin;
 * a 4-layer stack captured in a HIP graph and replayed on new inputs,
   against eager separate calls;
 * a call that cannot pin its working set changes nothing and writes no

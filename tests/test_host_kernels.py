@@ -226,8 +226,7 @@ def _resolve(exe, tmp_path, L, E, S, T, k, calls, fill=1, resident=0, dm=64, dff
         recs.append(np.int32(layer).reshape(1))
         recs.append(idx.astype(np.int32))
     out = _Reader(_run(exe, tmp_path, ["resolve", L, E, S, T, k, len(calls), fill, resident, dm, dff], recs))
-    per_call = [(out.take(3).copy(), out.take(T * k).copy()) + ((out.take(T * k).copy(),) if fill == 2 else ())
-                for _ in calls]
+    per_call = [(out.take(3).copy(), out.take(T * k).copy()) for _ in calls]
     stats = out.take(6, np.int64)
     tail = None
     if not resident:
@@ -239,9 +238,7 @@ def _resolve(exe, tmp_path, L, E, S, T, k, calls, fill=1, resident=0, dm=64, dff
 def _check_lru(per_call, stats, tail, L, E, S, calls):
     orc = oracle.LRUCache(L, E, S)
     failed = 0
-    for rec, (layer, idx) in zip(per_call, calls):
-        dm, sop = rec[0], rec[1]
-        fop = rec[2] if len(rec) > 2 else None
+    for (dm, sop), (layer, idx) in zip(per_call, calls):
         flat = idx.reshape(-1)
         valid = (flat >= 0) & (flat < E)
         nuniq = len(np.unique(flat[valid]))
@@ -250,23 +247,16 @@ def _check_lru(per_call, stats, tail, L, E, S, calls):
                 orc.resolve(layer, flat[valid])
             failed += 1
             assert dm.tolist() == [nuniq, 0, 1] and np.all(sop == -1)
-            assert fop is None or np.all(fop == -1)
             continue
         so, misses = orc.resolve(layer, flat[valid])
         want = np.full(flat.size, -1, np.int32)
         want[valid] = so
         assert dm.tolist() == [nuniq, len(misses), 0]
         assert np.array_equal(sop, want)
-        if fop is not None:
-            # the identity to stream: set on every pair of an expert this call missed
-            missed = {i for i, _slot in misses}
-            ids = layer * E + flat
-            want_f = np.where(valid & np.isin(ids, list(missed)), ids, -1).astype(np.int32)
-            assert np.array_equal(fop, want_f)
     slot_of, id_of, stamp, bad_blobs = tail
     assert slot_of.tolist() == orc.slot_of
     assert id_of.tolist() == orc.id_of.tolist() and stamp.tolist() == orc.stamp.tolist()
-    assert bad_blobs == 0  # every occupied slot holds its identity's blob (none checked when the FFN fills)
+    assert bad_blobs == 0  # every occupied slot holds its identity's blob
     assert stats.tolist() == [orc.lookups, orc.hits, orc.misses, len(calls) - failed, failed, orc.clock]
     return orc
 
@@ -280,10 +270,10 @@ def test_resolve_lru_with_fill(exe, tmp_path):
     assert orc.hits > 0 and orc.misses > S  # the table filled and evicted
 
 
-def test_resolve_leaves_fill_to_the_ffn(exe, tmp_path):
-    # no fill kernel: per pair the identity its FFN units stream from the host
-    # store, exactly the pairs of the experts each call missed; the table as
-    # with the fill kernel, failed calls and ids outside the range included
+def test_resolve_with_the_fill_in_the_bucketing_launch(exe, tmp_path):
+    # no fill kernel: the bucketing launch of a capped decode layer copies the
+    # misses in its spare workgroups; the same table and slot contents as with
+    # the fill kernel, failed calls and ids outside the range included
     L, E, S, T, k = 3, 48, 7, 2, 4
     rng = np.random.default_rng(15)
     calls = []
