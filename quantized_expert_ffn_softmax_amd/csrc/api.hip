@@ -421,15 +421,24 @@ extern "C" moe_status moe_decode_layer(moe_ctx *c, int32_t layer, const float *x
             "moe_decode_layer: needs T * top_k <= 1024");
   hipStream_t s = as_stream(stream);
   const int xh = moe::xrec_halves(c->L.gate.nsb);
-  hipError_t e = moe::launch_router(c, x, T, w_router, bias, logits ? logits : c->logits_ws, idx, w, s);
+  float *lg = logits ? logits : c->logits_ws;
+  hipError_t e = hipSuccess;
   if (c->resident) {
+    e = moe::launch_router(c, x, T, w_router, bias, lg, idx, w, s);
     if (e == hipSuccess) e = moe::launch_bucket_lookup(c, idx, T, moe::kEntryTokens, x, c->xrec, xh, s);
     if (e == hipSuccess) e = moe::launch_ffn_decode_kernels(c, layer, T, nullptr, y_pairs, y_shared, s);
   } else {
-    // capped: the resolve, then one launch for the bucketing, the x record
-    // and the zero-copy fill of the resolve's misses (no fill launch of its
-    // own), then the FFN on the filled slots
-    if (e == hipSuccess) e = moe::launch_resolve(c, layer, idx, T, c->slot_ws, true, s, false);
+    // capped: the router and the resolve (for one or two tokens the top-k
+    // and the resolve share one workgroup), then one launch for the
+    // bucketing, the x record and the zero-copy fill of the resolve's misses
+    // (no fill launch of its own), then the FFN on the filled slots
+    if (T <= 2 && T <= c->route_small_t) {
+      e = moe::launch_router_partials(c, x, T, w_router, s);
+      if (e == hipSuccess) e = moe::launch_route_resolve(c, layer, T, bias, lg, idx, w, c->slot_ws, s);
+    } else {
+      e = moe::launch_router(c, x, T, w_router, bias, lg, idx, w, s);
+      if (e == hipSuccess) e = moe::launch_resolve(c, layer, idx, T, c->slot_ws, true, s, false);
+    }
     if (e == hipSuccess) e = moe::launch_bucket_fill(c, idx, T, moe::kEntryTokens, x, c->xrec, xh, s);
     if (e == hipSuccess) e = moe::launch_ffn_decode_kernels(c, layer, T, c->slot_ws, y_pairs, y_shared, s);
   }

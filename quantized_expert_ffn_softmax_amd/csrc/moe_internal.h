@@ -152,6 +152,14 @@ moe_status moe_fail(moe_status s, const std::string &msg);
 namespace moe {
 hipError_t launch_router(const moe_ctx *c, const float *x, int T, const float *wr, const float *bias,
                          float *logits, int32_t *idx, float *w, hipStream_t s);
+// the decode-size router's first kernel alone (partial logits into
+// c->route_part); T <= c->route_small_t
+hipError_t launch_router_partials(const moe_ctx *c, const float *x, int T, const float *wr, hipStream_t s);
+// capped cache, T <= 2: the router's top-k from c->route_part and the
+// resolve (no fill kernel; a call that cannot pin its working set gives every
+// pair slot -1) in one single-workgroup launch
+hipError_t launch_route_resolve(moe_ctx *c, int layer, int T, const float *bias, float *logits, int32_t *idx,
+                                float *w, int32_t *slot_of_pair, hipStream_t s);
 hipError_t launch_bucket(const moe_ctx *c, const int32_t *idx, int T, int32_t *offsets, int32_t *perm,
                          bool build_work, hipStream_t s);
 // bucketing with the work list of entry_m-token entries (and, with work8, the

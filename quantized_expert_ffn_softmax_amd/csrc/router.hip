@@ -6,6 +6,7 @@
 // 如何做到：三层存储); the scoring function is the softmax reading.
 #include "device_util.h"
 #include "moe_internal.h"
+#include "topk_small.h"
 
 namespace {
 
@@ -255,102 +256,36 @@ __global__ void __launch_bounds__(64 * kRouteWaves) router_logits_mfma(const flo
   }
 }
 
-// One workgroup per token: logits = sum of the KS slices (in order) + bias,
-// then the top-k by rank, where an expert's rank is the number of experts
-// ordered before it by (logit desc, index asc).  The order is that of one
-// 64-bit key, (logit mapped to an order-preserving uint32) << 32 | ~index, so
-// each comparison is one v_cmp_gt_u64.  Two passes: each wave ranks its 64
-// experts among themselves; an expert of global rank < k has wave rank < k,
-// so only those candidates (k per wave) are ranked against each other, and
-// for a candidate in the global top-k that rank is its global rank (every
-// expert ordered before it is a candidate too).  Weights: softmax of the k
-// chosen logits.
-using moe::order_key;
-
+// One workgroup per token (topk_small.h).
 __global__ void __launch_bounds__(1024) router_finish_small(const float *__restrict__ part, int T, int E, int KS,
                                                             const float *__restrict__ bias, int k,
                                                             float *__restrict__ logits, int32_t *__restrict__ idx,
                                                             float *__restrict__ w) {
-  __shared__ __attribute__((aligned(16))) uint64_t lk[1024];
-  __shared__ __attribute__((aligned(16))) uint64_t ck[16 * 32];
-  __shared__ float top_v[32];
-  __shared__ int top_e[32];
-  const int t = blockIdx.x, e = threadIdx.x, wave = e >> 6;
-  float v = -INFINITY;
-  if (e < E) {
-    // the bias and the KS partial sums, requested together (8 slices at a
-    // time, slices past KS clamped and not added), added in slice order
-    const float bv = bias ? bias[e] : 0.f;
-    v = 0.f;
-    for (int q0 = 0; q0 < KS; q0 += 8) {
-      float p[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = part[((size_t)min(q0 + i, KS - 1) * T + t) * E + e];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (q0 + i < KS) v += p[i];
-    }
-    v += bv;
-    logits[(size_t)t * E + e] = v;
-  }
-  const uint64_t key = e < E ? order_key(v, e) : 0ull;  // lanes past E order after everything
-  lk[e] = key;
-  const int nc = (blockDim.x / 64) * k;  // candidate slots, k per wave
-  for (int i = e; i < nc; i += blockDim.x) ck[i] = 0ull;  // empty candidate: orders before nothing
-  __syncthreads();
-  // pass 1: rank inside the wave, two keys per LDS read
-  int r1 = 0;
-  const ulonglong2 *wk = reinterpret_cast<const ulonglong2 *>(lk + wave * 64);
-#pragma unroll 8
-  for (int o = 0; o < 32; ++o) {
-    const ulonglong2 q = wk[o];
-    r1 += (q.x > key) + (q.y > key);
-  }
-  if (e < E && r1 < k) ck[wave * k + r1] = key;
-  __syncthreads();
-  // pass 2: the candidates, one per thread of the first waves, ranked among
-  // themselves; the k best give their expert and logit
-  if (e < nc) {
-    const uint64_t ce = ck[e];
-    if (ce != 0ull) {
-      int r = 0;
-      const ulonglong2 *c2 = reinterpret_cast<const ulonglong2 *>(ck);
-      for (int i = 0; i < nc / 2; ++i) {  // two candidates per LDS read
-        const ulonglong2 q = c2[i];
-        r += (q.x > ce) + (q.y > ce);
-      }
-      if (nc & 1) r += ck[nc - 1] > ce;
-      if (r < k) {
-        top_v[r] = moe::key_logit(ce);
-        top_e[r] = moe::key_expert(ce);
-      }
-    }
-  }
-  __syncthreads();
-  // softmax of the k chosen logits
-  if (e < k) {
-    const float m = top_v[0];
-    float sum = 0.f;
-    for (int j = 0; j < k; ++j) sum += expf(top_v[j] - m);
-    idx[(size_t)t * k + e] = top_e[e];
-    w[(size_t)t * k + e] = expf(top_v[e] - m) / sum;
-  }
+  moe::finish_token(part, T, blockIdx.x, E, KS, bias, k, logits, idx, w);
 }
 
 }  // namespace
 
 namespace moe {
 
+hipError_t launch_router_partials(const moe_ctx *c, const float *x, int T, const float *wr, hipStream_t s) {
+  const int E = c->cfg.n_experts, d = c->cfg.d_model;
+  if (T > c->route_small_t) return hipErrorInvalidValue;
+  const int KS = c->route_ks;
+  const int n_tg = (T + 15) / 16;
+  hipLaunchKernelGGL(router_logits_mfma, dim3(n_tg * ((E + 15) / 16) * KS), dim3(64 * kRouteWaves), 0, s, x, T, d, wr,
+                     E, KS, c->route_part);
+  return hipGetLastError();
+}
+
 hipError_t launch_router(const moe_ctx *c, const float *x, int T, const float *wr, const float *bias, float *logits,
                          int32_t *idx, float *w, hipStream_t s) {
   const int E = c->cfg.n_experts, d = c->cfg.d_model, k = c->cfg.top_k;
   if (T <= c->route_small_t) {
-    const int KS = c->route_ks;
-    const int n_tg = (T + 15) / 16;
-    hipLaunchKernelGGL(router_logits_mfma, dim3(n_tg * ((E + 15) / 16) * KS), dim3(64 * kRouteWaves), 0, s, x, T, d,
-                       wr, E, KS, c->route_part);
-    hipLaunchKernelGGL(router_finish_small, dim3(T), dim3((E + 63) / 64 * 64), 0, s, c->route_part, T, E, KS, bias,
-                       k, logits, idx, w);
+    hipError_t e = launch_router_partials(c, x, T, wr, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(router_finish_small, dim3(T), dim3((E + 63) / 64 * 64), 0, s, c->route_part, T, E,
+                       c->route_ks, bias, k, logits, idx, w);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(router_logits_gemm, dim3((E + kGm - 1) / kGm, (T + kGm - 1) / kGm), dim3(256), 0, s, x, T, d, wr,

@@ -56,6 +56,9 @@ struct dim3 {
 struct uint4 {
   unsigned x, y, z, w;
 };
+struct ulonglong2 {
+  unsigned long long x, y;
+};
 
 typedef int hipError_t;
 enum { hipSuccess = 0, hipErrorInvalidValue = 1, hipErrorInvalidDevice = 101, hipErrorInvalidSymbol = 701 };

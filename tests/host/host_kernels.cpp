@@ -262,6 +262,77 @@ int run_resolve(char **a) {
   return 0;
 }
 
+// A capped decode layer's first single-workgroup launch for one or two
+// tokens: the router's top-k from given partial logits, then the resolve.
+// Input: bias [E] (float32 bits), then per call its layer and the partials
+// [KS][T][E].  Output per call: logits [T][E], idx [T][k], w [T][k], the
+// miss-list head and slot_of_pair; then the counters and the table.
+int run_route_resolve(char **a) {
+  const int L = std::atoi(a[0]), E = std::atoi(a[1]), S = std::atoi(a[2]), T = std::atoi(a[3]), k = std::atoi(a[4]);
+  const int KS = std::atoi(a[5]), calls = std::atoi(a[6]);
+  const char *in = a[7], *out = a[8];
+  const int n = T * k;
+  const size_t per_call = 1 + (size_t)KS * T * E;
+  std::vector<int32_t> iv = read_i32(in, (size_t)E + (size_t)calls * per_call);
+  moe_ctx c{};
+  c.cfg.d_model = 64;
+  c.cfg.d_ff = 64;
+  c.cfg.n_experts = E;
+  c.cfg.top_k = k;
+  c.cfg.n_layers = L;
+  c.cfg.n_slots = S;
+  c.cfg.max_tokens = T;
+  c.L = moe::make_layout(64, 64);
+  c.resident = false;
+  c.route_ks = KS;
+  c.route_small_t = T;
+  const Sizes z = ctx_sizes(T, k, E);
+  c.max_pairs = z.max_pairs;
+  const size_t ids = (size_t)L * E;
+  c.slot_of = exact<int32_t>(ids, 0xff);
+  c.id_of = exact<int32_t>(S, 0xff);
+  c.stamp = exact<uint32_t>(S, 0);
+  c.dstats = exact<int64_t>(8, 0);
+  c.dmiss = exact<int32_t>(3 + 2 * (size_t)z.max_pairs + 2 * (size_t)E, 0xa5);
+  c.route_part = exact<float>((size_t)KS * T * E, 0);
+  float *bias = exact<float>(E, 0);
+  std::memcpy(bias, iv.data(), (size_t)E * 4);
+  float *logits = exact<float>((size_t)T * E, 0xa5);
+  int32_t *idx = exact<int32_t>(n, 0xa5);
+  float *w = exact<float>(n, 0xa5);
+  int32_t *sop = exact<int32_t>(n, 0xa5);
+  Out o(out);
+  for (int call = 0; call < calls; ++call) {
+    const int32_t *rec = iv.data() + E + (size_t)call * per_call;
+    const int layer = rec[0];
+    if (layer < 0 || layer >= L) die("layer out of range");
+    std::memcpy(c.route_part, rec + 1, (size_t)KS * T * E * 4);
+    if (moe::launch_route_resolve(&c, layer, T, bias, logits, idx, w, sop, (hipStream_t) nullptr) != hipSuccess)
+      die("launch_route_resolve refused the shape");
+    o.put(reinterpret_cast<const int32_t *>(logits), (size_t)T * E);
+    o.put(idx, n);
+    o.put(reinterpret_cast<const int32_t *>(w), n);
+    o.put(c.dmiss, 3);
+    o.put(sop, n);
+  }
+  o.put(c.dstats, 6);
+  o.put(c.slot_of, ids);
+  o.put(c.id_of, S);
+  o.put(c.stamp, S);
+  std::free(c.slot_of);
+  std::free(c.id_of);
+  std::free(c.stamp);
+  std::free(c.dstats);
+  std::free(c.dmiss);
+  std::free(c.route_part);
+  std::free(bias);
+  std::free(logits);
+  std::free(idx);
+  std::free(w);
+  std::free(sop);
+  return 0;
+}
+
 // The bucketing launch of a resident decode layer, which also records the
 // lookup (as the resolve kernel does for a resident call).  Input: idx [T][k],
 // x [T][d] (float32 bits).
@@ -339,5 +410,6 @@ int main(int argc, char **argv) {
   if (mode == "noalloc" && argc == 7) return run_noalloc(argv + 2);
   if (mode == "resolve" && argc == 14) return run_resolve(argv + 2);
   if (mode == "bucket_lookup" && argc == 8) return run_bucket_lookup(argv + 2);
+  if (mode == "route_resolve" && argc == 11) return run_route_resolve(argv + 2);
   die("bad arguments");
 }

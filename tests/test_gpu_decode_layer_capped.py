@@ -4,7 +4,9 @@ the decode path -> moe_combine_norm) on a twin context over the same host
 store:
 
 * every output bit for bit, call after call, with misses, hits and
-  evictions; the same table, stamps and counters after every call;
+  evictions; the same table, stamps and counters after every call (one or
+  two tokens take the top-k and the resolve in one workgroup, more tokens
+  the router's own finishing kernel and the resolve kernel);
 * no fill kernel runs (the bucketing launch copies the misses in spare
   workgroups): every slot in use then holds its identity's blob, byte for byte
   up to the end of the last section, and later calls that hit those slots
@@ -88,8 +90,8 @@ def _slots_hold_blobs(ctx, host, used):
 
 
 @pytest.mark.parametrize("shape,T,S,calls,alpha", [
-    ("REAL", 1, 40, 14, 0.75), ("REAL", 4, 60, 10, 0.75), ("REAL", 5, 80, 8, 0.75), ("TINY", 1, 5, 30, 0.75),
-    ("TINY", 3, 7, 30, 0.75), ("TINY", 9, 16, 20, 0.0),
+    ("REAL", 1, 40, 14, 0.75), ("REAL", 2, 40, 12, 0.75), ("REAL", 4, 60, 10, 0.75), ("REAL", 5, 80, 8, 0.75),
+    ("TINY", 1, 5, 30, 0.75), ("TINY", 2, 6, 30, 0.0), ("TINY", 3, 7, 30, 0.75), ("TINY", 9, 16, 20, 0.0),
 ], ids=lambda v: str(v))
 def test_capped_layer_equals_separate_calls(shape, T, S, calls, alpha):
     s = REAL if shape == "REAL" else TINY

@@ -337,6 +337,52 @@ def test_resolve_resident_identity_map(exe, tmp_path):
     assert stats[:5].tolist() == [lookups, lookups, 0, len(calls), 0]
 
 
+@pytest.mark.parametrize("T", [1, 2])
+def test_route_resolve_one_workgroup(exe, tmp_path, T):
+    # a capped decode layer of one or two tokens: the router's top-k from the
+    # partial logits, token after token, then the resolve, in one workgroup of
+    # 1,024 threads -- logits bit for bit (slices summed in order, then the
+    # bias, in float32), idx the oracle's top-k of those logits (exact ties
+    # included), w its weights, slots and table the oracle LRU's
+    L, E, S, k, KS, calls = 3, 512, 40, 10, 8, 10
+    rng = np.random.default_rng(20 + T)
+    bias = (rng.normal(0.0, 1.0, E) + 2.0 * (np.arange(E) < 24)).astype(np.float32)  # a hot set: hits
+    bias[40:52] = bias[40]
+    parts = []
+    for c in range(calls):
+        p = rng.normal(0.0, 0.5, (KS, T, E)).astype(np.float32)
+        if c % 4 == 1:  # exact ties among the leaders: twelve experts with equal partials and bias
+            p[:, :, 40:52] = 1.5
+        parts.append(p)
+    recs = [bias.view(np.int32)]
+    for c, p in enumerate(parts):
+        recs += [np.int32(c % L).reshape(1), p.view(np.int32)]
+    out = _Reader(_run(exe, tmp_path, ["route_resolve", L, E, S, T, k, KS, calls], recs))
+    orc = oracle.LRUCache(L, E, S)
+    for c, p in enumerate(parts):
+        logits = out.take(T * E, np.float32).reshape(T, E)
+        idx = out.take(T * k).reshape(T, k)
+        w = out.take(T * k, np.float32).reshape(T, k)
+        dm, sop = out.take(3), out.take(T * k)
+        want = np.zeros((T, E), np.float32)
+        for q in range(KS):
+            want = want + p[q]
+        want = want + bias
+        assert np.array_equal(logits.view(np.int32), want.view(np.int32)), c
+        idx_o, w_o = oracle.topk_from_logits(want.astype(np.float64), k)
+        assert np.array_equal(idx, idx_o), (c, idx, idx_o)
+        assert np.allclose(w, w_o, rtol=1e-6, atol=1e-7), c
+        so, misses = orc.resolve(c % L, idx.reshape(-1))
+        assert dm.tolist() == [len(np.unique(idx)), len(misses), 0] and np.array_equal(sop, so.reshape(-1)), c
+    stats = out.take(6, np.int64)
+    slot_of, id_of, stamp = out.take(L * E), out.take(S), out.take(S, np.uint32)
+    out.done()
+    assert stats.tolist() == [orc.lookups, orc.hits, orc.misses, calls, 0, orc.clock]
+    assert slot_of.tolist() == orc.slot_of and id_of.tolist() == orc.id_of.tolist()
+    assert stamp.tolist() == orc.stamp.tolist()
+    assert orc.hits > 0 and orc.misses > 0
+
+
 @pytest.mark.slow
 def test_resolve_more_slots_than_threads(exe, tmp_path):
     # 1,100 slots: the victim search strides past the workgroup's 1,024
