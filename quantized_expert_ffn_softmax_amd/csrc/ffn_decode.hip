@@ -330,7 +330,7 @@ struct WordSrc {
 
 template <int NSB, int NMAT, int S>
 __device__ inline void load_words(const WordSrc<NSB, NMAT> &Src, uint4 (&W)[NSB][NMAT]) {
-  // only a range's last superblock can lie past the row (a shorter second half)
+  // only a range's last superblock can lie past the row (a shorter range)
   const uint32_t so = S + 1 < NSB ? (uint32_t)S * 64 : (uint32_t)min(S, Src.nvalid - 1) * 64;
 #pragma unroll
   for (int mat = 0; mat < NMAT; ++mat) W[S][mat] = *reinterpret_cast<const uint4 *>(Src.blob + (Src.off[mat] + so));
@@ -353,25 +353,30 @@ __device__ inline void refill(uint4 (&W)[NSB][NMAT], const WordSrc<NSB, NMAT> &S
 
 // superblocks S and S + 1 together, their steps interleaved (twice the
 // independent dequantise-and-MFMA chains per wave); a last odd superblock
-// alone
-template <int NSB, int NMAT, int COLS, int S>
+// alone.  With SHORT (quarters of K, ranges one superblock shorter than NSB
+// after the first) the last pair may hold one superblock only: a uniform
+// branch, and every scale block index is clamped to the row.
+template <int NSB, int NMAT, int COLS, bool SHORT, int S>
 __device__ inline void compute_pair(uint4 (&W)[NSB][NMAT], const WordSrc<NSB, NMAT> &Src,
                                     const uint8_t *(&srow)[NMAT], int g, int nblk, const uint32_t (&sel)[6],
                                     const Consts &K, const uint8_t *xb, f4 &acc0, f4 &acc1, f4 &acc2, f4 &acc3) {
   // g carries the range's first scale block: block 5 S + g of the range
   if constexpr (S + 1 >= NSB) {
-    if (S >= Src.nvalid) return;  // a second half one superblock shorter (uniform)
+    if (S >= Src.nvalid) return;  // a range one superblock shorter (uniform)
   }
   MatSb M[NMAT];
 #pragma unroll
-  for (int mat = 0; mat < NMAT; ++mat) M[mat] = mat_sb<S + 2 >= NSB>(W[S][mat], srow[mat], 5 * S + g, nblk, sel);
+  for (int mat = 0; mat < NMAT; ++mat)
+    M[mat] = mat_sb<(S + 2 >= NSB || SHORT)>(W[S][mat], srow[mat], 5 * S + g, nblk, sel);
   refill<NSB, NMAT, S>(W, Src);
   const uint8_t *xs = xb + S * Cols<COLS>::kSbBytes;
-  if constexpr (S + 1 < NSB) {
+  bool two = S + 1 < NSB;
+  if constexpr (SHORT && S + 2 == NSB) two = S + 1 < Src.nvalid;
+  if (two) {
     MatSb M2[NMAT];
 #pragma unroll
     for (int mat = 0; mat < NMAT; ++mat)
-      M2[mat] = mat_sb<S + 3 >= NSB>(W[S + 1][mat], srow[mat], 5 * (S + 1) + g, nblk, sel);
+      M2[mat] = mat_sb<(S + 3 >= NSB || SHORT)>(W[(S + 1) % NSB][mat], srow[mat], 5 * (S + 1) + g, nblk, sel);
     refill<NSB, NMAT, S + 1>(W, Src);
     const uint8_t *xs2 = xs + Cols<COLS>::kSbBytes;
     sb_step<NMAT, 0, COLS>(M, K, xs, acc0, acc1);
@@ -393,19 +398,23 @@ __device__ inline void compute_pair(uint4 (&W)[NSB][NMAT], const WordSrc<NSB, NM
   }
 }
 
-template <int NSB, int NMAT, int COLS, int... Ps>
+template <int NSB, int NMAT, int COLS, bool SHORT, int... Ps>
 __device__ inline void compute_all(std::integer_sequence<int, Ps...>, uint4 (&W)[NSB][NMAT],
                                    const WordSrc<NSB, NMAT> &Src, const uint8_t *(&srow)[NMAT], int g, int nblk,
                                    const uint32_t (&sel)[6], const Consts &K, const uint8_t *xb, f4 &acc0, f4 &acc1,
                                    f4 &acc2, f4 &acc3) {
-  (compute_pair<NSB, NMAT, COLS, 2 * Ps>(W, Src, srow, g, nblk, sel, K, xb, acc0, acc1, acc2, acc3), ...);
+  (compute_pair<NSB, NMAT, COLS, SHORT, 2 * Ps>(W, Src, srow, g, nblk, sel, K, xb, acc0, acc1, acc2, acc3), ...);
 }
 
 // KS = 2 (gate/up of small batches): K split in two halves over the waves of a
 // workgroup -- waves 2h + l take tile l of the unit's 2 tiles and superblocks
 // [h H, min((h + 1) H, NSB)) with H = ceil(NSB / 2) -- and the halves' sums
 // added through LDS before the epilogue.  Twice the waves in flight and half
-// the chain per wave, for batches whose units leave CUs idle.
+// the chain per wave, for batches whose units leave CUs idle.  KS = 4 (the
+// smallest batches, whose quarter units all fit in the CUs at once): one tile
+// per unit, wave q takes NSB / 4 superblocks, one more for the first NSB mod 4
+// waves (13 = 4 + 3 + 3 + 3: only a range's last pair can be short), and
+// wave 0 adds the other three quarters' sums in order.
 // workgroups per CU the kernel is built for: gate/up 3; down 4 up to 6
 // superblocks (the model's d_ff = 768 is 5), then what its registers allow
 // on entries of 8 tokens (3 up to 9 superblocks, 2 beyond)
@@ -416,21 +425,26 @@ constexpr int decode_min_blocks() {
 
 template <int NSB, int NMAT, int KS, int COLS>
 __global__ void __launch_bounds__(64 * kWaves, (decode_min_blocks<NSB, NMAT>())) ffn_decode_kernel(DecodeParams P) {
-  static_assert(KS == 1 || (NMAT == 2 && ((NSB + 1) / 2) % 2 == 1), "K split: gate/up, an odd half length");
+  static_assert(KS == 1 || (NMAT == 2 && (KS == 4 || ((NSB + 1) / 2) % 2 == 1)),
+                "K split: gate/up; halves of an odd length, or quarters");
   static_assert(COLS == 4 || COLS == 8, "entries of 4 or 8 tokens");
-  constexpr int NS = KS == 2 ? (NSB + 1) / 2 : NSB;  // superblocks of a wave's range
-  constexpr int kTiles = kWaves / KS;                 // 16-row tiles of a unit
+  static_assert(KS != 4 || (NSB % 4 <= 1 && NSB >= 8), "quarters: a first range at most one longer");
+  constexpr int NS = (NSB + KS - 1) / KS;  // superblocks of a wave's range (the longest)
+  constexpr bool SHORT = KS == 4;
+  constexpr int kTiles = kWaves / KS;      // 16-row tiles of a unit
   constexpr int kActBytes = NSB * Cols<COLS>::kSbBytes;
   constexpr int kScMat = 16 * kTiles * sc_pitch(5 * NSB + 8);  // one matrix's scales of the unit's rows (nblk <= 5 NSB)
   constexpr int kScBytes = NMAT * kScMat;
   __shared__ __attribute__((aligned(1024))) uint8_t lact[kActBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t lsc[(kScBytes + 4095) / 4096 * 4096];
-  __shared__ f4 red[KS == 2 ? kTiles * 64 * 2 : 1];
+  __shared__ f4 red[KS == 1 ? 1 : (KS - 1) * kTiles * 64 * 2];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
-  const int ltile = KS == 2 ? (w & 1) : w;                                 // tile of the unit
-  const int half = KS == 2 ? __builtin_amdgcn_readfirstlane(w >> 1) : 0;  // range (uniform per wave)
-  const int sb0 = half * NS;
+  const int ltile = KS == 1 ? w : w % kTiles;                                    // tile of the unit
+  const int half = KS == 1 ? 0 : __builtin_amdgcn_readfirstlane(w / kTiles);  // range (uniform per wave)
+  // the wave's range: superblocks [sb0, sb0 + nvalid) of the row
+  const int sb0 = KS == 4 ? half * (NSB / 4) + min(half, NSB % 4) : half * NS;
+  const int nvalid = KS == 4 ? NSB / 4 + (half < NSB % 4 ? 1 : 0) : min(NS, NSB - sb0);
   const Mats<NMAT> Mt = mats_of<NMAT>(P);
   const int ntile = Mt.m[0].rows / 16;
   const int tpu = (ntile + kTiles - 1) / kTiles;
@@ -464,7 +478,7 @@ __global__ void __launch_bounds__(64 * kWaves, (decode_min_blocks<NSB, NMAT>()))
     const int row = min((U.tile0 + ltile) * 16 + r16, Mt.m[0].rows - 1);
     WordSrc<NS, NMAT> Src;
     Src.blob = U.blob;
-    Src.nvalid = min(NS, NSB - sb0);
+    Src.nvalid = nvalid;
 #pragma unroll
     for (int mat = 0; mat < NMAT; ++mat)
       Src.off[mat] = Mt.m[mat].code_off + (uint32_t)row * Mt.m[mat].wpr * 4 + g * 16 + sb0 * 64;
@@ -480,7 +494,7 @@ __global__ void __launch_bounds__(64 * kWaves, (decode_min_blocks<NSB, NMAT>()))
     for (int mat = 0; mat < NMAT; ++mat)
       srow[mat] = lsc + mat * kScMat + (ltile * 16 + r16) * sc_pitch(nblk);
     f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f}, acc2 = acc0, acc3 = acc0;
-    compute_all<NS, NMAT, COLS>(std::make_integer_sequence<int, (NS + 1) / 2>{}, W, Src, srow, 5 * sb0 + g, nblk,
+    compute_all<NS, NMAT, COLS, SHORT>(std::make_integer_sequence<int, (NS + 1) / 2>{}, W, Src, srow, 5 * sb0 + g, nblk,
                                 sel, K, xb, acc0, acc1, acc2, acc3);
     acc0 += acc2;
     acc1 += acc3;
@@ -494,6 +508,19 @@ __global__ void __launch_bounds__(64 * kWaves, (decode_min_blocks<NSB, NMAT>()))
       if (half == 1) continue;
       acc0 += red[(ltile * 64 + lane) * 2 + 0];
       acc1 += red[(ltile * 64 + lane) * 2 + 1];
+    } else if constexpr (KS == 4) {
+      // quarters 1..3 -> LDS; quarter 0 adds them in order (fixed order: q0 + q1 + q2 + q3)
+      if (half != 0) {
+        red[((half - 1) * 64 + lane) * 2 + 0] = acc0;
+        red[((half - 1) * 64 + lane) * 2 + 1] = acc1;
+      }
+      __syncthreads();
+      if (half != 0) continue;
+#pragma unroll
+      for (int q = 0; q < 3; ++q) {
+        acc0 += red[(q * 64 + lane) * 2 + 0];
+        acc1 += red[(q * 64 + lane) * 2 + 1];
+      }
     }
     unit_epilogue<NMAT, COLS>(P, U, ltile, lane, acc0, acc1);
   }
@@ -583,12 +610,13 @@ struct OccMat {
 namespace moe {
 
 hipError_t decode_occupancy(moe_ctx *c) {
-  c->decode_occ[0] = c->decode_occ[1] = c->decode_occ[2] = 1;
+  c->decode_occ[0] = c->decode_occ[1] = c->decode_occ[2] = c->decode_occ[3] = 1;
   // widths the decode kernels are not built for take the prefill path only
   if (c->L.gate.nsb > kDecodeMaxNsb || c->L.down.nsb > kDecodeMaxNsb) return hipSuccess;
   hipError_t e = by_nsb<OccMat<2>::F>(c->L.gate.nsb, &c->decode_occ[0]);
   if (e == hipSuccess) e = by_nsb<OccMat<1>::F>(c->L.down.nsb, &c->decode_occ[1]);
   if (e == hipSuccess && c->L.gate.nsb == 13) e = occupancy_nsb<13, 2, 2>(&c->decode_occ[2]);
+  if (e == hipSuccess && c->L.gate.nsb == 13) e = occupancy_nsb<13, 2, 4>(&c->decode_occ[3]);
   return e;
 }
 
@@ -650,9 +678,15 @@ hipError_t launch_ffn_decode_kernels(const moe_ctx *c, int layer, int T, const i
   // to 32 tokens the split is also ahead on average (half-length chains in
   // twice the waves; at 15 tokens 51.4 -> 50.2 us per call).
   // Built for the 13-superblock rows of d_model = 1,921..2,080.
+  // A batch whose quarter-K units (one tile each) all fit in the workgroups
+  // the CUs hold at once -- a single token's ~11 entries -- splits K in four.
   if (T <= kSplitMaxTokens && c->L.gate.nsb == 13) {
     const int u1s = ents * ((k.d_ff / 16 + kWaves / 2 - 1) / (kWaves / 2));
-    e = launch_decode_nsb<13, 2, 2>(P, u1s, c->decode_occ[2], c->n_cu, s);
+    const int u1q = ents * (k.d_ff / 16);
+    if (u1q <= c->decode_occ[3] * c->n_cu)
+      e = launch_decode_nsb<13, 2, 4>(P, u1q, c->decode_occ[3], c->n_cu, s);
+    else
+      e = launch_decode_nsb<13, 2, 2>(P, u1s, c->decode_occ[2], c->n_cu, s);
   } else {
     e = by_nsb<LaunchMat<2>::F>(c->L.gate.nsb, &P, u1, c->decode_occ[0], c->n_cu, s);
   }

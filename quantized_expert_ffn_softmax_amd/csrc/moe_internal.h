@@ -126,7 +126,7 @@ struct moe_ctx {
   int32_t max_work8;
   int32_t n_chunks_max;
   int32_t n_cu;          // compute units of the context's device
-  int32_t decode_occ[3]; // decode FFN workgroups per CU: gate/up, down, gate/up K-split (queried at create)
+  int32_t decode_occ[4]; // decode FFN workgroups per CU: gate/up, down, gate/up K in halves, in quarters (at create)
 
   // miss path
   int32_t *dmiss;        // device: [0]=unique, [1]=misses, [2]=error, then (id, slot) pairs

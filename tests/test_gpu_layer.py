@@ -148,6 +148,16 @@ def test_block_scale_range_edges(path, scales):
     layer.close()
 
 
+@pytest.mark.parametrize("T,alpha", [(1, 0.0), (1, 0.75), (2, 0.75)])
+def test_real_layer_decode_small_batches(T, alpha):
+    # one token: gate/up's ~11 entries x 48 one-tile units fit in the CUs at
+    # once, so K is split in four (13 = 4 + 3 + 3 + 3 superblocks); two tokens
+    # take the halves
+    layer = _layer(seed=11 + T, T=T, alpha=alpha, **REAL)
+    _check_layer(layer, B.MOE_PATH_DECODE, "fp16_weights", 1e-4)
+    layer.close()
+
+
 def test_real_layer_decode_T5():
     layer = _layer(T=5, **REAL)
     _check_layer(layer, B.MOE_PATH_DECODE, "fp16_weights", 1e-4)
