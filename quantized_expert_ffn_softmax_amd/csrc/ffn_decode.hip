@@ -309,6 +309,32 @@ __device__ inline void unit_epilogue(const DecodeParams &P, const Unit &U, int w
   }
 }
 
+// gate/up of a K-split unit: the wave's two rows i0, i0 + 1 of its four (the
+// two halves of K finalise two rows each), the same arithmetic per row as above
+template <int COLS>
+__device__ inline void gateup_rows(const DecodeParams &P, const Unit &U, int w, int lane, int i0, float g0, float g1,
+                                   float u0, float u1) {
+  const int r16 = lane & 15, g = lane >> 4;
+  const int rt = U.tile0 + w;
+  g0 += __shfl_xor(g0, COLS, 64);
+  g1 += __shfl_xor(g1, COLS, 64);
+  u0 += __shfl_xor(u0, COLS, 64);
+  u1 += __shfl_xor(u1, COLS, 64);
+  if (!(U.has_tok && r16 < COLS && rt * 16 < P.d_ff)) return;
+  uint16_t *hr = P.hrec + (size_t)U.rrow * P.hrec_h;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float gv = j ? g1 : g0, uv = j ? u1 : u0;
+    float inv_f;
+    const int pos = rec_pos(rt * 16 + 4 * g + i0 + j, inv_f);
+    const float h = gv / (1.0f + __expf(-gv)) * uv * inv_f;
+    const _Float16 hi = (_Float16)h;
+    const _Float16 lo = (_Float16)(h - (float)hi);
+    hr[pos] = __builtin_bit_cast(uint16_t, hi);
+    hr[pos + 8] = __builtin_bit_cast(uint16_t, lo);
+  }
+}
+
 // word quads of superblocks issued up front; the rest is requested as the
 // registers of superblock S - depth free up (gate/up keeps 9 superblocks of
 // two matrices in flight within the register budget of 3 waves per SIMD)
@@ -437,7 +463,7 @@ __global__ void __launch_bounds__(64 * kWaves, (decode_min_blocks<NSB, NMAT>()))
   constexpr int kScBytes = NMAT * kScMat;
   __shared__ __attribute__((aligned(1024))) uint8_t lact[kActBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t lsc[(kScBytes + 4095) / 4096 * 4096];
-  __shared__ f4 red[KS == 1 ? 1 : (KS - 1) * kTiles * 64 * 2];
+  __shared__ f4 red[KS == 1 ? 1 : (KS == 2 ? 2 * kTiles * 64 : 3 * 64 * 2)];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
   const int ltile = KS == 1 ? w : w % kTiles;                                    // tile of the unit
@@ -499,15 +525,19 @@ __global__ void __launch_bounds__(64 * kWaves, (decode_min_blocks<NSB, NMAT>()))
     acc0 += acc2;
     acc1 += acc3;
     if constexpr (KS == 2) {
-      // second half -> LDS; the first half adds it (fixed order: first + second)
-      if (half == 1) {
-        red[(ltile * 64 + lane) * 2 + 0] = acc0;
-        red[(ltile * 64 + lane) * 2 + 1] = acc1;
-      }
+      // each half finalises two of the lane's four rows (2 h, 2 h + 1) and
+      // writes its partial sums of the other two through LDS; a row is the
+      // sum of the two halves' partials (one addition: the same value in
+      // either order)
+      const f4 mine = half == 0 ? f4{acc0[2], acc0[3], acc1[2], acc1[3]} : f4{acc0[0], acc0[1], acc1[0], acc1[1]};
+      red[(half * kTiles + ltile) * 64 + lane] = mine;
       __syncthreads();
-      if (half == 1) continue;
-      acc0 += red[(ltile * 64 + lane) * 2 + 0];
-      acc1 += red[(ltile * 64 + lane) * 2 + 1];
+      const f4 r = red[((1 - half) * kTiles + ltile) * 64 + lane];
+      if (half == 0)
+        gateup_rows<COLS>(P, U, ltile, lane, 0, acc0[0] + r[0], acc0[1] + r[1], acc1[0] + r[2], acc1[1] + r[3]);
+      else
+        gateup_rows<COLS>(P, U, ltile, lane, 2, acc0[2] + r[0], acc0[3] + r[1], acc1[2] + r[2], acc1[3] + r[3]);
+      continue;
     } else if constexpr (KS == 4) {
       // quarters 1..3 -> LDS; quarter 0 adds them in order (fixed order: q0 + q1 + q2 + q3)
       if (half != 0) {
