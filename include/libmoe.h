@@ -207,7 +207,8 @@ moe_status moe_combine(moe_ctx *ctx, const float *y_pairs, const float *w,
  * 如何做到：三层存储); the missed blobs are copied from the mapped host store
  * as moe_cache_resolve_async's fill kernel copies them, but by spare
  * workgroups of the bucketing launch, which does not depend on the resolve:
- * seven launches instead of the separate calls' eight.  A call that cannot
+ * seven launches instead of the separate calls' eight, and six for one or
+ * two tokens, whose top-k and resolve share one workgroup.  A call that cannot
  * pin its working set changes nothing in the table, counts one failed call
  * and leaves its pairs' y_pairs rows unwritten (out is then not
  * meaningful).
