@@ -282,8 +282,8 @@ def bench_stack(ctx, routers, biases, seed, d, f, L, T, W, K, use_graph, peaks):
     # six of moe_decode_layer (the headline)
     spread = {}
 
-    def graph_time(fn):
-        xin = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    def graph_time(fn, xs=xs, Tn=T):
+        xin = torch.empty((Tn, d), dtype=torch.float32, device="cuda")
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -321,6 +321,35 @@ def bench_stack(ctx, routers, biases, seed, d, f, L, T, W, K, use_graph, peaks):
         graph_ms = graph_time(step_fused)
         log(f"[bench] decode stack (graph, moe_decode_layer, 6 launches/layer): {graph_ms:.3f} ms/step, "
             f"{T / (graph_ms * 1e-3):.0f} tok/s")
+        fused_spread = dict(spread)
+        # one token per step through the same resident layers: where launch
+        # gaps weigh most (moe_decode_layer: five launches per layer at T = 1)
+        b1 = ctx.buffers(1)
+        x1 = [torch.empty((1, d), dtype=torch.float32, device="cuda") for _ in range(2)]
+        xs1 = [torch.from_numpy(moe_synth.gen_x(seed, 700000 + s_, 1, d)).cuda() for s_ in range(W + K)]
+
+        def step1(x0, fused):
+            x = x0
+            for l in range(L):
+                xn = x1[l % 2]
+                if fused:
+                    B.moe_decode_layer(c, l, x, 1, routers[l], biases[l], None, b1["idx"], b1["w"], b1["y_pairs"],
+                                       b1["y_shared"], b1["out"], xn)
+                else:
+                    B.moe_route(c, l, x, 1, routers[l], biases[l], None, b1["idx"], b1["w"])
+                    B.moe_cache_resolve(c, l, b1["idx"], 1, None)
+                    B.moe_expert_ffn(c, l, x, 1, b1["idx"], None, b1["y_pairs"], b1["y_shared"], B.MOE_PATH_DECODE)
+                    B.moe_combine_norm(c, b1["y_pairs"], b1["w"], b1["y_shared"], 1, b1["out"], xn)
+                x = xn
+
+        t1_sep = graph_time(lambda x0: step1(x0, False), xs1, 1)
+        t1_fused = graph_time(lambda x0: step1(x0, True), xs1, 1)
+        t1 = {"tokens_per_step": 1, "ms_per_step": round(t1_fused, 4), "tok_per_s": round(1 / (t1_fused * 1e-3), 1),
+              "launches_per_layer": 5, "separate_calls_ms_per_step": round(t1_sep, 4),
+              "separate_calls_tok_per_s": round(1 / (t1_sep * 1e-3), 1), "mode": "hip_graph, resident"}
+        log(f"[bench] decode stack at T=1 (graph): moe_decode_layer (5 launches/layer) {t1_fused:.3f} ms/step "
+            f"= {t1['tok_per_s']} tok/s; separate calls (7 launches/layer) {t1_sep:.3f} ms/step")
+        spread = fused_spread
     ms_per_step = graph_ms if graph_ms is not None else eager_ms
     roof = {"bound": "hbm", "kernel": "moe_expert_ffn (decode path)",
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -343,6 +372,7 @@ def bench_stack(ctx, routers, biases, seed, d, f, L, T, W, K, use_graph, peaks):
     if sep_graph_ms is not None:
         res["separate_calls_graph_ms_per_step"] = round(sep_graph_ms, 4)
         res["separate_calls_ms_per_step_spread"] = sep_spread["graph_ms"]
+        res["decode_stack_T1"] = t1
         res["separate_calls_tok_per_s"] = round(T / (sep_graph_ms * 1e-3), 1)
     return res
 

@@ -184,7 +184,8 @@ moe_status moe_combine(moe_ctx *ctx, const float *y_pairs, const float *w,
                        const float *y_shared, int32_t T, float *out, void *stream);
 
 /* One whole decode layer; on a resident cache in six launches instead of the
- * seven of the separate calls (the pages' engine has a fused-kernel mode,
+ * seven of the separate calls (five for one or two tokens, whose top-k joins
+ * the bucketing launch) (the pages' engine has a fused-kernel mode,
  * "融合核": "从一张到四张 RTX 4090 ...", section 调参：前后 40 多次重启):
  * the router's two launches; one launch for the resident lookup count, the
  * bucketing and the activation record; the two FFN kernels; the combine

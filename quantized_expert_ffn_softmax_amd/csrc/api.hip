@@ -424,8 +424,15 @@ extern "C" moe_status moe_decode_layer(moe_ctx *c, int32_t layer, const float *x
   float *lg = logits ? logits : c->logits_ws;
   hipError_t e = hipSuccess;
   if (c->resident) {
-    e = moe::launch_router(c, x, T, w_router, bias, lg, idx, w, s);
-    if (e == hipSuccess) e = moe::launch_bucket_lookup(c, idx, T, moe::kEntryTokens, x, c->xrec, xh, s);
+    // one or two tokens: the top-k joins the bucketing launch (five launches)
+    if (T <= 2 && T <= c->route_small_t) {
+      e = moe::launch_router_partials(c, x, T, w_router, s);
+      if (e == hipSuccess)
+        e = moe::launch_route_bucket_lookup(c, T, bias, lg, idx, w, moe::kEntryTokens, x, c->xrec, xh, s);
+    } else {
+      e = moe::launch_router(c, x, T, w_router, bias, lg, idx, w, s);
+      if (e == hipSuccess) e = moe::launch_bucket_lookup(c, idx, T, moe::kEntryTokens, x, c->xrec, xh, s);
+    }
     if (e == hipSuccess) e = moe::launch_ffn_decode_kernels(c, layer, T, nullptr, y_pairs, y_shared, s);
   } else {
     // capped: the router and the resolve (for one or two tokens the top-k

@@ -7,6 +7,7 @@
 #include "device_util.h"
 #include "moe_internal.h"
 #include "record.h"
+#include "topk_small.h"
 
 namespace {
 
@@ -209,6 +210,44 @@ __global__ void __launch_bounds__(kBucketThreads) bucket_small(const int32_t *__
   }
 }
 
+// A resident decode layer of one or two tokens: workgroup 0 finishes the
+// router's top-k of each token from its partial logits (topk_small.h, as the
+// router's own finishing kernel does with one workgroup per token), then
+// buckets the pairs it has just written and records the lookup, as
+// bucket_small does with stats; the other workgroups build the x record,
+// which does not depend on the routing.  One launch where the separate steps
+// make two.
+__global__ void __launch_bounds__(kBucketThreads) route_bucket_small(
+    const float *__restrict__ part, int KS, const float *__restrict__ bias, int k, float *__restrict__ logits,
+    int32_t *__restrict__ idx, float *__restrict__ w, int E, int T, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ perm, int entry_m, moe::WorkEntry *work, int32_t *n_work, const float *__restrict__ x, int d,
+    int nsb, uint16_t *__restrict__ xrec, int xrec_h, int xrec_blocks, int32_t *__restrict__ dmiss,
+    int64_t *__restrict__ stats, moe::WorkEntry *work8) {
+  if (blockIdx.x > 0) {
+    moe::build_xrec_range(x, T, d, nsb, xrec, xrec_h, (blockIdx.x - 1) * blockDim.x + threadIdx.x,
+                          xrec_blocks * blockDim.x);
+    return;
+  }
+  for (int t = 0; t < T; ++t) {
+    moe::finish_token(part, T, t, E, KS, bias, k, logits, idx, w);
+    __syncthreads();  // the top-k's LDS is reused by the next token
+  }
+  __threadfence_block();  // idx, written by the top-k's first k threads, read by every thread below
+  __shared__ int nuniq_sh;
+  if (threadIdx.x == 0) nuniq_sh = 0;
+  __syncthreads();
+  bucket_block(idx, T * k, E, T, offsets, perm, 1, entry_m, work, n_work, &nuniq_sh, work8);
+  if (threadIdx.x == 0) {
+    const int nu = nuniq_sh;
+    dmiss[0] = nu;
+    dmiss[1] = 0;
+    dmiss[2] = 0;
+    atomicAdd(reinterpret_cast<unsigned long long *>(stats + 0), (unsigned long long)nu);
+    atomicAdd(reinterpret_cast<unsigned long long *>(stats + 1), (unsigned long long)nu);
+    atomicAdd(reinterpret_cast<unsigned long long *>(stats + 3), 1ull);
+  }
+}
+
 // Multi-block path, phase 1: per-chunk histograms chunk_cnt[chunk][E].
 __global__ void __launch_bounds__(kChunk) bucket_hist(const int32_t *__restrict__ idx, int n, int E,
                                                       int32_t *__restrict__ chunk_cnt) {
@@ -320,6 +359,19 @@ hipError_t launch_bucket_lookup(const moe_ctx *c, const int32_t *idx, int T, int
   hipLaunchKernelGGL(bucket_small, dim3(1 + xb), dim3(nt), 0, s, idx, n, E, T, c->offsets_ws, c->perm_ws, 1, entry_m,
                      c->work, c->n_work, x, c->cfg.d_model, c->L.gate.nsb, xrec, xrec_h, xb, c->dmiss, c->dstats,
                      c->work8, moe::FillArgs{});
+  return hipGetLastError();
+}
+
+hipError_t launch_route_bucket_lookup(const moe_ctx *c, int T, const float *bias, float *logits, int32_t *idx, float *w,
+                                     int entry_m, const float *x, uint16_t *xrec, int xrec_h, hipStream_t s) {
+  const int E = c->cfg.n_experts, k = c->cfg.top_k, n = T * k;
+  if (!c->resident || T < 1 || T > 2 || T > c->route_small_t || n > kSmallMax || E > 1024) return hipErrorInvalidValue;
+  // the top-k needs a thread per expert, the bucketing one per pair and per expert
+  const int nt = ((n > E ? n : E) + 63) / 64 * 64;
+  const int xb = (T * c->L.gate.nsb * moe::kSteps * 8 + nt - 1) / nt;
+  hipLaunchKernelGGL(route_bucket_small, dim3(1 + xb), dim3(nt), 0, s, c->route_part, c->route_ks, bias, k, logits,
+                     idx, w, E, T, c->offsets_ws, c->perm_ws, entry_m, c->work, c->n_work, x, c->cfg.d_model,
+                     c->L.gate.nsb, xrec, xrec_h, xb, c->dmiss, c->dstats, c->work8);
   return hipGetLastError();
 }
 

@@ -185,6 +185,10 @@ hipError_t launch_ffn_decode_kernels(const moe_ctx *c, int layer, int T, const i
 // T * top_k <= 1024, n_experts <= 1024
 hipError_t launch_bucket_lookup(const moe_ctx *c, const int32_t *idx, int T, int entry_m, const float *x,
                                 uint16_t *xrec, int xrec_h, hipStream_t s);
+// resident cache, T <= 2: the router's top-k from c->route_part, the lookup
+// count, the bucketing with its work lists and the x record, in one launch
+hipError_t launch_route_bucket_lookup(const moe_ctx *c, int T, const float *bias, float *logits, int32_t *idx, float *w,
+                                     int entry_m, const float *x, uint16_t *xrec, int xrec_h, hipStream_t s);
 // the zero-copy fill's arguments for c's cache, `chunks` workgroups per blob
 FillArgs fill_args(const moe_ctx *c, int chunks);
 // capped cache: the bucketing with its work lists, the x record (with x) and,

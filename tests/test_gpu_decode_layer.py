@@ -1,6 +1,7 @@
 """moe_decode_layer -- a whole decode layer on a resident cache in six
-launches (the capped cache: test_gpu_decode_layer_capped.py) -- against the
-seven-launch sequence of separate calls it replaces
+launches, five for one or two tokens (the capped cache:
+test_gpu_decode_layer_capped.py) -- against the seven-launch sequence of
+separate calls it replaces
 (moe_route -> moe_cache_resolve -> moe_expert_ffn on the decode path ->
 moe_combine_norm / moe_combine), through the C ABI: every output bit for bit,
 the cumulative counters equal, at the real shape (T = 1 .. 64) and small ones
@@ -63,7 +64,8 @@ def _fresh(buf):
 
 
 @pytest.mark.parametrize("shape,T,opts", [
-    ("REAL", 15, "logits,bias,norm"), ("REAL", 1, "norm"), ("REAL", 5, "bias,norm"),
+    ("REAL", 15, "logits,bias,norm"), ("REAL", 1, "norm"), ("REAL", 2, "logits,bias,norm"), ("REAL", 5, "bias,norm"),
+    ("TINY", 1, "logits,bias,norm"), ("TINY", 2, "bias"),
     ("REAL", 28, "logits,bias"), ("REAL", 64, "bias,norm"), ("TINY", 9, "logits,bias,norm"),
     ("TINY", 40, "bias"), ("TINY", 300, "logits,bias,norm"),
 ], ids=lambda v: str(v))
@@ -93,9 +95,10 @@ def test_fused_layer_equals_separate_calls(shape, T, opts):
     b.close()
 
 
-def test_fused_stack_in_graph_equals_eager_separate():
+@pytest.mark.parametrize("T", [15, 1])
+def test_fused_stack_in_graph_equals_eager_separate(T):
     d, f, E, k = REAL["d"], REAL["f"], REAL["E"], REAL["k"]
-    L, T = 6, 15
+    L = 6
     say(f"  {L}-layer stack, T={T}: fused layers in a HIP graph against eager separate calls")
     g, e = _ctx(d, f, E, k, L, T), _ctx(d, f, E, k, L, T)
     wr, bias, _ = _inputs(d, E, L, T, seed=6, alpha=0.75)
