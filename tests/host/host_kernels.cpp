@@ -335,12 +335,15 @@ int run_route_resolve(char **a) {
 
 // The bucketing launch of a resident decode layer, which also records the
 // lookup (as the resolve kernel does for a resident call).  Input: idx [T][k],
-// x [T][d] (float32 bits).
-int run_bucket_lookup(char **a) {
+// x [T][d] (float32 bits).  With KS > 0 (T <= 2) the launch also finishes the
+// router's top-k: the input is then bias [E], partial logits [KS][T][E] and x,
+// and the output starts with logits [T][E], idx [T][k] and w [T][k].
+int run_bucket_lookup(char **a, int KS) {
   const int E = std::atoi(a[0]), T = std::atoi(a[1]), k = std::atoi(a[2]), d = std::atoi(a[3]);
   const char *in = a[4], *out = a[5];
   const int n = T * k;
-  std::vector<int32_t> iv = read_i32(in, (size_t)n + (size_t)T * d);
+  const size_t head = KS > 0 ? (size_t)E + (size_t)KS * T * E : (size_t)n;
+  std::vector<int32_t> iv = read_i32(in, head + (size_t)T * d);
   moe_ctx c{};
   c.cfg.n_experts = E;
   c.cfg.top_k = k;
@@ -354,10 +357,18 @@ int run_bucket_lookup(char **a) {
   const Sizes z = ctx_sizes(T, k, E);
   c.max_pairs = z.max_pairs;
   c.max_work = z.max_work;
-  int32_t *idx = exact<int32_t>(n, 0);
-  std::memcpy(idx, iv.data(), (size_t)n * 4);
+  int32_t *idx = exact<int32_t>(n, 0xa5);
+  if (KS == 0) std::memcpy(idx, iv.data(), (size_t)n * 4);
+  float *bias = exact<float>(E, 0), *logits = exact<float>((size_t)T * E, 0xa5), *w = exact<float>(n, 0xa5);
+  if (KS > 0) {
+    c.route_ks = KS;
+    c.route_small_t = T;
+    c.route_part = exact<float>((size_t)KS * T * E, 0);
+    std::memcpy(bias, iv.data(), (size_t)E * 4);
+    std::memcpy(c.route_part, iv.data() + E, (size_t)KS * T * E * 4);
+  }
   float *x = exact<float>((size_t)T * d, 0);
-  std::memcpy(x, iv.data() + n, (size_t)T * d * 4);
+  std::memcpy(x, iv.data() + head, (size_t)T * d * 4);
   const int xh = moe::xrec_halves(c.L.gate.nsb);
   const size_t xrec_n = (size_t)(T + 1) * xh;
   uint16_t *xrec = exact<uint16_t>(xrec_n, 0);
@@ -368,10 +379,19 @@ int run_bucket_lookup(char **a) {
   c.work = exact<moe::WorkEntry>(z.max_work, 0xa5);
   c.work8 = exact<moe::WorkEntry>(z.max_work8, 0xa5);
   c.n_work = exact<int32_t>(4, 0xa5);
-  for (int call = 0; call < 2; ++call)  // twice: the counters accumulate
-    if (moe::launch_bucket_lookup(&c, idx, T, moe::kEntryTokens, x, xrec, xh, (hipStream_t) nullptr) != hipSuccess)
-      die("launch_bucket_lookup refused the shape");
+  for (int call = 0; call < 2; ++call) {  // twice: the counters accumulate
+    const hipError_t e =
+        KS > 0 ? moe::launch_route_bucket_lookup(&c, T, bias, logits, idx, w, moe::kEntryTokens, x, xrec, xh,
+                                                 (hipStream_t) nullptr)
+               : moe::launch_bucket_lookup(&c, idx, T, moe::kEntryTokens, x, xrec, xh, (hipStream_t) nullptr);
+    if (e != hipSuccess) die("the bucketing launch refused the shape");
+  }
   Out o(out);
+  if (KS > 0) {
+    o.put(reinterpret_cast<const int32_t *>(logits), (size_t)T * E);
+    o.put(idx, n);
+    o.put(reinterpret_cast<const int32_t *>(w), n);
+  }
   o.put(c.offsets_ws, E + 1);
   o.put(c.perm_ws, n);
   const int nw = c.n_work[0];
@@ -386,6 +406,10 @@ int run_bucket_lookup(char **a) {
   o.put(c.dmiss, 3);
   o.put(c.dstats, 6);
   std::free(idx);
+  std::free(bias);
+  std::free(logits);
+  std::free(w);
+  std::free(c.route_part);
   std::free(x);
   std::free(xrec);
   std::free(c.dmiss);
@@ -409,7 +433,8 @@ int main(int argc, char **argv) {
   if (mode == "bucket" && argc == 10) return run_bucket(argv + 2);
   if (mode == "noalloc" && argc == 7) return run_noalloc(argv + 2);
   if (mode == "resolve" && argc == 14) return run_resolve(argv + 2);
-  if (mode == "bucket_lookup" && argc == 8) return run_bucket_lookup(argv + 2);
+  if (mode == "bucket_lookup" && argc == 8) return run_bucket_lookup(argv + 2, 0);
+  if (mode == "route_bucket" && argc == 9) return run_bucket_lookup(argv + 3, std::atoi(argv[2]));
   if (mode == "route_resolve" && argc == 11) return run_route_resolve(argv + 2);
   die("bad arguments");
 }

@@ -399,6 +399,49 @@ def test_resolve_more_slots_than_threads(exe, tmp_path):
 # the bucketing launch of a resident decode layer, with its lookup count
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("T", [1, 2])
+def test_route_bucket_one_or_two_tokens(exe, tmp_path, T):
+    # a resident decode layer of one or two tokens: the top-k of each token
+    # (from partial logits, exact ties included) and then the bucketing, the
+    # work lists, the lookup count and the x record in one launch -- against
+    # the oracle's top-k of the launch's own logits and the bucketing of its idx
+    E, k, d, KS = 512, 10, 320, 8
+    rng = np.random.default_rng(40 + T)
+    bias = rng.normal(0.0, 1.0, E).astype(np.float32)
+    bias[100:112] = bias[100]
+    part = rng.normal(0.0, 0.5, (KS, T, E)).astype(np.float32)
+    part[:, :, 100:112] = 1.5  # twelve experts tied at the top
+    x = (rng.standard_normal((T, d)) * 2.0).astype(np.float32)
+    out = _Reader(_run(exe, tmp_path, ["route_bucket", KS, E, T, k, d], [bias.view(np.int32), part.view(np.int32),
+                                                                         x.view(np.int32)]))
+    logits = out.take(T * E, np.float32).reshape(T, E)
+    want = np.zeros((T, E), np.float32)
+    for q in range(KS):
+        want = want + part[q]
+    want = want + bias
+    assert np.array_equal(logits.view(np.int32), want.view(np.int32))
+    idx = out.take(T * k).reshape(T, k)
+    w = out.take(T * k, np.float32).reshape(T, k)
+    idx_o, w_o = oracle.topk_from_logits(want.astype(np.float64), k)
+    assert np.array_equal(idx, idx_o) and np.allclose(w, w_o, rtol=1e-6, atol=1e-7)
+    assert idx[0].tolist() == list(range(100, 110))  # ties broken by index
+    counts, offsets, perm = _bucket_expected(idx, E)
+    assert np.array_equal(out.take(E + 1), offsets)
+    assert np.array_equal(out.take(T * k), perm)
+    work, routed = _work_expected(counts, offsets, T, 4)
+    assert out.take(2).tolist() == [len(work), routed]
+    assert np.array_equal(out.take(len(work) * 4).reshape(-1, 4), work)
+    work8, routed8 = _work_expected(counts, offsets, T, 8)
+    assert out.take(2).tolist() == [len(work8), routed8]
+    assert np.array_equal(out.take(len(work8) * 4).reshape(-1, 4), work8)
+    nsb = -(-d // 160)
+    assert np.array_equal(out.take((T + 1) * nsb * 320, np.uint16).reshape(T + 1, -1), _xrec_expected(x, nsb))
+    nuniq = len(np.unique(idx))
+    assert out.take(3).tolist() == [nuniq, 0, 0]
+    assert out.take(6, np.int64).tolist() == [2 * nuniq, 2 * nuniq, 0, 2, 0, 0]
+    out.done()
+
+
 @pytest.mark.parametrize("E,T,k,d", [(512, 15, 10, 2048), (64, 128, 8, 96), (1024, 1, 1, 160)],
                          ids=["decode_workload", "1024_pairs", "1024_experts"])
 def test_bucket_lookup(exe, tmp_path, E, T, k, d):
