@@ -335,6 +335,24 @@ __device__ inline void gateup_rows(const DecodeParams &P, const Unit &U, int w, 
   }
 }
 
+// the same for one row i of the four (the quarters of K finalise one row each)
+template <int COLS>
+__device__ inline void gateup_row(const DecodeParams &P, const Unit &U, int w, int lane, int i, float gv, float uv) {
+  const int r16 = lane & 15, g = lane >> 4;
+  const int rt = U.tile0 + w;
+  gv += __shfl_xor(gv, COLS, 64);
+  uv += __shfl_xor(uv, COLS, 64);
+  if (!(U.has_tok && r16 < COLS && rt * 16 < P.d_ff)) return;
+  uint16_t *hr = P.hrec + (size_t)U.rrow * P.hrec_h;
+  float inv_f;
+  const int pos = rec_pos(rt * 16 + 4 * g + i, inv_f);
+  const float h = gv / (1.0f + __expf(-gv)) * uv * inv_f;
+  const _Float16 hi = (_Float16)h;
+  const _Float16 lo = (_Float16)(h - (float)hi);
+  hr[pos] = __builtin_bit_cast(uint16_t, hi);
+  hr[pos + 8] = __builtin_bit_cast(uint16_t, lo);
+}
+
 // word quads of superblocks issued up front; the rest is requested as the
 // registers of superblock S - depth free up (gate/up keeps 9 superblocks of
 // two matrices in flight within the register budget of 3 waves per SIMD)
@@ -463,7 +481,7 @@ __global__ void __launch_bounds__(64 * kWaves, (decode_min_blocks<NSB, NMAT>()))
   constexpr int kScBytes = NMAT * kScMat;
   __shared__ __attribute__((aligned(1024))) uint8_t lact[kActBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t lsc[(kScBytes + 4095) / 4096 * 4096];
-  __shared__ f4 red[KS == 1 ? 1 : (KS == 2 ? 2 * kTiles * 64 : 3 * 64 * 2)];
+  __shared__ f4 red[KS == 1 ? 1 : (KS == 2 ? 2 * kTiles * 64 : 4 * 64 * 2)];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
   const int ltile = KS == 1 ? w : w % kTiles;                                    // tile of the unit
@@ -539,18 +557,20 @@ __global__ void __launch_bounds__(64 * kWaves, (decode_min_blocks<NSB, NMAT>()))
         gateup_rows<COLS>(P, U, ltile, lane, 2, acc0[2] + r[0], acc0[3] + r[1], acc1[2] + r[2], acc1[3] + r[3]);
       continue;
     } else if constexpr (KS == 4) {
-      // quarters 1..3 -> LDS; quarter 0 adds them in order (fixed order: q0 + q1 + q2 + q3)
-      if (half != 0) {
-        red[((half - 1) * 64 + lane) * 2 + 0] = acc0;
-        red[((half - 1) * 64 + lane) * 2 + 1] = acc1;
-      }
+      // every quarter's sums -> LDS; quarter q finalises row q of the lane's
+      // four, adding the quarters in order (q0 + q1 + q2 + q3)
+      red[(half * 64 + lane) * 2 + 0] = acc0;
+      red[(half * 64 + lane) * 2 + 1] = acc1;
       __syncthreads();
-      if (half != 0) continue;
+      const int q = half;  // uniform
+      float gv = red[lane * 2 + 0][q], uv = red[lane * 2 + 1][q];
 #pragma unroll
-      for (int q = 0; q < 3; ++q) {
-        acc0 += red[(q * 64 + lane) * 2 + 0];
-        acc1 += red[(q * 64 + lane) * 2 + 1];
+      for (int p = 1; p < 4; ++p) {
+        gv += red[(p * 64 + lane) * 2 + 0][q];
+        uv += red[(p * 64 + lane) * 2 + 1][q];
       }
+      gateup_row<COLS>(P, U, ltile, lane, q, gv, uv);
+      continue;
     }
     unit_epilogue<NMAT, COLS>(P, U, ltile, lane, acc0, acc1);
   }
