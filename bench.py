@@ -779,9 +779,10 @@ def bench_kv(seed, peaks, reps=5):
 def verify_sweep(ctx, routers, biases, seed, d, f, L, reps=5, warm=2):
     """Speculative verify as a batch: `slots` requests each verify 1 + `spec`
     tokens in one pass, T = slots * (1 + spec) tokens per step, for spec 1..6
-    and slots 1..4.  Each T: the 48-layer resident stack captured in a HIP
-    graph, replayed on fresh inputs; reports tok/s and the expert bytes each
-    token costs (touched routed experts + the shared one, per layer)."""
+    and slots 1..4.  Each T: the 48-layer resident stack of moe_decode_layer
+    captured in a HIP graph, replayed on fresh inputs; reports tok/s and the
+    expert bytes each token costs (touched routed experts + the shared one,
+    per layer)."""
     import numpy as np
     import torch
 
@@ -800,12 +801,9 @@ def verify_sweep(ctx, routers, biases, seed, d, f, L, reps=5, warm=2):
             def step():
                 x = xin
                 for l in range(L):
-                    B.moe_route(c, l, x, T, routers[l], biases[l], None, buf["idx"], buf["w"])
-                    B.moe_cache_resolve(c, l, buf["idx"], T, None)
-                    B.moe_expert_ffn(c, l, x, T, buf["idx"], None, buf["y_pairs"], buf["y_shared"],
-                                     B.MOE_PATH_DECODE)
                     xn = xa if (l % 2 == 0) else xb
-                    B.moe_combine_norm(c, buf["y_pairs"], buf["w"], buf["y_shared"], T, buf["out"], xn)
+                    B.moe_decode_layer(c, l, x, T, routers[l], biases[l], None, buf["idx"], buf["w"],
+                                       buf["y_pairs"], buf["y_shared"], buf["out"], xn)
                     x = xn
 
             torch.cuda.synchronize()
