@@ -184,7 +184,7 @@ moe_status moe_combine(moe_ctx *ctx, const float *y_pairs, const float *w,
                        const float *y_shared, int32_t T, float *out, void *stream);
 
 /* One whole decode layer; on a resident cache in six launches instead of the
- * seven of the separate calls (five for one or two tokens, whose top-k joins
+ * seven of the separate calls (five for a single token, whose top-k joins
  * the bucketing launch) (the pages' engine has a fused-kernel mode,
  * "融合核": "从一张到四张 RTX 4090 ...", section 调参：前后 40 多次重启):
  * the router's two launches; one launch for the resident lookup count, the
@@ -208,8 +208,8 @@ moe_status moe_combine(moe_ctx *ctx, const float *y_pairs, const float *w,
  * 如何做到：三层存储); the missed blobs are copied from the mapped host store
  * as moe_cache_resolve_async's fill kernel copies them, but by spare
  * workgroups of the bucketing launch, which does not depend on the resolve:
- * seven launches instead of the separate calls' eight, and six for one or
- * two tokens, whose top-k and resolve share one workgroup.  A call that cannot
+ * seven launches instead of the separate calls' eight, and six for a single
+ * token, whose top-k and resolve share one workgroup.  A call that cannot
  * pin its working set changes nothing in the table, counts one failed call
  * and leaves its pairs' y_pairs rows unwritten (out is then not
  * meaningful).

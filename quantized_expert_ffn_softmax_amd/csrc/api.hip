@@ -424,8 +424,10 @@ extern "C" moe_status moe_decode_layer(moe_ctx *c, int32_t layer, const float *x
   float *lg = logits ? logits : c->logits_ws;
   hipError_t e = hipSuccess;
   if (c->resident) {
-    // one or two tokens: the top-k joins the bucketing launch (five launches)
-    if (T <= 2 && T <= c->route_small_t) {
+    // a single token: the top-k joins the bucketing launch (five launches;
+    // at two tokens the two top-ks one after another in one workgroup cost
+    // more than the launch they save)
+    if (T == 1 && T <= c->route_small_t) {
       e = moe::launch_router_partials(c, x, T, w_router, s);
       if (e == hipSuccess)
         e = moe::launch_route_bucket_lookup(c, T, bias, lg, idx, w, moe::kEntryTokens, x, c->xrec, xh, s);
@@ -435,11 +437,11 @@ extern "C" moe_status moe_decode_layer(moe_ctx *c, int32_t layer, const float *x
     }
     if (e == hipSuccess) e = moe::launch_ffn_decode_kernels(c, layer, T, nullptr, y_pairs, y_shared, s);
   } else {
-    // capped: the router and the resolve (for one or two tokens the top-k
-    // and the resolve share one workgroup), then one launch for the
+    // capped: the router and the resolve (for a single token the top-k and
+    // the resolve share one workgroup), then one launch for the
     // bucketing, the x record and the zero-copy fill of the resolve's misses
     // (no fill launch of its own), then the FFN on the filled slots
-    if (T <= 2 && T <= c->route_small_t) {
+    if (T == 1 && T <= c->route_small_t) {
       e = moe::launch_router_partials(c, x, T, w_router, s);
       if (e == hipSuccess) e = moe::launch_route_resolve(c, layer, T, bias, lg, idx, w, c->slot_ws, s);
     } else {

@@ -210,9 +210,11 @@ __global__ void __launch_bounds__(kBucketThreads) bucket_small(const int32_t *__
   }
 }
 
-// A resident decode layer of one or two tokens: workgroup 0 finishes the
-// router's top-k of each token from its partial logits (topk_small.h, as the
-// router's own finishing kernel does with one workgroup per token), then
+// A resident decode layer of one or two tokens (moe_decode_layer uses it for
+// one: two top-ks one after another cost more than the launch they save):
+// workgroup 0 finishes the router's top-k of each token from its partial
+// logits (topk_small.h, as the router's own finishing kernel does with one
+// workgroup per token), then
 // buckets the pairs it has just written and records the lookup, as
 // bucket_small does with stats; the other workgroups build the x record,
 // which does not depend on the routing.  One launch where the separate steps

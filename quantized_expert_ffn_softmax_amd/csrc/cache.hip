@@ -42,11 +42,11 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(const int32_t *__rest
   moe::resolve_block(idx, n, layer, E, S, resident, clear_on_fail, slot_of, id_of, stamp, slot_of_pair, dmiss, stats);
 }
 
-// A capped decode layer of at most kRouteResolveMaxT tokens: the router's
-// top-k of each token (from the partial logits of the router's first
-// kernel), then the resolve of the call's pairs, in one workgroup -- one
-// launch where the separate calls make two, with no handoff between
-// workgroups (the top-k's idx reaches the resolve through a barrier).
+// A capped decode layer of at most kRouteResolveMaxT tokens (moe_decode_layer
+// uses it for one): the router's top-k of each token (from the partial logits
+// of the router's first kernel), then the resolve of the call's pairs, in one
+// workgroup -- one launch where the separate calls make two, with no handoff
+// between workgroups (the top-k's idx reaches the resolve through a barrier).
 constexpr int kRouteResolveMaxT = 2;
 
 __global__ void __launch_bounds__(kThreads) route_resolve_kernel(const float *__restrict__ part, int T, int E, int KS,

@@ -155,7 +155,7 @@ hipError_t launch_router(const moe_ctx *c, const float *x, int T, const float *w
 // the decode-size router's first kernel alone (partial logits into
 // c->route_part); T <= c->route_small_t
 hipError_t launch_router_partials(const moe_ctx *c, const float *x, int T, const float *wr, hipStream_t s);
-// capped cache, T <= 2: the router's top-k from c->route_part and the
+// capped cache, T <= 2 (the decode layer uses it at T = 1): the router's top-k from c->route_part and the
 // resolve (no fill kernel; a call that cannot pin its working set gives every
 // pair slot -1) in one single-workgroup launch
 hipError_t launch_route_resolve(moe_ctx *c, int layer, int T, const float *bias, float *logits, int32_t *idx,
@@ -185,7 +185,7 @@ hipError_t launch_ffn_decode_kernels(const moe_ctx *c, int layer, int T, const i
 // T * top_k <= 1024, n_experts <= 1024
 hipError_t launch_bucket_lookup(const moe_ctx *c, const int32_t *idx, int T, int entry_m, const float *x,
                                 uint16_t *xrec, int xrec_h, hipStream_t s);
-// resident cache, T <= 2: the router's top-k from c->route_part, the lookup
+// resident cache, T <= 2 (the decode layer uses it at T = 1): the router's top-k from c->route_part, the lookup
 // count, the bucketing with its work lists and the x record, in one launch
 hipError_t launch_route_bucket_lookup(const moe_ctx *c, int T, const float *bias, float *logits, int32_t *idx, float *w,
                                      int entry_m, const float *x, uint16_t *xrec, int xrec_h, hipStream_t s);

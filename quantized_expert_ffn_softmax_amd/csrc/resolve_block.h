@@ -1,6 +1,6 @@
 // The cache resolve as a workgroup-wide device function (the LRU rules are
 // stated where the resolve kernel is defined, cache.hip): the resolve kernel
-// runs it alone, and a capped decode layer of one or two tokens runs it in
+// runs it alone, and a capped decode layer of a single token runs it in
 // the workgroup that has just finished the router's top-k.
 #pragma once
 #include <hip/hip_runtime.h>

@@ -1,5 +1,5 @@
 """moe_decode_layer -- a whole decode layer on a resident cache in six
-launches, five for one or two tokens (the capped cache:
+launches, five for a single token (the capped cache:
 test_gpu_decode_layer_capped.py) -- against the seven-launch sequence of
 separate calls it replaces
 (moe_route -> moe_cache_resolve -> moe_expert_ffn on the decode path ->

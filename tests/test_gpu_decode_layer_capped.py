@@ -4,9 +4,9 @@ the decode path -> moe_combine_norm) on a twin context over the same host
 store:
 
 * every output bit for bit, call after call, with misses, hits and
-  evictions; the same table, stamps and counters after every call (one or
-  two tokens take the top-k and the resolve in one workgroup, more tokens
-  the router's own finishing kernel and the resolve kernel);
+  evictions; the same table, stamps and counters after every call (a single
+  token takes the top-k and the resolve in one workgroup, more tokens the
+  router's own finishing kernel and the resolve kernel);
 * no fill kernel runs (the bucketing launch copies the misses in spare
   workgroups): every slot in use then holds its identity's blob, byte for byte
   up to the end of the last section, and later calls that hit those slots
